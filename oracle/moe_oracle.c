@@ -1,0 +1,455 @@
+/*
+ * moe_oracle.c -- plain, slow CPU oracle of the batch-invariant MoE layer
+ * forward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg load this library.  The product path (the HIP
+ * library) never calls it and shares no code with it.
+ *
+ * What the layer computes, and where the pages ask for it:
+ *   - Fireworks page "位级一致：前沿训练的差异化关键" (bit-level agreement),
+ *     section "为什么比特级一致是一个复杂的问题" (why bit-level agreement is
+ *     hard): float addition is not associative; the router can nearly tie
+ *     between experts; per-expert matmul kernels change with the per-expert
+ *     token count.  The fix named there: one fixed kernel choice for the expert
+ *     matmuls whatever the token count, and a deterministic router tie-break.
+ *   - Same page, section "曾经只有前沿实验室才有的功能" (capabilities once
+ *     exclusive to frontier labs): batch invariance means a request's result
+ *     does not depend on what else shares its batch; the MoE router and the
+ *     expert GEMMs are among the reductions that must stay consistent; split-K
+ *     breaks invariance.
+ *   - Fireworks page on numerical alignment and MoE routing (best2ai.com),
+ *     section "混合专家模型更难对齐" (MoE models are harder to align): the
+ *     precision and the order used to weight and sum the expert outputs must
+ *     both be fixed.
+ *   - "GLM Post-Training Beyond SFT", section "迁移到 NPU 时" (when moving to
+ *     NPU) and the sparse/version contract: a top-k must fix ties at the
+ *     boundary, sort stability, NaN handling and the index dtype, and is
+ *     compared by index set and order.
+ *
+ * The pages never write the layer's formula.  The definition implemented here
+ * (steps D1..D7) is the plainest reading consistent with them:
+ *   D1 l[t,e]  = fp32 chain over i = 0..H-1 ascending: acc = fma(x, w, acc)
+ *               (bf16 x bf16 products are exact in fp32, so this is also the
+ *               plain multiply-then-add chain).  The logit decides an integer
+ *               (the expert set), so it is taken in the kernel's precision.
+ *   D2 keys:   softmax -> key_e = l_e (softmax is strictly increasing, so the
+ *               top-k of the logits is the top-k of the exact probabilities);
+ *               sigmoid -> key_e = fp32(1/(1+expf(-l_e))) + bias_e in fp32.
+ *   D3 top-k:  order by key descending, then expert index ascending; -0 equals
+ *               +0; a NaN key ranks below every other key (also below -inf),
+ *               NaNs among themselves by index.  Slot j holds the j-th.
+ *   D4 weights (fp64, rounded to fp32 once): softmax p_e = exp(l_e-m)/sum_e
+ *               exp(l_e-m) with m = max_e l_e; sigmoid p_e = 1/(1+exp(-l_e));
+ *               renormalised w_j = p_{e_j} / sum_j p_{e_j}, else w_j = p_{e_j}.
+ *               The bias never enters the weights.
+ *   D5 permute: counts[e], offsets = exclusive prefix sum, perm lists the
+ *               assignment ids a = t*k + j routed to e in ascending a,
+ *               inv_perm[perm[p]] = p.
+ *   D6 expert:  g_f = sum_i x_i Wg[e,f,i], u_f = sum_i x_i Wu[e,f,i] (fp64);
+ *               act_f = bf16_rne(fp32(silu(g_f) * u_f)), silu(g) = g/(1+e^-g);
+ *               Y[a,h] = fp32(sum_f act_f Wd[e,h,f]) (fp64 sum, one rounding).
+ *               act is a stored bf16 code, so it is rounded from fp32, the
+ *               precision the kernel decides it in.
+ *   D7 combine: acc = +0.0f; for j = 0..k-1: acc = fmaf(w[t,j], Y[t*k+j,h], acc);
+ *               out[t,h] = bf16_rne(acc).  The precision (fp32) and the order
+ *               (slot order) are both part of the definition.
+ *
+ * Everything is plain loops.  Tokens are independent, so the token loop may
+ * run on several threads; every per-token result is the same at any thread
+ * count.  Built with -ffp-contract=off: every fma below is an explicit call.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_SOFTMAX 0
+#define ORC_SIGMOID 1
+
+/* ------------------------------------------------------------------------ */
+/* number formats                                                            */
+/* ------------------------------------------------------------------------ */
+
+static float f32_from_bits(uint32_t b) { float f; memcpy(&f, &b, 4); return f; }
+static uint32_t bits_from_f32(float f) { uint32_t b; memcpy(&b, &f, 4); return b; }
+
+float orc_bf16_to_f32(uint16_t h) { return f32_from_bits((uint32_t)h << 16); }
+
+/* fp32 -> bf16, round to nearest, ties to even.  NaN stays a (quiet) NaN with
+ * its sign; overflow rounds to +-inf as IEEE rounding does. */
+uint16_t orc_f32_to_bf16(float f)
+{
+    uint32_t b = bits_from_f32(f);
+    if (isnan(f))
+        return (uint16_t)((b >> 16) | 0x0040u);
+    uint32_t upper = b >> 16;
+    uint32_t lower = b & 0xFFFFu;
+    if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u)))
+        upper += 1u;  /* carries into the exponent where needed, up to inf */
+    return (uint16_t)upper;
+}
+
+void orc_f32_to_bf16_array(const float* in, uint16_t* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_f32_to_bf16(in[i]);
+}
+
+static int set_threads(int nthreads)
+{
+#ifdef _OPENMP
+    if (nthreads > 0) return nthreads;
+    return omp_get_max_threads();
+#else
+    (void)nthreads;
+    return 1;
+#endif
+}
+
+int orc_max_threads(void) { return set_threads(0); }
+
+/* ------------------------------------------------------------------------ */
+/* D1: router logits                                                         */
+/* ------------------------------------------------------------------------ */
+
+static float logit_one(const uint16_t* xrow, const uint16_t* wrow, int H)
+{
+    float acc = 0.0f;
+    for (int i = 0; i < H; ++i)
+        acc = fmaf(orc_bf16_to_f32(xrow[i]), orc_bf16_to_f32(wrow[i]), acc);
+    return acc;
+}
+
+void orc_router_logits(int T, int H, int E, const uint16_t* x, const uint16_t* wr,
+                       float* logits, int nthreads)
+{
+    int nt = set_threads(nthreads);
+    (void)nt;
+#pragma omp parallel for num_threads(nt) schedule(dynamic, 4)
+    for (int t = 0; t < T; ++t)
+        for (int e = 0; e < E; ++e)
+            logits[(int64_t)t * E + e] = logit_one(x + (int64_t)t * H, wr + (int64_t)e * H, H);
+}
+
+/* ------------------------------------------------------------------------ */
+/* D2 + D3: selection keys and top-k                                         */
+/* ------------------------------------------------------------------------ */
+
+/* Is expert a (key ka) ahead of expert b (key kb) in selection order? */
+static int ranks_before(float ka, int a, float kb, int b)
+{
+    int na = isnan(ka), nb = isnan(kb);
+    if (na || nb) {
+        if (na && nb) return a < b;
+        return nb;  /* the non-NaN one is ahead */
+    }
+    if (ka > kb) return 1;
+    if (ka < kb) return 0;
+    return a < b;   /* equal by value (covers -0 == +0): lower index first */
+}
+
+/* Select k of E keys: repeated scans for the best key not yet taken. */
+static void select_topk(const float* key, int E, int k, int32_t* ids, unsigned char* taken)
+{
+    memset(taken, 0, (size_t)E);
+    for (int j = 0; j < k; ++j) {
+        int best = -1;
+        for (int e = 0; e < E; ++e) {
+            if (taken[e]) continue;
+            if (best < 0 || ranks_before(key[e], e, key[best], best)) best = e;
+        }
+        taken[best] = 1;
+        ids[j] = best;
+    }
+}
+
+/* Top-k over given keys (exported for the tie/NaN pin tests). */
+void orc_topk_keys(int n, int E, int k, const float* keys, int32_t* ids)
+{
+    unsigned char* taken = (unsigned char*)malloc((size_t)E);
+    for (int r = 0; r < n; ++r)
+        select_topk(keys + (int64_t)r * E, E, k, ids + (int64_t)r * k, taken);
+    free(taken);
+}
+
+static float sigmoid_key_f32(float l, float b)
+{
+    float s = 1.0f / (1.0f + expf(-l));
+    return s + b;
+}
+
+/* D1..D4 for one token. scratch: 2*E floats + E bytes. */
+static void route_one(const uint16_t* xrow, const uint16_t* wr, const float* bias,
+                      int H, int E, int k, int score, int renorm,
+                      int32_t* ids, float* w, double* gap, float* keys, float* logits,
+                      unsigned char* taken)
+{
+    for (int e = 0; e < E; ++e) logits[e] = logit_one(xrow, wr + (int64_t)e * H, H);
+    for (int e = 0; e < E; ++e)
+        keys[e] = (score == ORC_SOFTMAX) ? logits[e]
+                                         : sigmoid_key_f32(logits[e], bias ? bias[e] : 0.0f);
+    select_topk(keys, E, k, ids, taken);
+
+    /* gap between the k-th and (k+1)-th key, in fp64 (diagnostic for the
+     * near-tie exemption); +inf when k == E */
+    if (gap) {
+        if (k >= E) {
+            *gap = INFINITY;
+        } else {
+            int next = -1;
+            for (int e = 0; e < E; ++e) {
+                if (taken[e]) continue;
+                if (next < 0 || ranks_before(keys[e], e, keys[next], next)) next = e;
+            }
+            *gap = (double)keys[ids[k - 1]] - (double)keys[next];
+        }
+    }
+
+    /* D4 weights in fp64 */
+    double p[16];
+    if (score == ORC_SOFTMAX) {
+        double m = -INFINITY;
+        for (int e = 0; e < E; ++e)
+            if ((double)logits[e] > m) m = (double)logits[e];
+        double S = 0.0;
+        for (int e = 0; e < E; ++e) S += exp((double)logits[e] - m);
+        for (int j = 0; j < k; ++j) p[j] = exp((double)logits[ids[j]] - m) / S;
+    } else {
+        for (int j = 0; j < k; ++j) p[j] = 1.0 / (1.0 + exp(-(double)logits[ids[j]]));
+    }
+    if (renorm) {
+        double D = 0.0;
+        for (int j = 0; j < k; ++j) D += p[j];
+        for (int j = 0; j < k; ++j) w[j] = (float)(p[j] / D);
+    } else {
+        for (int j = 0; j < k; ++j) w[j] = (float)p[j];
+    }
+}
+
+/* Route T tokens.  ids [T,k] int32, w [T,k] fp32, gap [T] fp64 (or NULL). */
+int orc_route(int T, int H, int E, int k, int score, int renorm,
+              const uint16_t* x, const uint16_t* wr, const float* bias,
+              int32_t* ids, float* w, double* gap, int nthreads)
+{
+    if (k < 1 || k > E || k > 16) return -2;
+    int nt = set_threads(nthreads);
+    (void)nt;
+#pragma omp parallel num_threads(nt)
+    {
+        float* keys = (float*)malloc(sizeof(float) * (size_t)E * 2);
+        unsigned char* taken = (unsigned char*)malloc((size_t)E);
+#pragma omp for schedule(dynamic, 4)
+        for (int t = 0; t < T; ++t)
+            route_one(x + (int64_t)t * H, wr, bias, H, E, k, score, renorm,
+                      ids + (int64_t)t * k, w + (int64_t)t * k, gap ? gap + t : NULL,
+                      keys, keys + E, taken);
+        free(keys);
+        free(taken);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* D5: histogram, offsets and the stable permutation                         */
+/* ------------------------------------------------------------------------ */
+
+int orc_permute(int A, int E, const int32_t* ids, int32_t* counts, int32_t* offsets,
+                int32_t* perm, int32_t* inv_perm)
+{
+    for (int e = 0; e < E; ++e) counts[e] = 0;
+    for (int a = 0; a < A; ++a) {
+        if (ids[a] < 0 || ids[a] >= E) return -2;
+        counts[ids[a]] += 1;
+    }
+    offsets[0] = 0;
+    for (int e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+    /* walk assignments in ascending id; each lands after the earlier ones of
+     * its expert (a stable counting sort) */
+    int32_t* fill = (int32_t*)malloc(sizeof(int32_t) * (size_t)(E > 0 ? E : 1));
+    for (int e = 0; e < E; ++e) fill[e] = offsets[e];
+    for (int a = 0; a < A; ++a) {
+        int p = fill[ids[a]]++;
+        perm[p] = a;
+        inv_perm[a] = p;
+    }
+    free(fill);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* D6: one expert's SwiGLU FFN for one token                                 */
+/* ------------------------------------------------------------------------ */
+
+static double silu_d(double g) { return g / (1.0 + exp(-g)); }
+
+/* act_out [F] bf16 (may be NULL), y_out [H] fp32.  scratch [F] doubles. */
+static void expert_one(const uint16_t* xrow, int e, int H, int F,
+                       const uint16_t* wg, const uint16_t* wu, const uint16_t* wd,
+                       uint16_t* act_out, float* y_out, double* act_d)
+{
+    const uint16_t* G = wg + (int64_t)e * F * H;
+    const uint16_t* U = wu + (int64_t)e * F * H;
+    const uint16_t* D = wd + (int64_t)e * H * F;
+    for (int f = 0; f < F; ++f) {
+        double g = 0.0, u = 0.0;
+        const uint16_t* gr = G + (int64_t)f * H;
+        const uint16_t* ur = U + (int64_t)f * H;
+        for (int i = 0; i < H; ++i) {
+            double xi = (double)orc_bf16_to_f32(xrow[i]);
+            g += xi * (double)orc_bf16_to_f32(gr[i]);
+            u += xi * (double)orc_bf16_to_f32(ur[i]);
+        }
+        uint16_t a = orc_f32_to_bf16((float)(silu_d(g) * u));
+        if (act_out) act_out[f] = a;
+        act_d[f] = (double)orc_bf16_to_f32(a);
+    }
+    for (int h = 0; h < H; ++h) {
+        const uint16_t* dr = D + (int64_t)h * F;
+        double y = 0.0;
+        for (int f = 0; f < F; ++f) y += act_d[f] * (double)orc_bf16_to_f32(dr[f]);
+        y_out[h] = (float)y;
+    }
+}
+
+/* n (token, expert) pairs -> act [n,F] bf16 (or NULL) and y [n,H] fp32. */
+int orc_expert_ffn(int n, const int32_t* tokens, const int32_t* experts,
+                   int H, int E, int F, const uint16_t* x,
+                   const uint16_t* wg, const uint16_t* wu, const uint16_t* wd,
+                   uint16_t* act, float* y, int nthreads)
+{
+    for (int r = 0; r < n; ++r)
+        if (experts[r] < 0 || experts[r] >= E) return -2;
+    int nt = set_threads(nthreads);
+    (void)nt;
+#pragma omp parallel num_threads(nt)
+    {
+        double* act_d = (double*)malloc(sizeof(double) * (size_t)F);
+#pragma omp for schedule(dynamic, 1)
+        for (int r = 0; r < n; ++r)
+            expert_one(x + (int64_t)tokens[r] * H, experts[r], H, F, wg, wu, wd,
+                       act ? act + (int64_t)r * F : NULL, y + (int64_t)r * H, act_d);
+        free(act_d);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* D7: fixed-order fp32 combine                                              */
+/* ------------------------------------------------------------------------ */
+
+static void combine_one(const float* y_tok /* [k,H] */, const float* w, int H, int k,
+                        uint16_t* out_row)
+{
+    for (int h = 0; h < H; ++h) {
+        float acc = 0.0f;
+        for (int j = 0; j < k; ++j) acc = fmaf(w[j], y_tok[(int64_t)j * H + h], acc);
+        out_row[h] = orc_f32_to_bf16(acc);
+    }
+}
+
+void orc_combine(int T, int H, int k, const float* y, const float* w, uint16_t* out)
+{
+    for (int t = 0; t < T; ++t)
+        combine_one(y + (int64_t)t * k * H, w + (int64_t)t * k, H, k, out + (int64_t)t * H);
+}
+
+/* ------------------------------------------------------------------------ */
+/* whole layer                                                               */
+/* ------------------------------------------------------------------------ */
+
+/* The layer in the method's order: route all tokens, permute, run each
+ * expert over its segment of the permutation, combine.  Optional outputs
+ * (NULL to skip): ids [T,k], w [T,k], gap [T], counts [E], offsets [E+1],
+ * perm [A], inv_perm [A], y [A,H] (assignment order). */
+int orc_forward(int T, int H, int E, int F, int k, int score, int renorm,
+                const uint16_t* x, const uint16_t* wr, const float* bias,
+                const uint16_t* wg, const uint16_t* wu, const uint16_t* wd,
+                uint16_t* out, int32_t* ids_o, float* w_o, double* gap_o,
+                int32_t* counts_o, int32_t* offsets_o, int32_t* perm_o,
+                int32_t* inv_perm_o, float* y_o, int nthreads)
+{
+    if (k < 1 || k > E || k > 16) return -2;
+    int64_t A = (int64_t)T * k;
+    int32_t* ids = ids_o ? ids_o : (int32_t*)malloc(sizeof(int32_t) * (size_t)(A + 1));
+    float* w = w_o ? w_o : (float*)malloc(sizeof(float) * (size_t)(A + 1));
+    int32_t* counts = counts_o ? counts_o : (int32_t*)malloc(sizeof(int32_t) * (size_t)E);
+    int32_t* offsets = offsets_o ? offsets_o : (int32_t*)malloc(sizeof(int32_t) * (size_t)(E + 1));
+    int32_t* perm = perm_o ? perm_o : (int32_t*)malloc(sizeof(int32_t) * (size_t)(A + 1));
+    int32_t* inv = inv_perm_o ? inv_perm_o : (int32_t*)malloc(sizeof(int32_t) * (size_t)(A + 1));
+    float* y = y_o ? y_o : (float*)malloc(sizeof(float) * (size_t)(A * H + 1));
+    int rc = orc_route(T, H, E, k, score, renorm, x, wr, bias, ids, w, gap_o, nthreads);
+    if (rc == 0) rc = orc_permute((int)A, E, ids, counts, offsets, perm, inv);
+    if (rc == 0) {
+        /* expert by expert over its contiguous segment of the permutation */
+        int32_t* tok = (int32_t*)malloc(sizeof(int32_t) * (size_t)(A + 1));
+        int32_t* exp_ = (int32_t*)malloc(sizeof(int32_t) * (size_t)(A + 1));
+        float* yp = (float*)malloc(sizeof(float) * (size_t)(A * H + 1));
+        for (int e = 0; e < E; ++e)
+            for (int p = offsets[e]; p < offsets[e + 1]; ++p) {
+                tok[p] = perm[p] / k;
+                exp_[p] = e;
+            }
+        rc = orc_expert_ffn((int)A, tok, exp_, H, E, F, x, wg, wu, wd, NULL, yp, nthreads);
+        /* scatter expert outputs back to assignment order */
+        for (int64_t p = 0; p < A; ++p)
+            memcpy(y + (int64_t)perm[p] * H, yp + p * H, sizeof(float) * (size_t)H);
+        free(tok); free(exp_); free(yp);
+    }
+    if (rc == 0) orc_combine(T, H, k, y, w, out);
+    if (!ids_o) free(ids);
+    if (!w_o) free(w);
+    if (!counts_o) free(counts);
+    if (!offsets_o) free(offsets);
+    if (!perm_o) free(perm);
+    if (!inv_perm_o) free(inv);
+    if (!y_o) free(y);
+    return rc;
+}
+
+/* Per-token evaluation of a chosen subset of tokens (no permutation): route
+ * token t, run its k experts, combine.  Each token's result does not depend on
+ * any other token, so this equals orc_forward on those rows.  out [n,H],
+ * ids [n,k], w [n,k], gap [n] (optional). */
+int orc_forward_tokens(int n, const int32_t* tokens, int H, int E, int F, int k,
+                       int score, int renorm, const uint16_t* x, const uint16_t* wr,
+                       const float* bias, const uint16_t* wg, const uint16_t* wu,
+                       const uint16_t* wd, uint16_t* out, int32_t* ids_o, float* w_o,
+                       double* gap_o, int nthreads)
+{
+    if (k < 1 || k > E || k > 16) return -2;
+    int nt = set_threads(nthreads);
+    (void)nt;
+    int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)n * k + 4);
+    float* w = (float*)malloc(sizeof(float) * (size_t)n * k + 4);
+    float* y = (float*)malloc(sizeof(float) * ((size_t)n * k * H + 1));
+#pragma omp parallel num_threads(nt)
+    {
+        float* keys = (float*)malloc(sizeof(float) * (size_t)E * 2);
+        unsigned char* taken = (unsigned char*)malloc((size_t)E);
+        double* act_d = (double*)malloc(sizeof(double) * (size_t)F);
+#pragma omp for schedule(dynamic, 1)
+        for (int r = 0; r < n * k; ++r) {
+            int i = r / k, j = r % k;
+            const uint16_t* xrow = x + (int64_t)tokens[i] * H;
+            int32_t sel[16];
+            float wsel[16];
+            route_one(xrow, wr, bias, H, E, k, score, renorm, sel, wsel,
+                      (j == 0 && gap_o) ? gap_o + i : NULL, keys, keys + E, taken);
+            if (j == 0)
+                for (int q = 0; q < k; ++q) {
+                    ids[(int64_t)i * k + q] = sel[q];
+                    w[(int64_t)i * k + q] = wsel[q];
+                }
+            expert_one(xrow, sel[j], H, F, wg, wu, wd, NULL, y + (int64_t)r * H, act_d);
+        }
+        free(keys); free(taken); free(act_d);
+    }
+    orc_combine(n, H, k, y, w, out);
+    if (ids_o) memcpy(ids_o, ids, sizeof(int32_t) * (size_t)n * k);
+    if (w_o) memcpy(w_o, w, sizeof(float) * (size_t)n * k);
+    free(ids); free(w); free(y);
+    return 0;
+}

@@ -1,0 +1,204 @@
+"""ctypes wrapper of the CPU oracle (oracle/moe_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, the smoke check and the
+benchmark's CPU-baseline leg.  It never imports the HIP library or its
+binding, and the product path never imports it.
+
+All arrays are numpy; bf16 tensors travel as uint16 bit patterns.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libmoe_oracle.so")
+_lib = None
+
+SOFTMAX = 0
+SIGMOID = 1
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            # the checker is plain C; build it on first use if nobody has
+            from oracle import build as _b
+            _b.build(verbose=False)
+        _lib = ctypes.CDLL(_LIB_PATH)
+        _declare(_lib)
+    return _lib
+
+
+def _declare(L):
+    P = ctypes.c_void_p
+    i32 = ctypes.c_int
+    i64 = ctypes.c_int64
+    L.orc_bf16_to_f32.restype = ctypes.c_float
+    L.orc_bf16_to_f32.argtypes = [ctypes.c_uint16]
+    L.orc_f32_to_bf16.restype = ctypes.c_uint16
+    L.orc_f32_to_bf16.argtypes = [ctypes.c_float]
+    L.orc_f32_to_bf16_array.argtypes = [P, P, i64]
+    L.orc_max_threads.restype = i32
+    L.orc_router_logits.argtypes = [i32, i32, i32, P, P, P, i32]
+    L.orc_topk_keys.argtypes = [i32, i32, i32, P, P]
+    L.orc_route.restype = i32
+    L.orc_route.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, i32]
+    L.orc_permute.restype = i32
+    L.orc_permute.argtypes = [i32, i32, P, P, P, P, P]
+    L.orc_expert_ffn.restype = i32
+    L.orc_expert_ffn.argtypes = [i32, P, P, i32, i32, i32, P, P, P, P, P, P, i32]
+    L.orc_combine.argtypes = [i32, i32, i32, P, P, P]
+    L.orc_forward.restype = i32
+    L.orc_forward.argtypes = [i32, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P,
+                              P, P, P, P, P, P, P, P, i32]
+    L.orc_forward_tokens.restype = i32
+    L.orc_forward_tokens.argtypes = [i32, P, i32, i32, i32, i32, i32, i32, P, P, P, P, P,
+                                     P, P, P, P, P, i32]
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _u16(a):
+    a = np.ascontiguousarray(a)
+    assert a.dtype == np.uint16, a.dtype
+    return a
+
+
+def _c(a, dt):
+    return np.ascontiguousarray(a, dtype=dt)
+
+
+def max_threads() -> int:
+    return int(lib().orc_max_threads())
+
+
+def f32_to_bf16(v) -> np.ndarray:
+    v = _c(v, np.float32)
+    out = np.empty(v.shape, dtype=np.uint16)
+    lib().orc_f32_to_bf16_array(_p(v), _p(out), v.size)
+    return out
+
+
+def bf16_to_f32(b) -> np.ndarray:
+    b = _u16(b)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def router_logits(x, wr, nthreads=0) -> np.ndarray:
+    x, wr = _u16(x), _u16(wr)
+    T, H = x.shape
+    E = wr.shape[0]
+    out = np.empty((T, E), dtype=np.float32)
+    lib().orc_router_logits(T, H, E, _p(x), _p(wr), _p(out), nthreads)
+    return out
+
+
+def topk_keys(keys, k) -> np.ndarray:
+    keys = _c(keys, np.float32)
+    n, E = keys.shape
+    ids = np.empty((n, k), dtype=np.int32)
+    lib().orc_topk_keys(n, E, k, _p(keys), _p(ids))
+    return ids
+
+
+def route(x, wr, k, score, renorm=True, bias=None, nthreads=0):
+    """-> (ids [T,k] int32, w [T,k] fp32, gap [T] fp64)"""
+    x, wr = _u16(x), _u16(wr)
+    T, H = x.shape
+    E = wr.shape[0]
+    b = None if bias is None else _c(bias, np.float32)
+    ids = np.empty((T, k), dtype=np.int32)
+    w = np.empty((T, k), dtype=np.float32)
+    gap = np.empty((T,), dtype=np.float64)
+    rc = lib().orc_route(T, H, E, k, score, int(renorm), _p(x), _p(wr), _p(b), _p(ids), _p(w),
+                         _p(gap), nthreads)
+    if rc != 0:
+        raise ValueError(f"orc_route rc={rc}")
+    return ids, w, gap
+
+
+def permute(ids, E):
+    """-> (counts [E], offsets [E+1], perm [A], inv_perm [A]) all int32"""
+    ids = _c(ids, np.int32).reshape(-1)
+    A = ids.size
+    counts = np.empty(E, dtype=np.int32)
+    offsets = np.empty(E + 1, dtype=np.int32)
+    perm = np.empty(A, dtype=np.int32)
+    inv = np.empty(A, dtype=np.int32)
+    rc = lib().orc_permute(A, E, _p(ids), _p(counts), _p(offsets), _p(perm), _p(inv))
+    if rc != 0:
+        raise ValueError(f"orc_permute rc={rc}")
+    return counts, offsets, perm, inv
+
+
+def expert_ffn(tokens, experts, x, wg, wu, wd, want_act=False, nthreads=0):
+    """(token, expert) pairs -> y [n,H] fp32 (and act [n,F] bf16 bits)."""
+    x, wg, wu, wd = _u16(x), _u16(wg), _u16(wu), _u16(wd)
+    tokens = _c(tokens, np.int32).reshape(-1)
+    experts = _c(experts, np.int32).reshape(-1)
+    n = tokens.size
+    H = x.shape[1]
+    E, F = wg.shape[0], wg.shape[1]
+    y = np.empty((n, H), dtype=np.float32)
+    act = np.empty((n, F), dtype=np.uint16) if want_act else None
+    rc = lib().orc_expert_ffn(n, _p(tokens), _p(experts), H, E, F, _p(x), _p(wg), _p(wu),
+                              _p(wd), _p(act), _p(y), nthreads)
+    if rc != 0:
+        raise ValueError(f"orc_expert_ffn rc={rc}")
+    return (y, act) if want_act else y
+
+
+def combine(y, w, T, H, k) -> np.ndarray:
+    y = _c(y, np.float32)
+    w = _c(w, np.float32)
+    assert y.size == T * k * H and w.size == T * k
+    out = np.empty((T, H), dtype=np.uint16)
+    lib().orc_combine(T, H, k, _p(y), _p(w), _p(out))
+    return out
+
+
+def forward(x, wr, wg, wu, wd, k, score, renorm=True, bias=None, nthreads=0, want_y=True):
+    """The whole layer in the method's order.  Returns a dict of numpy arrays."""
+    x, wr, wg, wu, wd = _u16(x), _u16(wr), _u16(wg), _u16(wu), _u16(wd)
+    T, H = x.shape
+    E, F = wg.shape[0], wg.shape[1]
+    A = T * k
+    b = None if bias is None else _c(bias, np.float32)
+    r = dict(out=np.empty((T, H), dtype=np.uint16), ids=np.empty((T, k), dtype=np.int32),
+             w=np.empty((T, k), dtype=np.float32), gap=np.empty(T, dtype=np.float64),
+             counts=np.empty(E, dtype=np.int32), offsets=np.empty(E + 1, dtype=np.int32),
+             perm=np.empty(A, dtype=np.int32), inv_perm=np.empty(A, dtype=np.int32),
+             y=np.empty((A, H), dtype=np.float32) if want_y else None)
+    rc = lib().orc_forward(T, H, E, F, k, score, int(renorm), _p(x), _p(wr), _p(b), _p(wg),
+                           _p(wu), _p(wd), _p(r["out"]), _p(r["ids"]), _p(r["w"]),
+                           _p(r["gap"]), _p(r["counts"]), _p(r["offsets"]), _p(r["perm"]),
+                           _p(r["inv_perm"]), _p(r["y"]), nthreads)
+    if rc != 0:
+        raise ValueError(f"orc_forward rc={rc}")
+    return r
+
+
+def forward_tokens(tokens, x, wr, wg, wu, wd, k, score, renorm=True, bias=None, nthreads=0):
+    """Per-token evaluation of the chosen rows.  -> (out [n,H] bf16 bits, ids, w, gap)"""
+    x, wr, wg, wu, wd = _u16(x), _u16(wr), _u16(wg), _u16(wu), _u16(wd)
+    tokens = _c(tokens, np.int32).reshape(-1)
+    n = tokens.size
+    H = x.shape[1]
+    E, F = wg.shape[0], wg.shape[1]
+    b = None if bias is None else _c(bias, np.float32)
+    out = np.empty((n, H), dtype=np.uint16)
+    ids = np.empty((n, k), dtype=np.int32)
+    w = np.empty((n, k), dtype=np.float32)
+    gap = np.empty(n, dtype=np.float64)
+    rc = lib().orc_forward_tokens(n, _p(tokens), H, E, F, k, score, int(renorm), _p(x), _p(wr),
+                                  _p(b), _p(wg), _p(wu), _p(wd), _p(out), _p(ids), _p(w),
+                                  _p(gap), nthreads)
+    if rc != 0:
+        raise ValueError(f"orc_forward_tokens rc={rc}")
+    return out, ids, w, gap
