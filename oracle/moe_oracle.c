@@ -29,10 +29,15 @@
  *
  * The pages never write the layer's formula.  The definition implemented here
  * (steps D1..D7) is the plainest reading consistent with them:
- *   D1 l[t,e]  = fp32 chain over i = 0..H-1 ascending: acc = fma(x, w, acc)
- *               (bf16 x bf16 products are exact in fp32, so this is also the
- *               plain multiply-then-add chain).  The logit decides an integer
- *               (the expert set), so it is taken in the kernel's precision.
+ *   D1 l[t,e]:  i = 0..H-1 is cut into chunks of 256 consecutive indices
+ *               (the last may be shorter).  Each chunk is an fp32 chain in
+ *               ascending i from +0: s = fma(x_i, w_i, s) (bf16 x bf16
+ *               products are exact in fp32, so this equals multiply-then-add);
+ *               then l = +0, l = l + s_c for c ascending, in fp32.  The logit
+ *               decides an integer (the expert set), so it is taken in the
+ *               kernel's precision and in one fixed order.  The pages fix no
+ *               order; the chunked one lets the many short chains of a small
+ *               batch run in parallel.
  *   D2 keys:   softmax -> key_e = l_e (softmax is strictly increasing, so the
  *               top-k of the logits is the top-k of the exact probabilities);
  *               sigmoid -> key_e = fp32(1/(1+expf(-l_e))) + bias_e in fp32.
@@ -115,12 +120,19 @@ int orc_max_threads(void) { return set_threads(0); }
 /* D1: router logits                                                         */
 /* ------------------------------------------------------------------------ */
 
+#define ORC_LOGIT_CHUNK 256
+
 static float logit_one(const uint16_t* xrow, const uint16_t* wrow, int H)
 {
-    float acc = 0.0f;
-    for (int i = 0; i < H; ++i)
-        acc = fmaf(orc_bf16_to_f32(xrow[i]), orc_bf16_to_f32(wrow[i]), acc);
-    return acc;
+    float total = 0.0f;
+    for (int c0 = 0; c0 < H; c0 += ORC_LOGIT_CHUNK) {
+        int c1 = c0 + ORC_LOGIT_CHUNK < H ? c0 + ORC_LOGIT_CHUNK : H;
+        float s = 0.0f;
+        for (int i = c0; i < c1; ++i)
+            s = fmaf(orc_bf16_to_f32(xrow[i]), orc_bf16_to_f32(wrow[i]), s);
+        total = total + s;
+    }
+    return total;
 }
 
 void orc_router_logits(int T, int H, int E, const uint16_t* x, const uint16_t* wr,

@@ -64,13 +64,16 @@ def test_bf16_rounding_matches_torch_rne():
 # D1 router logits
 # --------------------------------------------------------------------------
 
-def test_logits_equal_sequential_fp32_sum():
-    """Logits are the ascending-i fp32 running sum of the (exact) products.
+@pytest.mark.parametrize("H", [64, 256, 960, 2048])
+def test_logits_equal_chunked_sequential_fp32_sum(H):
+    """Logits: ascending fp32 running sums over 256-wide chunks of i, then an
+    ascending fp32 running sum of the chunk sums.
 
-    numpy's cumulative sum in float32 adds left to right, one rounding per
-    step; bf16 x bf16 products are exact in fp32.
+    numpy's cumulative sum in float32 adds left to right with one rounding per
+    step; bf16 x bf16 products are exact in fp32.  H = 960 has a short last
+    chunk.
     """
-    cfg = I.scaled(I.CONFIGS["mid"], T=8, H=512, E=16)
+    cfg = I.scaled(I.CONFIGS["mid"], T=6, H=H, E=16)
     L = I.make_layer(cfg)
     x = I.make_x(cfg)
     got = O.router_logits(bits(x), bits(L["w_router"]))
@@ -80,8 +83,14 @@ def test_logits_equal_sequential_fp32_sum():
         for e in range(cfg.E):
             prod = (xf[t] * wf[e]).astype(np.float32)
             assert np.array_equal(prod.astype(np.float64), xf[t].astype(np.float64) * wf[e])
-            ref = np.cumsum(prod, dtype=np.float32)[-1]
+            parts = [np.cumsum(prod[c:c + 256], dtype=np.float32)[-1] for c in range(0, H, 256)]
+            ref = np.cumsum(np.array(parts, dtype=np.float32), dtype=np.float32)[-1]
             assert got[t, e].view(np.uint32) == np.float32(ref).view(np.uint32), (t, e)
+    # the order is not arbitrary: a single running sum differs somewhere
+    if H > 256:
+        single = np.array([[np.cumsum((xf[t] * wf[e]).astype(np.float32), dtype=np.float32)[-1]
+                            for e in range(cfg.E)] for t in range(cfg.T)], dtype=np.float32)
+        assert not np.array_equal(single.view(np.uint32), got.view(np.uint32))
 
 
 def test_logits_within_recursive_summation_bound():
