@@ -348,6 +348,31 @@ int orc_expert_ffn(int n, const int32_t* tokens, const int32_t* experts,
     return 0;
 }
 
+/* The down projection of D6 alone, on given act codes: n rows, row r uses
+ * expert experts[r] and act[r, :] (bf16 bits); y[r,h] = fp32(sum_f act Wd)
+ * with an fp64 sum.  Lets a test check the second expert GEMM on the first
+ * one's output. */
+int orc_expert_down(int n, const int32_t* experts, int H, int E, int F,
+                    const uint16_t* act, const uint16_t* wd, float* y, int nthreads)
+{
+    for (int r = 0; r < n; ++r)
+        if (experts[r] < 0 || experts[r] >= E) return -2;
+    int nt = set_threads(nthreads);
+    (void)nt;
+#pragma omp parallel for num_threads(nt) schedule(dynamic, 1)
+    for (int r = 0; r < n; ++r) {
+        const uint16_t* D = wd + (int64_t)experts[r] * H * F;
+        const uint16_t* a = act + (int64_t)r * F;
+        for (int h = 0; h < H; ++h) {
+            double acc = 0.0;
+            for (int f = 0; f < F; ++f)
+                acc += (double)orc_bf16_to_f32(a[f]) * (double)orc_bf16_to_f32(D[(int64_t)h * F + f]);
+            y[(int64_t)r * H + h] = (float)acc;
+        }
+    }
+    return 0;
+}
+
 /* ------------------------------------------------------------------------ */
 /* D7: fixed-order fp32 combine                                              */
 /* ------------------------------------------------------------------------ */

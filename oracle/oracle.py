@@ -51,6 +51,8 @@ def _declare(L):
     L.orc_permute.argtypes = [i32, i32, P, P, P, P, P]
     L.orc_expert_ffn.restype = i32
     L.orc_expert_ffn.argtypes = [i32, P, P, i32, i32, i32, P, P, P, P, P, P, i32]
+    L.orc_expert_down.restype = i32
+    L.orc_expert_down.argtypes = [i32, P, i32, i32, i32, P, P, P, i32]
     L.orc_combine.argtypes = [i32, i32, i32, P, P, P]
     L.orc_forward.restype = i32
     L.orc_forward.argtypes = [i32, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P,
@@ -152,6 +154,20 @@ def expert_ffn(tokens, experts, x, wg, wu, wd, want_act=False, nthreads=0):
     if rc != 0:
         raise ValueError(f"orc_expert_ffn rc={rc}")
     return (y, act) if want_act else y
+
+
+def expert_down(experts, act, wd, nthreads=0) -> np.ndarray:
+    """Down projection of given act rows (bf16 bits [n,F]) -> y [n,H] fp32."""
+    act, wd = _u16(act), _u16(wd)
+    experts = _c(experts, np.int32).reshape(-1)
+    n, F = act.shape
+    E, H = wd.shape[0], wd.shape[1]
+    assert wd.shape[2] == F and experts.size == n
+    y = np.empty((n, H), dtype=np.float32)
+    rc = lib().orc_expert_down(n, _p(experts), H, E, F, _p(act), _p(wd), _p(y), nthreads)
+    if rc != 0:
+        raise ValueError(f"orc_expert_down rc={rc}")
+    return y
 
 
 def combine(y, w, T, H, k) -> np.ndarray:

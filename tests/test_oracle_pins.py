@@ -347,6 +347,23 @@ def test_expert_error_within_bound():
         assert np.all(np.abs(y[r] - exact) <= bound + 1e-30)
 
 
+def test_down_step_alone_matches_full_ffn():
+    """Down projection on the FFN's own act codes reproduces the FFN's y bitwise,
+    and equals a torch fp64 matmul of those codes within one fp32 rounding."""
+    cfg = I.scaled(I.CONFIGS["tiny"], T=6, E=3, k=1)
+    L = I.make_layer(cfg)
+    x = I.make_x(cfg)
+    experts = np.array([0, 1, 2, 2, 1, 0])
+    y, act = O.expert_ffn(np.arange(6), experts, bits(x), bits(L["w_gate"]), bits(L["w_up"]),
+                          bits(L["w_down"]), want_act=True)
+    y2 = O.expert_down(experts, act, bits(L["w_down"]))
+    assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+    a = torch.from_numpy(O.bf16_to_f32(act).astype(np.float64))
+    for r in range(6):
+        ref = (L["w_down"][experts[r]].double() @ a[r]).numpy()
+        assert np.all(np.abs(y2[r] - ref) <= np.abs(ref) * U + 1e-12)
+
+
 # --------------------------------------------------------------------------
 # D7 combine
 # --------------------------------------------------------------------------
