@@ -1,0 +1,225 @@
+#!/usr/bin/env python3
+"""Benchmark of the batch-invariant MoE layer forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload large|mid|tie|dec|tiny]
+
+One step is one pass of the whole path (route, permute, gate/up + SwiGLU,
+down, combine) over one synthetic batch that is already resident in HBM.  The
+step is enqueued as the five C entry points that moe_forward chains (checked
+bitwise against moe_forward before timing), so HIP events on the launch stream
+can time each stage inside the timed region.
+
+Prints one JSON line: tokens/s, the dominant kernel's roofline fraction, the
+oracle's CPU baseline on a bounded sample, and the batch-invariance check of
+16 probe tokens embedded in the batch (differing bits against each probe
+alone; must be 0).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+METRIC = "MoE-layer tokens/s + MFMA util; bitwise-identical output across batch sizes"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="large", choices=["large", "mid", "tie", "dec", "tiny"])
+    ap.add_argument("--T", type=int, default=None, help="override the workload's token count")
+    ap.add_argument("--variant", type=int, default=0, help="0 invariant, 1 split-K variant")
+    ap.add_argument("--cpu-sample", type=int, default=None,
+                    help="tokens of the oracle CPU baseline (0 disables)")
+    ap.add_argument("--no-check", action="store_true", help="skip the probe invariance check")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only (the MoE layer forward on one "
+              "MI355X); --gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from serve_router_gemm_amd import inputs as I
+    from serve_router_gemm_amd import moe as M
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    M.lib()   # fail loudly if libmoe.so is missing
+    dev = "cuda"
+
+    cfg = I.CONFIGS[args.workload]
+    if args.T is not None:
+        cfg = I.scaled(cfg, T=args.T)
+    T, H, E, F, k = cfg.T, cfg.H, cfg.E, cfg.F, cfg.k
+    A = T * k
+    log(f"[bench] workload {I.describe(cfg)}")
+    t0 = time.time()
+    L = I.make_layer(cfg, dev)
+    x = I.make_x(cfg, dev)
+    probes = I.probes(H, 16, dev)
+    n_probe = min(16, T)
+    if T >= 16:
+        x, probe_pos = I.embed_probes(probes, T, rep=0)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs ready in {time.time() - t0:.1f}s")
+
+    bias = L["bias"]
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(A, dtype=torch.int32, device=dev)
+    inv = torch.empty(A, dtype=torch.int32, device=dev)
+    h_act = torch.empty((A, F), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((A, H), dtype=torch.float32, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    ws_r = M.workspace(M.OP_ROUTE, T, H, E, F, k)
+    ws_p = M.workspace(M.OP_PERMUTE, T, H, E, F, k)
+    ws_g = M.workspace(M.OP_GATE_UP, T, H, E, F, k)
+    ws_d = M.workspace(M.OP_DOWN, T, H, E, F, k, args.variant)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        M.route(x, L["w_router"], k, cfg.score, cfg.renorm, bias=bias, topk_ids=ids, topk_w=w,
+                ws=ws_r)
+        if ev is not None:
+            ev[1].record(stream)
+        M.permute(ids, E, counts, offsets, perm, inv, ws=ws_p)
+        if ev is not None:
+            ev[2].record(stream)
+        M.expert_gate_up(x, perm, offsets, L["w_gate"], L["w_up"], k, h_act=h_act, ws=ws_g)
+        if ev is not None:
+            ev[3].record(stream)
+        M.expert_down(h_act, perm, offsets, L["w_down"], k, variant=args.variant, y=y, ws=ws_d)
+        if ev is not None:
+            ev[4].record(stream)
+        M.combine(y, w, out=out)
+        if ev is not None:
+            ev[5].record(stream)
+
+    # the staged step is moe_forward: check once, bitwise
+    step()
+    ref = M.forward(x, L["w_router"], L["w_gate"], L["w_up"], L["w_down"], k, cfg.score,
+                    cfg.renorm, bias=bias, variant=args.variant)
+    torch.cuda.synchronize()
+    if args.variant == 0:
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), \
+            "staged step differs from moe_forward"
+    del ref
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(K):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    names = ["route", "permute", "gate_up", "down", "combine"]
+    stage_ms = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(K)]))
+                for j, n in enumerate(names)}
+    ms_step = wall * 1000.0 / K
+    value = T / (ms_step / 1000.0)
+
+    counts_np = counts.cpu().numpy()
+    gu_flops = 4.0 * A * H * F
+    dn_flops = 2.0 * A * H * F
+    gu_tflops = gu_flops / (stage_ms["gate_up"] * 1e-3) / 1e12
+    grouped_tflops = (gu_flops + dn_flops) / ((stage_ms["gate_up"] + stage_ms["down"]) * 1e-3) / 1e12
+    comb_bytes = 4.0 * A * H + 4.0 * A + 2.0 * T * H
+    comb_gbs = comb_bytes / (stage_ms["combine"] * 1e-3) / 1e9
+
+    # batch invariance of the embedded probes: each probe alone (T = 1) vs in the batch
+    inv_bits = None
+    if not args.no_check and args.variant == 0:
+        batch_bits = out.view(torch.int16).cpu().numpy()
+        nd = 0
+        for i in range(n_probe):
+            o1 = M.forward(probes[i:i + 1].contiguous(), L["w_router"], L["w_gate"], L["w_up"],
+                           L["w_down"], k, cfg.score, cfg.renorm, bias=bias)
+            a = o1.view(torch.int16).cpu().numpy()[0]
+            b = batch_bits[probe_pos[i]] if T >= 16 else batch_bits[0]
+            nd += int(np.unpackbits(np.bitwise_xor(a, b).view(np.uint8)).sum())
+        inv_bits = nd
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: T={T} H={H} E={E} top-{k} F={F} "
+                               f"{'sigmoid+Zipf(1.2) bias' if cfg.score else 'softmax'}"
+                               f"{' renorm' if cfg.renorm else ''}",
+                   "variant": "invariant" if args.variant == 0 else "splitk",
+                   "active_experts": int((counts_np > 0).sum()),
+                   "max_expert_tokens": int(counts_np.max())},
+        "roofline": {"kernel": "expert_gemm_kernel<gate_up> (moe_expert_gate_up)",
+                     "bound": "mfma", "achieved": round(gu_tflops, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(gu_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "stages_ms": {n: round(v, 4) for n, v in stage_ms.items()},
+        "grouped_gemm_tflops": round(grouped_tflops, 2),
+        "grouped_gemm_mfma_frac": round(grouped_tflops / PEAK_BF16_TFLOPS, 4),
+        "combine_hbm_frac": round(comb_gbs / PEAK_HBM_GBS, 4),
+        "probe_bits_differing": inv_bits,
+    }
+
+    # oracle on the host cores, bounded sample of the same workload
+    nsample = args.cpu_sample
+    if nsample is None:
+        nsample = {"large": 96, "dec": 32, "tie": 96, "mid": 256, "tiny": 64}[cfg.name]
+    nsample = min(nsample, T)
+    if nsample > 0:
+        from oracle import oracle as O
+        xb = I.bf16_bits(x)
+        hb = {n: I.bf16_bits(t) for n, t in L.items() if t is not None and t.dtype == torch.bfloat16}
+        bias_np = bias.cpu().numpy() if bias is not None else None
+        rows = np.sort(np.random.default_rng(0).choice(T, nsample, replace=False))
+        c0 = time.perf_counter()
+        O.forward_tokens(rows, xb, hb["w_router"], hb["w_gate"], hb["w_up"], hb["w_down"], k,
+                         cfg.score, cfg.renorm, bias=bias_np)
+        cdt = time.perf_counter() - c0
+        res["cpu_baseline"] = {"value": round(nsample / cdt, 3), "unit": "tokens/s",
+                               "cores": O.max_threads(), "kind": "oracle",
+                               "sample": f"{nsample} of the {T} tokens, whole layer per token "
+                                         f"(route over all {E} experts, {k} expert FFNs, "
+                                         f"combine), {cdt:.1f}s"}
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

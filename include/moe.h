@@ -1,0 +1,199 @@
+/*
+ * moe.h -- C ABI of the batch-invariant Mixture-of-Experts layer forward for
+ * AMD Instinct MI355X (gfx950).  Library: libmoe.so.
+ *
+ * What the library guarantees.  For one layer shape (H, E, F, top_k, score,
+ * renormalize) and the invariant GEMM variant, every token's rows of
+ * `topk_ids`, `topk_w` and `out` are bit-identical whatever the number of
+ * tokens in the call, whichever other tokens share it, and wherever the
+ * token sits in it.  Sources on the pages:
+ *   - Fireworks page "位级一致：前沿训练的差异化关键" (bit-level agreement),
+ *     section "曾经只有前沿实验室才有的功能": batch invariance is a request
+ *     getting the same result whatever else shares its batch; the MoE router
+ *     and the expert GEMMs are reductions that must stay consistent; split-K
+ *     breaks invariance.
+ *   - Same page, section "为什么比特级一致是一个复杂的问题": per-expert matmul
+ *     kernels that change with the expert's token count, and router near-ties,
+ *     both move bits; the fix is one expert-matmul kernel choice whatever the
+ *     token count and a deterministic router tie-break.
+ *   - Fireworks page on numerical alignment and MoE routing, section
+ *     "混合专家模型更难对齐": the precision and the order of the weighted sum of
+ *     the expert outputs must both be fixed.
+ *   - "GLM Post-Training Beyond SFT", section "迁移到 NPU 时": a top-k must fix
+ *     boundary ties, stability, NaN handling and the index dtype.
+ *
+ * The layer (the pages give no formula; this is the reading the library
+ * implements):
+ *   logits  l[t,e] = sum_i x[t,i] * w_router[e,i] in fp32 and in one fixed
+ *           order: i in chunks of 256, each chunk an ascending chain of fp32
+ *           fmas from +0 (bf16*bf16 products are exact), chunk sums added to
+ *           +0 in ascending chunk order.
+ *   select  softmax: key = l;  sigmoid: key = fp32(1/(1+exp(-l))) + bias[e].
+ *           top_k experts by key descending, ties to the lower expert index,
+ *           -0 == +0, NaN keys last (NaNs by index).  Slot j = j-th selected.
+ *   weights softmax p = exp(l - max l) / sum exp(...) over all E experts;
+ *           sigmoid p = 1/(1+exp(-l)) (bias excluded); renormalize: w_j =
+ *           p_j / sum_j p_j, else w_j = p_j.  fp32.
+ *   permute a = t*top_k + j is an assignment; perm lists assignments grouped
+ *           by expert ascending and, inside an expert, by a ascending.
+ *   experts act = bf16(silu(x W_gate[e]^T) * (x W_up[e]^T)),
+ *           y[a] = act W_down[e]^T in fp32 (not rounded).  bf16 MFMA, fp32
+ *           accumulate, one MFMA instruction and one ascending K order for
+ *           every tile of every expert, no split-K (invariant variant).
+ *   combine acc = 0; for j = 0..top_k-1: acc = fmaf(w[t,j], y[t*top_k+j,h], acc);
+ *           out[t,h] = bf16(acc) (round to nearest even).
+ *
+ * Conventions for every entry point.
+ *   - Pointers marked [device] are device pointers (hipMalloc'd or equivalent
+ *     coarse-grained memory) and must be 16-byte aligned.  [host] pointers
+ *     are host memory.  bf16 tensors are passed as uint16_t bit patterns.
+ *   - Row-major layouts, K contiguous:
+ *       x [T,H], w_router [E,H], w_gate [E,F,H], w_up [E,F,H], w_down [E,H,F],
+ *       bias [E] fp32, topk_ids [T,k] int32, topk_w [T,k] fp32,
+ *       expert_counts [E], expert_offsets [E+1], perm [T*k], inv_perm [T*k]
+ *       (int32), h_act [T*k,F] bf16 (rows in perm order), y [T*k,H] fp32
+ *       (rows in assignment order a = t*k + j), out [T,H] bf16.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *     enqueues work on that stream and returns; it never synchronizes,
+ *     allocates, frees, prints or aborts, and keeps no state between calls.
+ *     The caller owns every buffer; outputs are fully overwritten.
+ *   - `ws` is caller-owned device scratch of at least moe_workspace_bytes()
+ *     bytes for the same op and sizes; it may be NULL when that size is 0.
+ *     Its contents on entry do not matter.  Calls that overlap in time on
+ *     different streams must use different workspaces.
+ *   - Every argument is checked on the host before anything is enqueued; a
+ *     failed check enqueues nothing and returns a negative moe_status.  T == 0
+ *     is valid and enqueues nothing.  A launch failure returns MOE_ERR_HIP.
+ *   - Limits: 1 <= E <= 512; 1 <= top_k <= min(E, 16); H and F multiples of
+ *     64 in [64, 65536]; 0 <= T; T*top_k <= 2^24 and T*top_k*max(H,F) < 2^31.
+ *   - Thread-safe and reentrant (no global mutable state).
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_NULL = -1,        /* a required pointer is NULL */
+    MOE_ERR_SHAPE = -2,       /* a size is out of range (see Limits) */
+    MOE_ERR_ALIGN = -3,       /* a device pointer is not 16-byte aligned */
+    MOE_ERR_UNSUPPORTED = -4, /* H or F not a multiple of 64, bad enum value */
+    MOE_ERR_WORKSPACE = -5,   /* ws_bytes smaller than moe_workspace_bytes() */
+    MOE_ERR_HIP = -6          /* the HIP runtime reported a launch error */
+} moe_status;
+
+typedef enum moe_score_fn {
+    MOE_SCORE_SOFTMAX = 0,
+    MOE_SCORE_SIGMOID = 1
+} moe_score_fn;
+
+typedef enum moe_gemm_variant {
+    /* fixed tile, one MFMA instruction, ascending K, no split-K */
+    MOE_GEMM_INVARIANT = 0,
+    /* deliberately NOT batch-invariant: the down projection of an expert is
+     * split along K into a number of parts chosen from that expert's token
+     * count, and the parts are summed with fp32 atomics.  Exists to show the
+     * drift that load-dependent kernels cause and to measure what invariance
+     * costs. */
+    MOE_GEMM_SPLITK_VARIANT = 1
+} moe_gemm_variant;
+
+typedef enum moe_op {
+    MOE_OP_ROUTE = 0,
+    MOE_OP_PERMUTE = 1,
+    MOE_OP_GATE_UP = 2,
+    MOE_OP_DOWN = 3,
+    MOE_OP_GROUPED_SWIGLU = 4,
+    MOE_OP_COMBINE = 5,
+    MOE_OP_FORWARD = 6
+} moe_op;
+
+/* Bytes of device scratch the entry point `op` needs for these sizes
+ * (0 when it needs none).  Host only; never touches the GPU.  Returns 0 for
+ * sizes that the entry point would reject. */
+size_t moe_workspace_bytes(int op, int T, int H, int E, int F, int top_k, int variant);
+
+/* Static description of a status code.  Host only. */
+const char* moe_status_string(int status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int moe_version(void);
+
+/* Router: logits, selection and weights (the "route" step).
+ *   x [device] [T,H] bf16; w_router [device] [E,H] bf16;
+ *   bias [device] [E] fp32 or NULL (sigmoid only: NULL means all zero; a
+ *   non-NULL bias with softmax is rejected with MOE_ERR_UNSUPPORTED);
+ *   topk_ids [device] out [T,k] int32; topk_w [device] out [T,k] fp32.
+ * score: moe_score_fn.  renormalize: 0 or 1.  ws holds partial logits. */
+int moe_route(int T, int H, int E, int top_k, int score, int renormalize,
+              const uint16_t* x, const uint16_t* w_router, const float* bias,
+              int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes, void* stream);
+
+/* Expert histogram, offsets and the stable permutation (the "permute" step).
+ *   topk_ids [device] [T,k] int32 with values in [0,E) (other values are
+ *   skipped: not counted and not placed, and the tail of perm is then left
+ *   unwritten);
+ *   expert_counts [device] out [E]; expert_offsets [device] out [E+1]
+ *   (exclusive prefix sum, offsets[E] = number of placed assignments);
+ *   perm [device] out [T*k]: perm[p] = assignment id at permuted position p;
+ *   inv_perm [device] out [T*k]: inv_perm[perm[p]] = p (-1 if skipped). */
+int moe_permute(int T, int E, int top_k, const int32_t* topk_ids,
+                int32_t* expert_counts, int32_t* expert_offsets, int32_t* perm,
+                int32_t* inv_perm, void* ws, size_t ws_bytes, void* stream);
+
+/* Gate/up projections with the SwiGLU epilogue, grouped by expert (the
+ * first expert GEMM).  For every permuted row p of expert e:
+ *   h_act[p, f] = bf16(silu(g) * u), g = x[perm[p]/k] . w_gate[e,f,:],
+ *   u = x[perm[p]/k] . w_up[e,f,:], fp32 accumulation.
+ *   x [device] [T,H]; perm, expert_offsets [device] from moe_permute;
+ *   w_gate, w_up [device] [E,F,H]; h_act [device] out [T*k,F] bf16.
+ * Always the invariant kernel. */
+int moe_expert_gate_up(int T, int H, int E, int F, int top_k, const uint16_t* x,
+                       const int32_t* perm, const int32_t* expert_offsets,
+                       const uint16_t* w_gate, const uint16_t* w_up, uint16_t* h_act,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* Down projection grouped by expert (the second expert GEMM): for every
+ * permuted row p of expert e, y[perm[p], h] = h_act[p,:] . w_down[e,h,:] in
+ * fp32, written to assignment order.
+ *   h_act [device] [T*k,F] bf16; w_down [device] [E,H,F]; y [device] out
+ *   [T*k,H] fp32.  variant: moe_gemm_variant. */
+int moe_expert_down(int T, int H, int E, int F, int top_k, const uint16_t* h_act,
+                    const int32_t* perm, const int32_t* expert_offsets,
+                    const uint16_t* w_down, float* y, int variant,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* Both expert GEMMs: moe_expert_gate_up then moe_expert_down, with h_act
+ * kept in the workspace. */
+int moe_grouped_swiglu(int T, int H, int E, int F, int top_k, const uint16_t* x,
+                       const int32_t* perm, const int32_t* expert_offsets,
+                       const uint16_t* w_gate, const uint16_t* w_up,
+                       const uint16_t* w_down, float* y, int variant,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* Fixed-order fp32 weighted combine (the "combine" step):
+ *   out[t,h] = bf16(fma chain over j = 0..k-1 of topk_w[t,j] * y[t*k+j,h]).
+ *   y [device] [T*k,H] fp32; topk_w [device] [T,k]; out [device] out [T,H]. */
+int moe_combine(int T, int H, int top_k, const float* y, const float* topk_w,
+                uint16_t* out, void* stream);
+
+/* The whole layer: route, permute, both expert GEMMs, combine, enqueued in
+ * that order on `stream`.  topk_ids / topk_w may be NULL (then they live in
+ * the workspace); when given they receive the routing. */
+int moe_forward(int T, int H, int E, int F, int top_k, int score, int renormalize,
+                const uint16_t* x, const uint16_t* w_router, const float* bias,
+                const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
+                uint16_t* out, int32_t* topk_ids, float* topk_w, int variant,
+                void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

@@ -1,0 +1,52 @@
+"""Build libmoe.so (the HIP library behind include/moe.h) for gfx950, in-tree.
+
+    python -m serve_router_gemm_amd.build
+"""
+from __future__ import annotations
+
+import glob
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+LIB = os.path.join(PKG, "libmoe.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+
+def sources():
+    return sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
+
+
+def command(out: str, extra=()) -> list:
+    # -ffp-contract=off: every fused multiply-add is written out (fmaf / MFMA);
+    #   the compiler fuses nothing on its own, so each rounding step is explicit.
+    # -packed-fp32-ops off: no v_pk_* fp32 instructions are generated.
+    return [HIPCC, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+            "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include"),
+            *extra, "-o", out, *sources()]
+
+
+def build(verbose: bool = True) -> str:
+    tmp = LIB + ".tmp"
+    cmd = command(tmp)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    # the host pass does not know the gfx950 feature flag; drop that notice
+    out = "\n".join(l for l in r.stdout.splitlines()
+                    if "is not a recognized feature for this target" not in l)
+    if out.strip():
+        print(out, flush=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({r.returncode})")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build()
+    sys.exit(0)

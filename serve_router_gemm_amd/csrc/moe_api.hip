@@ -1,0 +1,282 @@
+// moe_api.hip -- the C ABI of libmoe (declared in include/moe.h): argument
+// checks, workspace layout and the order of launches.  Every check runs on
+// the host before anything is enqueued; nothing here allocates, synchronizes
+// or keeps state.
+#include <hip/hip_runtime.h>
+
+#include "../../include/moe.h"
+#include "moe_internal.h"
+
+namespace {
+
+using moe::launch_combine;
+
+constexpr int kMaxE = 512;
+constexpr int kMaxK = 16;
+constexpr long kMaxA = 1L << 24;
+constexpr long kMaxElems = (1L << 31) - 1;
+constexpr size_t kAlign = 256;
+
+size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_dim(int v) { return (v >= 64 && v <= 65536) ? ((v % 64 == 0) ? 0 : MOE_ERR_UNSUPPORTED) : MOE_ERR_SHAPE; }
+
+int check_tk(int T, int top_k) {
+    if (T < 0 || top_k < 1 || top_k > kMaxK) return MOE_ERR_SHAPE;
+    if ((long)T * top_k > kMaxA) return MOE_ERR_SHAPE;
+    return 0;
+}
+
+int check_e(int E, int top_k) {
+    if (E < 1 || E > kMaxE || top_k > E) return MOE_ERR_SHAPE;
+    return 0;
+}
+
+int check_elems(int T, int top_k, int D) {
+    return ((long)T * top_k * (long)D > kMaxElems) ? MOE_ERR_SHAPE : 0;
+}
+
+#define MOE_TRY(expr)          \
+    do {                       \
+        const int rc_ = (expr); \
+        if (rc_ != 0) return rc_; \
+    } while (0)
+
+int hip_rc(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// Shape checks shared by the expert GEMM entry points.
+int check_layer(int T, int H, int E, int F, int top_k) {
+    MOE_TRY(check_tk(T, top_k));
+    MOE_TRY(check_e(E, top_k));
+    MOE_TRY(check_dim(H));
+    MOE_TRY(check_dim(F));
+    MOE_TRY(check_elems(T, top_k, H > F ? H : F));
+    return 0;
+}
+
+// Workspace layout of moe_forward (every piece 256-byte aligned).
+struct FwdLayout {
+    size_t ids, w, counts, offsets, perm, inv_perm, route, permute, sched, hact, y, total;
+};
+
+FwdLayout fwd_layout(int T, int H, int E, int F, int top_k) {
+    const size_t A = (size_t)T * top_k;
+    FwdLayout L;
+    size_t o = 0;
+    L.ids = o; o += up(A * 4);
+    L.w = o; o += up(A * 4);
+    L.counts = o; o += up((size_t)E * 4);
+    L.offsets = o; o += up((size_t)(E + 1) * 4);
+    L.perm = o; o += up(A * 4);
+    L.inv_perm = o; o += up(A * 4);
+    L.route = o; o += up(moe::route_ws_bytes(T, H, E));
+    L.permute = o; o += up(moe::permute_ws_bytes((int)A, E));
+    L.sched = o; o += up(moe::gemm_sched_ws_bytes(E));
+    L.hact = o; o += up(A * (size_t)F * 2);
+    L.y = o; o += up(A * (size_t)H * 4);
+    L.total = o;
+    return L;
+}
+
+size_t swiglu_ws(int T, int E, int F, int top_k) {
+    return up(moe::gemm_sched_ws_bytes(E)) + up((size_t)T * top_k * (size_t)F * 2);
+}
+
+hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+template <typename P>
+unsigned char* at(P* base, size_t off) {
+    return reinterpret_cast<unsigned char*>(base) + off;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_version(void) { return 10000; }
+
+const char* moe_status_string(int status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_NULL: return "a required pointer is NULL";
+        case MOE_ERR_SHAPE: return "a size is out of the supported range";
+        case MOE_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
+        case MOE_ERR_UNSUPPORTED: return "unsupported argument (H/F not a multiple of 64, or bad enum)";
+        case MOE_ERR_WORKSPACE: return "workspace smaller than moe_workspace_bytes()";
+        case MOE_ERR_HIP: return "the HIP runtime reported a launch error";
+        default: return "unknown status";
+    }
+}
+
+size_t moe_workspace_bytes(int op, int T, int H, int E, int F, int top_k, int variant) {
+    if (variant != MOE_GEMM_INVARIANT && variant != MOE_GEMM_SPLITK_VARIANT) return 0;
+    switch (op) {
+        case MOE_OP_ROUTE:
+            if (check_tk(T, top_k) || check_e(E, top_k) || check_dim(H) || check_elems(T, 1, H))
+                return 0;
+            return moe::route_ws_bytes(T, H, E);
+        case MOE_OP_PERMUTE:
+            if (check_tk(T, top_k) || check_e(E, top_k)) return 0;
+            return moe::permute_ws_bytes(T * top_k, E);
+        case MOE_OP_GATE_UP:
+        case MOE_OP_DOWN:
+            if (check_layer(T, H, E, F, top_k)) return 0;
+            return moe::gemm_sched_ws_bytes(E);
+        case MOE_OP_GROUPED_SWIGLU:
+            if (check_layer(T, H, E, F, top_k)) return 0;
+            return swiglu_ws(T, E, F, top_k);
+        case MOE_OP_COMBINE:
+            return 0;
+        case MOE_OP_FORWARD:
+            if (check_layer(T, H, E, F, top_k)) return 0;
+            return fwd_layout(T, H, E, F, top_k).total;
+        default:
+            return 0;
+    }
+}
+
+int moe_route(int T, int H, int E, int top_k, int score, int renormalize, const uint16_t* x,
+              const uint16_t* w_router, const float* bias, int32_t* topk_ids, float* topk_w,
+              void* ws, size_t ws_bytes, void* stream) {
+    MOE_TRY(check_tk(T, top_k));
+    MOE_TRY(check_e(E, top_k));
+    MOE_TRY(check_dim(H));
+    MOE_TRY(check_elems(T, 1, H));
+    if (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID) return MOE_ERR_UNSUPPORTED;
+    if (renormalize != 0 && renormalize != 1) return MOE_ERR_UNSUPPORTED;
+    if (score == MOE_SCORE_SOFTMAX && bias) return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!x || !w_router || !topk_ids || !topk_w || !ws) return MOE_ERR_NULL;
+    if (!aligned16(x) || !aligned16(w_router) || !aligned16(topk_ids) || !aligned16(topk_w) ||
+        !aligned16(ws) || (bias && !aligned16(bias)))
+        return MOE_ERR_ALIGN;
+    if (ws_bytes < moe::route_ws_bytes(T, H, E)) return MOE_ERR_WORKSPACE;
+    return hip_rc(moe::launch_route(T, H, E, top_k, score, renormalize, x, w_router, bias,
+                                    topk_ids, topk_w, static_cast<float*>(ws), S(stream)));
+}
+
+int moe_permute(int T, int E, int top_k, const int32_t* topk_ids, int32_t* expert_counts,
+                int32_t* expert_offsets, int32_t* perm, int32_t* inv_perm, void* ws,
+                size_t ws_bytes, void* stream) {
+    MOE_TRY(check_tk(T, top_k));
+    MOE_TRY(check_e(E, top_k));
+    if (T == 0) return MOE_OK;
+    if (!topk_ids || !expert_counts || !expert_offsets || !perm || !inv_perm || !ws)
+        return MOE_ERR_NULL;
+    if (!aligned16(topk_ids) || !aligned16(expert_counts) || !aligned16(expert_offsets) ||
+        !aligned16(perm) || !aligned16(inv_perm) || !aligned16(ws))
+        return MOE_ERR_ALIGN;
+    if (ws_bytes < moe::permute_ws_bytes(T * top_k, E)) return MOE_ERR_WORKSPACE;
+    return hip_rc(moe::launch_permute(T * top_k, E, topk_ids, expert_counts, expert_offsets, perm,
+                                      inv_perm, static_cast<int32_t*>(ws), S(stream)));
+}
+
+int moe_expert_gate_up(int T, int H, int E, int F, int top_k, const uint16_t* x,
+                       const int32_t* perm, const int32_t* expert_offsets, const uint16_t* w_gate,
+                       const uint16_t* w_up, uint16_t* h_act, void* ws, size_t ws_bytes,
+                       void* stream) {
+    MOE_TRY(check_layer(T, H, E, F, top_k));
+    if (T == 0) return MOE_OK;
+    if (!x || !perm || !expert_offsets || !w_gate || !w_up || !h_act || !ws) return MOE_ERR_NULL;
+    if (!aligned16(x) || !aligned16(perm) || !aligned16(expert_offsets) || !aligned16(w_gate) ||
+        !aligned16(w_up) || !aligned16(h_act) || !aligned16(ws))
+        return MOE_ERR_ALIGN;
+    if (ws_bytes < moe::gemm_sched_ws_bytes(E)) return MOE_ERR_WORKSPACE;
+    return hip_rc(moe::launch_gate_up(T, H, E, F, top_k, x, perm, expert_offsets, w_gate, w_up,
+                                      h_act, static_cast<int32_t*>(ws), S(stream)));
+}
+
+int moe_expert_down(int T, int H, int E, int F, int top_k, const uint16_t* h_act,
+                    const int32_t* perm, const int32_t* expert_offsets, const uint16_t* w_down,
+                    float* y, int variant, void* ws, size_t ws_bytes, void* stream) {
+    MOE_TRY(check_layer(T, H, E, F, top_k));
+    if (variant != MOE_GEMM_INVARIANT && variant != MOE_GEMM_SPLITK_VARIANT)
+        return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!h_act || !perm || !expert_offsets || !w_down || !y || !ws) return MOE_ERR_NULL;
+    if (!aligned16(h_act) || !aligned16(perm) || !aligned16(expert_offsets) ||
+        !aligned16(w_down) || !aligned16(y) || !aligned16(ws))
+        return MOE_ERR_ALIGN;
+    if (ws_bytes < moe::gemm_sched_ws_bytes(E)) return MOE_ERR_WORKSPACE;
+    return hip_rc(moe::launch_down(T, H, E, F, top_k, h_act, perm, expert_offsets, w_down, y,
+                                   variant, static_cast<int32_t*>(ws), S(stream)));
+}
+
+int moe_grouped_swiglu(int T, int H, int E, int F, int top_k, const uint16_t* x,
+                       const int32_t* perm, const int32_t* expert_offsets, const uint16_t* w_gate,
+                       const uint16_t* w_up, const uint16_t* w_down, float* y, int variant,
+                       void* ws, size_t ws_bytes, void* stream) {
+    MOE_TRY(check_layer(T, H, E, F, top_k));
+    if (variant != MOE_GEMM_INVARIANT && variant != MOE_GEMM_SPLITK_VARIANT)
+        return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!x || !perm || !expert_offsets || !w_gate || !w_up || !w_down || !y || !ws)
+        return MOE_ERR_NULL;
+    if (!aligned16(x) || !aligned16(perm) || !aligned16(expert_offsets) || !aligned16(w_gate) ||
+        !aligned16(w_up) || !aligned16(w_down) || !aligned16(y) || !aligned16(ws))
+        return MOE_ERR_ALIGN;
+    if (ws_bytes < swiglu_ws(T, E, F, top_k)) return MOE_ERR_WORKSPACE;
+    int32_t* sched = static_cast<int32_t*>(ws);
+    uint16_t* hact = reinterpret_cast<uint16_t*>(at(ws, up(moe::gemm_sched_ws_bytes(E))));
+    MOE_TRY(hip_rc(moe::launch_gate_up(T, H, E, F, top_k, x, perm, expert_offsets, w_gate, w_up,
+                                       hact, sched, S(stream))));
+    return hip_rc(moe::launch_down(T, H, E, F, top_k, hact, perm, expert_offsets, w_down, y,
+                                   variant, sched, S(stream)));
+}
+
+int moe_combine(int T, int H, int top_k, const float* y, const float* topk_w, uint16_t* out,
+                void* stream) {
+    MOE_TRY(check_tk(T, top_k));
+    MOE_TRY(check_dim(H));
+    MOE_TRY(check_elems(T, top_k, H));
+    if (T == 0) return MOE_OK;
+    if (!y || !topk_w || !out) return MOE_ERR_NULL;
+    if (!aligned16(y) || !aligned16(topk_w) || !aligned16(out)) return MOE_ERR_ALIGN;
+    return hip_rc(launch_combine(T, H, top_k, y, topk_w, out, S(stream)));
+}
+
+int moe_forward(int T, int H, int E, int F, int top_k, int score, int renormalize,
+                const uint16_t* x, const uint16_t* w_router, const float* bias,
+                const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
+                uint16_t* out, int32_t* topk_ids, float* topk_w, int variant, void* ws,
+                size_t ws_bytes, void* stream) {
+    MOE_TRY(check_layer(T, H, E, F, top_k));
+    if (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID) return MOE_ERR_UNSUPPORTED;
+    if (renormalize != 0 && renormalize != 1) return MOE_ERR_UNSUPPORTED;
+    if (score == MOE_SCORE_SOFTMAX && bias) return MOE_ERR_UNSUPPORTED;
+    if (variant != MOE_GEMM_INVARIANT && variant != MOE_GEMM_SPLITK_VARIANT)
+        return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!x || !w_router || !w_gate || !w_up || !w_down || !out || !ws) return MOE_ERR_NULL;
+    if (!aligned16(x) || !aligned16(w_router) || !aligned16(w_gate) || !aligned16(w_up) ||
+        !aligned16(w_down) || !aligned16(out) || !aligned16(ws) || (bias && !aligned16(bias)) ||
+        (topk_ids && !aligned16(topk_ids)) || (topk_w && !aligned16(topk_w)))
+        return MOE_ERR_ALIGN;
+    const FwdLayout L = fwd_layout(T, H, E, F, top_k);
+    if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    const int A = T * top_k;
+    int32_t* ids = topk_ids ? topk_ids : reinterpret_cast<int32_t*>(at(ws, L.ids));
+    float* w = topk_w ? topk_w : reinterpret_cast<float*>(at(ws, L.w));
+    int32_t* counts = reinterpret_cast<int32_t*>(at(ws, L.counts));
+    int32_t* offsets = reinterpret_cast<int32_t*>(at(ws, L.offsets));
+    int32_t* perm = reinterpret_cast<int32_t*>(at(ws, L.perm));
+    int32_t* inv = reinterpret_cast<int32_t*>(at(ws, L.inv_perm));
+    float* part = reinterpret_cast<float*>(at(ws, L.route));
+    int32_t* pws = reinterpret_cast<int32_t*>(at(ws, L.permute));
+    int32_t* sched = reinterpret_cast<int32_t*>(at(ws, L.sched));
+    uint16_t* hact = reinterpret_cast<uint16_t*>(at(ws, L.hact));
+    float* y = reinterpret_cast<float*>(at(ws, L.y));
+    hipStream_t s = S(stream);
+    MOE_TRY(hip_rc(moe::launch_route(T, H, E, top_k, score, renormalize, x, w_router, bias, ids,
+                                     w, part, s)));
+    MOE_TRY(hip_rc(moe::launch_permute(A, E, ids, counts, offsets, perm, inv, pws, s)));
+    MOE_TRY(hip_rc(moe::launch_gate_up(T, H, E, F, top_k, x, perm, offsets, w_gate, w_up, hact,
+                                       sched, s)));
+    MOE_TRY(hip_rc(moe::launch_down(T, H, E, F, top_k, hact, perm, offsets, w_down, y, variant,
+                                    sched, s)));
+    return hip_rc(launch_combine(T, H, top_k, y, w, out, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,54 @@
+// moe_combine.hip -- fixed-order fp32 weighted combine of the top-k expert
+// outputs.
+//
+// Both the precision and the execution order of weighting and summing the
+// expert outputs must be pinned (Fireworks page on numerical alignment and MoE
+// routing, section "混合专家模型更难对齐").  Here: acc starts at +0, one fp32
+// fused multiply-add per slot in slot order j = 0..k-1, one bf16
+// round-to-nearest-even at the end.  A token's k expert rows are adjacent in
+// y (assignment order a = t*k + j), so each thread streams k float4 rows.
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+__global__ __launch_bounds__(256) void combine_kernel(int T, int H4, int k,
+                                                      const float4* __restrict__ y,
+                                                      const float* __restrict__ w,
+                                                      uint2* __restrict__ out) {
+    const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (long)T * H4) return;
+    const int t = (int)(idx / H4);
+    const int h4 = (int)(idx - (long)t * H4);
+    const float4* yt = y + (size_t)t * k * H4 + h4;
+    const float* wt = w + (size_t)t * k;
+    float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
+    for (int j = 0; j < k; ++j) {
+        const float wj = wt[j];
+        const float4 v = yt[(size_t)j * H4];
+        a0 = __builtin_fmaf(wj, v.x, a0);
+        a1 = __builtin_fmaf(wj, v.y, a1);
+        a2 = __builtin_fmaf(wj, v.z, a2);
+        a3 = __builtin_fmaf(wj, v.w, a3);
+    }
+    uint2 o;
+    o.x = f32_to_bf16_rne(a0) | (f32_to_bf16_rne(a1) << 16);
+    o.y = f32_to_bf16_rne(a2) | (f32_to_bf16_rne(a3) << 16);
+    out[idx] = o;
+}
+
+}  // namespace
+
+hipError_t launch_combine(int T, int H, int k, const float* y, const float* w, uint16_t* out,
+                          hipStream_t s) {
+    const int H4 = H / 4;
+    const long n = (long)T * H4;
+    const int blocks = (int)((n + 255) / 256);
+    combine_kernel<<<blocks, 256, 0, s>>>(T, H4, k, reinterpret_cast<const float4*>(y), w,
+                                          reinterpret_cast<uint2*>(out));
+    return hipGetLastError();
+}
+
+}  // namespace moe

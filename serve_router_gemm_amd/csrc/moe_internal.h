@@ -1,0 +1,57 @@
+// moe_internal.h -- launchers shared between the translation units of libmoe.
+// Host-side declarations only; every launcher enqueues on `stream` and
+// returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Router logit order: chunks of this many consecutive hidden indices, each an
+// ascending fp32 fma chain, chunk sums added in ascending order.
+constexpr int kLogitChunk = 256;
+
+// Expert GEMM tile (the single tile of the invariant variant).
+constexpr int kTileTok = 128;   // token rows per workgroup tile
+constexpr int kTileW = 256;     // weight rows per workgroup tile
+constexpr int kTileK = 64;      // K per pipeline stage (two 32-deep MFMA steps)
+constexpr int kGateUpF = kTileW / 2;  // f columns per gate/up tile (gate + up rows)
+
+// router -------------------------------------------------------------------
+struct RoutePlan {
+    int split;     // 1: logits kernel folds every chunk; 0: one block per chunk
+    int nparts;    // partial-logit planes the select kernel folds
+    int tt, te;    // token / expert register tile of the logits kernel
+};
+RoutePlan route_plan(int T, int H, int E);
+size_t route_ws_bytes(int T, int H, int E);
+hipError_t launch_route(int T, int H, int E, int k, int score, int renorm,
+                        const uint16_t* x, const uint16_t* wr, const float* bias,
+                        int32_t* ids, float* w, float* part_ws, hipStream_t s);
+
+// permute ------------------------------------------------------------------
+int permute_chunk(int A);
+size_t permute_ws_bytes(int A, int E);
+hipError_t launch_permute(int A, int E, const int32_t* ids, int32_t* counts,
+                          int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                          int32_t* ws, hipStream_t s);
+
+// expert GEMMs ---------------------------------------------------------------
+size_t gemm_sched_ws_bytes(int E);  // tile_start [E+1] + split [E]
+hipError_t launch_gate_up(int T, int H, int E, int F, int k, const uint16_t* x,
+                          const int32_t* perm, const int32_t* offsets,
+                          const uint16_t* wg, const uint16_t* wu, uint16_t* h_act,
+                          int32_t* sched_ws, hipStream_t s);
+hipError_t launch_down(int T, int H, int E, int F, int k, const uint16_t* h_act,
+                       const int32_t* perm, const int32_t* offsets, const uint16_t* wd,
+                       float* y, int variant, int32_t* sched_ws, hipStream_t s);
+
+// combine ------------------------------------------------------------------
+hipError_t launch_combine(int T, int H, int k, const float* y, const float* w,
+                          uint16_t* out, hipStream_t s);
+
+int device_cu_count();
+
+}  // namespace moe

@@ -1,0 +1,270 @@
+// moe_route.hip -- router logits, selection keys, top-k and weights.
+//
+// The router's near-ties are what flips experts between runs (Fireworks page
+// "位级一致：前沿训练的差异化关键", section "为什么比特级一致是一个复杂的问题");
+// a deterministic tie-break is the fix named there.  A top-k must also fix
+// boundary ties, stability, NaN handling and the index dtype ("GLM
+// Post-Training Beyond SFT", section "迁移到 NPU 时").
+//
+// Logits are taken in one fixed order, independent of the batch: hidden
+// indices in chunks of 256, each chunk an ascending fp32 fma chain from +0,
+// chunk sums added in ascending order.  The logits kernel either folds all
+// chunks of its tile itself (large batches) or writes each chunk's sum to
+// its own plane for the select kernel to fold (small batches, where the
+// chunks give the parallelism).  Both produce the same bits.
+//
+// This is fp32 VALU work on purpose: the order inside an MFMA is the
+// hardware's, so only a VALU chain has an order the rest of the stack (and a
+// plain CPU program) can reproduce exactly.
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kRouteThreads = 256;
+constexpr int kStageK = 32;   // hidden indices staged in LDS per step
+
+// part[c][t][e] = fp32 logit (SPLIT=false: all chunks folded, c = 0) or the
+// chunk-c partial sum (SPLIT=true: blockIdx.z = c).
+// Thread (ty, tx): tokens t0 + ty*TT + i, experts e0 + tx + 32*j.
+template <int TT, int TE, bool SPLIT>
+__global__ __launch_bounds__(kRouteThreads) void router_logits_kernel(
+    int T, int H, int E, const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+    float* __restrict__ part) {
+    constexpr int BT = 8 * TT;
+    constexpr int BE = 32 * TE;
+    __shared__ float xs[kStageK][BT];
+    __shared__ float ws[kStageK][BE];
+
+    const int tid = threadIdx.x;
+    const int tx = tid & 31, ty = tid >> 5;
+    const int t0 = blockIdx.x * BT;
+    const int e0 = blockIdx.y * BE;
+
+    int k_begin = 0, k_end = H;
+    if (SPLIT) {
+        k_begin = blockIdx.z * kLogitChunk;
+        k_end = min(H, k_begin + kLogitChunk);
+    }
+
+    float total[TT][TE];
+    float acc[TT][TE];
+#pragma unroll
+    for (int i = 0; i < TT; ++i)
+#pragma unroll
+        for (int j = 0; j < TE; ++j) { total[i][j] = 0.0f; acc[i][j] = 0.0f; }
+
+    for (int k0 = k_begin; k0 < k_end; k0 += kStageK) {
+        __syncthreads();
+        // stage x[t0:t0+BT, k0:k0+32] and wr[e0:e0+BE, k0:k0+32] as fp32, k-major
+        for (int c = tid; c < BT * 4; c += kRouteThreads) {
+            const int row = c >> 2, q = c & 3;
+            const int t = t0 + row;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (t < T) v = *reinterpret_cast<const uint4*>(x + (size_t)t * H + k0 + q * 8);
+            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                xs[q * 8 + 2 * u][row] = bf16_to_f32(w4[u] & 0xFFFFu);
+                xs[q * 8 + 2 * u + 1][row] = bf16_to_f32(w4[u] >> 16);
+            }
+        }
+        for (int c = tid; c < BE * 4; c += kRouteThreads) {
+            const int row = c >> 2, q = c & 3;
+            const int e = e0 + row;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (e < E) v = *reinterpret_cast<const uint4*>(wr + (size_t)e * H + k0 + q * 8);
+            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                ws[q * 8 + 2 * u][row] = bf16_to_f32(w4[u] & 0xFFFFu);
+                ws[q * 8 + 2 * u + 1][row] = bf16_to_f32(w4[u] >> 16);
+            }
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int kk = 0; kk < kStageK; ++kk) {
+            float xv[TT], wv[TE];
+#pragma unroll
+            for (int i = 0; i < TT; ++i) xv[i] = xs[kk][ty * TT + i];
+#pragma unroll
+            for (int j = 0; j < TE; ++j) wv[j] = ws[kk][tx + 32 * j];
+#pragma unroll
+            for (int i = 0; i < TT; ++i)
+#pragma unroll
+                for (int j = 0; j < TE; ++j) acc[i][j] = __builtin_fmaf(xv[i], wv[j], acc[i][j]);
+        }
+        // end of a 256-wide chunk (or of H): fold the chunk sum in order
+        const int kn = k0 + kStageK;
+        if (!SPLIT && ((kn % kLogitChunk) == 0 || kn == k_end)) {
+#pragma unroll
+            for (int i = 0; i < TT; ++i)
+#pragma unroll
+                for (int j = 0; j < TE; ++j) {
+                    total[i][j] = total[i][j] + acc[i][j];
+                    acc[i][j] = 0.0f;
+                }
+        }
+    }
+
+    float* plane = part + (SPLIT ? (size_t)blockIdx.z * T * E : 0);
+#pragma unroll
+    for (int i = 0; i < TT; ++i) {
+        const int t = t0 + ty * TT + i;
+        if (t >= T) continue;
+#pragma unroll
+        for (int j = 0; j < TE; ++j) {
+            const int e = e0 + tx + 32 * j;
+            if (e < E) plane[(size_t)t * E + e] = SPLIT ? acc[i][j] : total[i][j];
+        }
+    }
+}
+
+constexpr int kSelMaxQ = 8;   // experts per lane: E <= 512
+
+// One wave per token: fold partial logits, keys, top-k, weights.
+__global__ __launch_bounds__(256) void router_select_kernel(
+    int T, int E, int k, int nparts, int score, int renorm, const float* __restrict__ part,
+    const float* __restrict__ bias, int32_t* __restrict__ ids, float* __restrict__ wout) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;  // whole wave leaves together
+
+    float lg[kSelMaxQ];
+    uint64_t rk[kSelMaxQ];
+#pragma unroll
+    for (int q = 0; q < kSelMaxQ; ++q) {
+        const int e = lane + 64 * q;
+        lg[q] = 0.0f;
+        rk[q] = 0;
+        if (e < E) {
+            float v = 0.0f;
+            for (int c = 0; c < nparts; ++c) v = v + part[((size_t)c * T + t) * E + e];
+            lg[q] = v;
+            float key;
+            if (score == 0) {
+                key = v;
+            } else {
+                const float sg = 1.0f / (1.0f + expf(-v));
+                key = sg + (bias ? bias[e] : 0.0f);
+            }
+            rk[q] = sel_rank(key, e);
+        }
+    }
+
+    int sel[16];
+    float lsel[16];
+    for (int j = 0; j < k; ++j) {
+        uint64_t best = rk[0];
+#pragma unroll
+        for (int q = 1; q < kSelMaxQ; ++q) best = rk[q] > best ? rk[q] : best;
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) {
+            const uint64_t o = shfl_xor_u64(best, m);
+            best = o > best ? o : best;
+        }
+        const int e = (int)(~(uint32_t)best);
+        const int qs = e >> 6, owner = e & 63;
+        float mine = 0.0f;
+#pragma unroll
+        for (int q = 0; q < kSelMaxQ; ++q)
+            if (q == qs) {
+                mine = lg[q];
+                if (lane == owner) rk[q] = 0;  // taken
+            }
+        sel[j] = e;
+        lsel[j] = __shfl(mine, owner, 64);
+    }
+
+    float p[16];
+    if (score == 0) {
+        float m = -INFINITY;
+#pragma unroll
+        for (int q = 0; q < kSelMaxQ; ++q)
+            if (lane + 64 * q < E) m = fmaxf(m, lg[q]);
+#pragma unroll
+        for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, 64));
+        float S = 0.0f;
+#pragma unroll
+        for (int q = 0; q < kSelMaxQ; ++q)
+            if (lane + 64 * q < E) S = S + expf(lg[q] - m);
+#pragma unroll
+        for (int s = 32; s >= 1; s >>= 1) S = S + __shfl_xor(S, s, 64);
+        for (int j = 0; j < k; ++j) p[j] = expf(lsel[j] - m) / S;
+    } else {
+        for (int j = 0; j < k; ++j) p[j] = 1.0f / (1.0f + expf(-lsel[j]));
+    }
+    if (renorm) {
+        float D = 0.0f;
+        for (int j = 0; j < k; ++j) D = D + p[j];
+        for (int j = 0; j < k; ++j) p[j] = p[j] / D;
+    }
+    for (int j = 0; j < k; ++j)
+        if (lane == j) {
+            ids[(size_t)t * k + j] = sel[j];
+            wout[(size_t)t * k + j] = p[j];
+        }
+}
+
+template <int TT, int TE, bool SPLIT>
+hipError_t launch_logits(int T, int H, int E, const uint16_t* x, const uint16_t* wr,
+                         float* part, hipStream_t s) {
+    constexpr int BT = 8 * TT, BE = 32 * TE;
+    const int nchunks = (H + kLogitChunk - 1) / kLogitChunk;
+    dim3 grid((T + BT - 1) / BT, (E + BE - 1) / BE, SPLIT ? nchunks : 1);
+    router_logits_kernel<TT, TE, SPLIT><<<grid, kRouteThreads, 0, s>>>(T, H, E, x, wr, part);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+RoutePlan route_plan(int T, int H, int E) {
+    RoutePlan p;
+    const int nchunks = (H + kLogitChunk - 1) / kLogitChunk;
+    // folded tiles: 64 tokens x up to 128 experts per block
+    const int te = E <= 32 ? 1 : (E <= 64 ? 2 : 4);
+    const long blocks = (long)((T + 63) / 64) * ((E + 32 * te - 1) / (32 * te));
+    if (blocks >= 512 || nchunks == 1) {
+        p.split = 0; p.nparts = 1; p.tt = 8; p.te = te;
+    } else if (T >= 512) {
+        // mid-sized batch: the same register tile, one block per chunk
+        p.split = 1; p.nparts = nchunks; p.tt = 8; p.te = te;
+    } else {
+        // small batch: one logit per thread, one block per chunk
+        p.split = 1; p.nparts = nchunks; p.tt = 1; p.te = 1;
+    }
+    return p;
+}
+
+size_t route_ws_bytes(int T, int H, int E) {
+    const RoutePlan p = route_plan(T, H, E);
+    return (size_t)p.nparts * (size_t)T * (size_t)E * sizeof(float);
+}
+
+hipError_t launch_route(int T, int H, int E, int k, int score, int renorm, const uint16_t* x,
+                        const uint16_t* wr, const float* bias, int32_t* ids, float* w,
+                        float* part_ws, hipStream_t s) {
+    const RoutePlan p = route_plan(T, H, E);
+    hipError_t err;
+    if (p.split && p.tt == 1) {
+        err = launch_logits<1, 1, true>(T, H, E, x, wr, part_ws, s);
+    } else if (p.split) {
+        if (p.te == 1) err = launch_logits<8, 1, true>(T, H, E, x, wr, part_ws, s);
+        else if (p.te == 2) err = launch_logits<8, 2, true>(T, H, E, x, wr, part_ws, s);
+        else err = launch_logits<8, 4, true>(T, H, E, x, wr, part_ws, s);
+    } else if (p.te == 1) {
+        err = launch_logits<8, 1, false>(T, H, E, x, wr, part_ws, s);
+    } else if (p.te == 2) {
+        err = launch_logits<8, 2, false>(T, H, E, x, wr, part_ws, s);
+    } else {
+        err = launch_logits<8, 4, false>(T, H, E, x, wr, part_ws, s);
+    }
+    if (err != hipSuccess) return err;
+    router_select_kernel<<<(T + 3) / 4, 256, 0, s>>>(T, E, k, p.nparts, score, renorm, part_ws,
+                                                     bias, ids, w);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,155 @@
+"""The C ABI without a GPU: exported symbols, binding signatures and every
+host-side argument check (all of which return before anything is enqueued)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from serve_router_gemm_amd import moe as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+OK, NULL, SHAPE, ALIGN, UNSUP, WS = 0, -1, -2, -3, -4, -5
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(M.LIB_PATH):
+        from serve_router_gemm_amd import build
+        build.build(verbose=False)
+    return M.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert set(names) >= {"moe_route", "moe_permute", "moe_grouped_swiglu", "moe_combine",
+                          "moe_forward", "moe_expert_gate_up", "moe_expert_down",
+                          "moe_workspace_bytes", "moe_status_string", "moe_version"}
+    raw = ctypes.CDLL(M.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+
+
+def test_binding_covers_header(L):
+    assert sorted(M.SIGNATURES) == declared_functions()
+
+
+def test_binding_arity_matches_header(L):
+    src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    for name, (_, args) in M.SIGNATURES.items():
+        m = re.search(name + r"\s*\(([^)]*)\)", src)
+        params = [p for p in m.group(1).split(",") if p.strip() and p.strip() != "void"]
+        assert len(params) == len(args), name
+
+
+def test_version_and_status_strings(L):
+    assert L.moe_version() >= 10000
+    for rc in (OK, NULL, SHAPE, ALIGN, UNSUP, WS, -6):
+        s = L.moe_status_string(rc).decode()
+        assert s and s != "unknown status"
+    assert L.moe_status_string(-99).decode() == "unknown status"
+
+
+FAKE = ctypes.c_void_p(0x10000)     # aligned, never dereferenced: checks fail first
+MIS = ctypes.c_void_p(0x10004)      # misaligned
+
+
+def route(L, T=4, H=64, E=8, k=2, score=0, renorm=1, x=FAKE, wr=FAKE, b=None, ids=FAKE,
+          w=FAKE, ws=FAKE, ws_bytes=0):
+    return L.moe_route(T, H, E, k, score, renorm, x, wr, b, ids, w, ws, ws_bytes, None)
+
+
+def test_route_checks(L):
+    assert route(L, x=None) == NULL
+    assert route(L, ws=None) == NULL
+    assert route(L, E=0) == SHAPE
+    assert route(L, E=513) == SHAPE
+    assert route(L, k=9) == SHAPE          # k > E
+    assert route(L, k=0) == SHAPE
+    assert route(L, E=32, k=17) == SHAPE   # k > 16
+    assert route(L, H=100) == UNSUP
+    assert route(L, H=32) == SHAPE
+    assert route(L, T=-1) == SHAPE
+    assert route(L, T=(1 << 24) // 2 + 1) == SHAPE    # T*k > 2^24
+    assert route(L, score=2) == UNSUP
+    assert route(L, renorm=2) == UNSUP
+    assert route(L, b=FAKE) == UNSUP       # bias with softmax
+    assert route(L, x=MIS) == ALIGN
+    assert route(L, score=1, b=MIS) == ALIGN
+    assert route(L, ws_bytes=0) == WS
+    assert route(L, T=0, x=None, wr=None, ids=None, w=None, ws=None) == OK
+
+
+def test_permute_checks(L):
+    p = L.moe_permute
+    assert p(4, 8, 2, None, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == NULL
+    assert p(4, 8, 9, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == SHAPE
+    assert p(4, 8, 2, FAKE, FAKE, MIS, FAKE, FAKE, FAKE, 0, None) == ALIGN
+    assert p(4, 8, 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == WS
+    assert p(0, 8, 2, None, None, None, None, None, None, 0, None) == OK
+
+
+def test_gemm_checks(L):
+    g = L.moe_expert_gate_up
+    args = [FAKE] * 6
+    assert g(4, 64, 8, 64, 2, *args, FAKE, 0, None) == WS
+    assert g(4, 64, 8, 96, 2, *args, FAKE, 0, None) == UNSUP       # F % 64
+    assert g(4, 64, 8, 64, 2, None, *args[1:], FAKE, 0, None) == NULL
+    assert g(4, 64, 8, 64, 2, *args[:5], MIS, FAKE, 0, None) == ALIGN
+    assert g(0, 64, 8, 64, 2, *([None] * 6), None, 0, None) == OK
+    d = L.moe_expert_down
+    assert d(4, 64, 8, 64, 2, *([FAKE] * 5), 0, FAKE, 0, None) == WS
+    assert d(4, 64, 8, 64, 2, *([FAKE] * 5), 7, FAKE, 0, None) == UNSUP   # variant
+    s = L.moe_grouped_swiglu
+    assert s(4, 64, 8, 64, 2, *([FAKE] * 7), 0, FAKE, 0, None) == WS
+    # T*k*max(H,F) must stay below 2^31
+    assert s(1 << 16, 65536, 8, 64, 1, *([FAKE] * 7), 0, FAKE, 0, None) == SHAPE
+
+
+def test_combine_and_forward_checks(L):
+    c = L.moe_combine
+    assert c(4, 64, 2, None, FAKE, FAKE, None) == NULL
+    assert c(4, 64, 2, FAKE, FAKE, MIS, None) == ALIGN
+    assert c(4, 65, 2, FAKE, FAKE, FAKE, None) == UNSUP
+    assert c(0, 64, 2, None, None, None, None) == OK
+    f = L.moe_forward
+    base = [FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None, None]
+    assert f(4, 64, 8, 64, 2, 0, 1, *base, 0, FAKE, 0, None) == WS
+    assert f(4, 64, 8, 64, 2, 1, 1, *base, 0, FAKE, 0, None) == WS        # sigmoid, no bias
+    b2 = list(base)
+    b2[2] = FAKE
+    assert f(4, 64, 8, 64, 2, 0, 1, *b2, 0, FAKE, 0, None) == UNSUP      # softmax + bias
+    assert f(4, 64, 8, 64, 2, 0, 1, *base, 3, FAKE, 0, None) == UNSUP    # variant
+    assert f(4, 64, 8, 64, 2, 0, 1, *base, 0, None, 0, None) == NULL
+    b3 = list(base)
+    b3[8] = MIS
+    assert f(4, 64, 8, 64, 2, 0, 1, *b3, 0, FAKE, 0, None) == ALIGN
+    assert f(0, 64, 8, 64, 2, 0, 1, *([None] * 9), 0, None, 0, None) == OK
+
+
+def test_workspace_sizes(L):
+    wb = L.moe_workspace_bytes
+    T, H, E, F, k = 16384, 6144, 256, 2048, 8
+    fwd = wb(M.OP_FORWARD, T, H, E, F, k, 0)
+    y = T * k * H * 4
+    hact = T * k * F * 2
+    assert fwd >= y + hact
+    assert fwd < y + hact + (1 << 30)
+    assert wb(M.OP_GROUPED_SWIGLU, T, H, E, F, k, 0) >= hact
+    assert wb(M.OP_ROUTE, T, H, E, F, k, 0) >= T * E * 4
+    assert wb(M.OP_PERMUTE, T, H, E, F, k, 0) >= E * 4
+    assert wb(M.OP_COMBINE, T, H, E, F, k, 0) == 0
+    # rejected sizes report 0
+    assert wb(M.OP_FORWARD, T, 100, E, F, k, 0) == 0
+    assert wb(M.OP_FORWARD, T, H, E, F, k, 5) == 0
+    assert wb(99, T, H, E, F, k, 0) == 0

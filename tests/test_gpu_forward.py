@@ -1,0 +1,252 @@
+"""End-to-end parity against the oracle, batch invariance (bitwise, GPU vs GPU)
+and the split-K variant's drift (GPU required).
+
+Batch invariance is the property the pages put first: a request gets the same
+result whatever else shares its batch (Fireworks page "位级一致：前沿训练的差异化关键",
+section "曾经只有前沿实验室才有的功能"); zero train/inference KL is checked as
+bit identity of the outputs (same page, section "端到端零 KLD").  The decode
+check reports the k3 estimator against the 0.001 equivalence threshold used
+on the Fireworks page on numerical alignment and MoE routing (section
+"混合专家模型更难对齐").
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from helpers import (DEV, GAP_EXEMPT, assert_out_close, bits, gpu, host, layer, log,
+                     routing_compare, weights_close)
+from oracle import oracle as O
+from serve_router_gemm_amd import inputs as I
+
+pytestmark = gpu
+
+if torch.cuda.is_available():
+    from serve_router_gemm_amd import moe as M
+
+
+def _cfg(name, **kw):
+    return I.scaled(I.CONFIGS[name], **kw)
+
+
+def fwd(cfg, L, x, variant=0):
+    return M.forward(x, L["w_router"], L["w_gate"], L["w_up"], L["w_down"], cfg.k, cfg.score,
+                     cfg.renorm, bias=L["bias"], variant=variant, return_routing=True)
+
+
+def stratified_rows(ids_np, counts_np, n, seed=3):
+    """n token rows, including ones routed to the busiest and the least busy
+    active experts."""
+    rng = np.random.default_rng(seed)
+    T = ids_np.shape[0]
+    active = np.nonzero(counts_np)[0]
+    busiest = active[np.argsort(-counts_np[active], kind="stable")][:4]
+    quietest = active[np.argsort(counts_np[active], kind="stable")][:4]
+    picks = []
+    for e in list(busiest) + list(quietest):
+        rows = np.nonzero(np.any(ids_np == e, axis=1))[0]
+        picks.extend(rng.choice(rows, size=min(4, len(rows)), replace=False).tolist())
+    rest = rng.choice(T, size=max(0, n - len(picks)), replace=False).tolist()
+    return np.unique(np.array(picks + rest + [0, T - 1], dtype=np.int64))[:max(n, 1) + 64]
+
+
+FWD_CASES = [
+    ("tiny_full", _cfg("tiny"), None),
+    ("mid_T4096", _cfg("mid"), 96),
+    ("large_T16384", _cfg("large"), 48),
+    ("dec_T64", _cfg("dec"), 16),
+]
+
+
+@pytest.mark.parametrize("case", FWD_CASES, ids=lambda c: c[0])
+def test_forward_parity(case):
+    name, cfg, nsample = case
+    log(f"[forward] {name}: {I.describe(cfg)}")
+    L = layer(cfg)
+    hb = host(cfg)
+    x = I.make_x(cfg, DEV)
+    out, ids, w = fwd(cfg, L, x)
+    torch.cuda.synchronize()
+    ids_np = ids.cpu().numpy()
+    if nsample is None:
+        rows = np.arange(cfg.T)
+    else:
+        counts = np.bincount(ids_np.reshape(-1), minlength=cfg.E)
+        rows = stratified_rows(ids_np, counts, nsample)
+    xb = bits(x)
+    out_r, ids_r, w_r, gap = O.forward_tokens(rows, xb, hb["w_router"], hb["w_gate"],
+                                              hb["w_up"], hb["w_down"], cfg.k, cfg.score,
+                                              cfg.renorm, bias=hb["bias"])
+    n_ex, n_mis = routing_compare(ids_np[rows], ids_r, gap)
+    same = np.all(ids_np[rows] == ids_r, axis=1)
+    weights_close(w.cpu().numpy()[rows][same], w_r[same])
+    stats = assert_out_close(bits(out)[rows][same], out_r[same], what=f"{name} out")
+    log(f"[forward] {name}: rows={len(rows)} exempt={n_ex} exempt_mismatch={n_mis} {stats}")
+
+
+def test_tie_config_forward_and_routing_invariance():
+    """Near-tie stress layer: stress tokens route exactly (no exemption), and
+    their ids do not change with T or with their position in the batch."""
+    cfg = I.CONFIGS["tie"]
+    d = I.make_tie_inputs(cfg)
+    L = dict(layer(cfg))
+    L["w_router"] = d["w_router"].to(DEV)
+    x = d["x"].to(DEV)
+    out, ids, w = fwd(cfg, L, x)
+    torch.cuda.synchronize()
+    ids_np = ids.cpu().numpy()
+    stress = d["kind"] >= 2
+    ids_r, _, gap = O.route(bits(d["x"]), bits(d["w_router"]), cfg.k, cfg.score, cfg.renorm)
+    routing_compare(ids_np, ids_r, gap, strict_rows=stress)
+    # values on a sample
+    hb = host(cfg)
+    rows = np.sort(np.random.default_rng(2).choice(cfg.T, 32, replace=False))
+    out_r, ids_r2, _, gap2 = O.forward_tokens(rows, bits(d["x"]), bits(d["w_router"]),
+                                              hb["w_gate"], hb["w_up"], hb["w_down"], cfg.k,
+                                              cfg.score, cfg.renorm)
+    same = np.all(ids_np[rows] == ids_r2, axis=1)
+    assert_out_close(bits(out)[rows][same], out_r[same], what="tie out")
+    # invariance of the chosen ids across T and under shuffled positions
+    out_full = bits(out)
+    for T in I.TIE_SWEEP_T[:-1]:
+        sel = np.random.default_rng(T).choice(cfg.T, T, replace=False)
+        o2, i2, _ = fwd(cfg, L, x[torch.from_numpy(sel).to(DEV)])
+        assert np.array_equal(i2.cpu().numpy(), ids_np[sel]), T
+        assert np.array_equal(bits(o2), out_full[sel]), T
+    log(f"[tie] stress tokens={int(stress.sum())}: ids and out invariant over "
+        f"T in {I.TIE_SWEEP_T}")
+
+
+def _probe_reference(cfg, L, probes):
+    """Each probe alone (T = 1): the reference bits."""
+    ref = []
+    for i in range(probes.shape[0]):
+        o, ids, w = fwd(cfg, L, probes[i:i + 1].contiguous())
+        ref.append((bits(o)[0], ids.cpu().numpy()[0], w.cpu().numpy()[0].view(np.uint32)))
+    return ref
+
+
+def _check_probes(cfg, L, probes, ref, T, rep, variant=0):
+    """Returns the number of differing output bits summed over probes."""
+    n = probes.shape[0]
+    ndiff = 0
+    if T < n:
+        # each probe in its own batch of T (T-1 fresh co-tokens)
+        for i in range(n):
+            x = I.make_tokens(T, cfg.H, I.COTOKEN_SEED_BASE + 97 * rep + i, "cpu").to(DEV)
+            pos = (rep * 5 + i) % T
+            x[pos] = probes[i]
+            o, ids, w = fwd(cfg, L, x, variant)
+            ndiff += _diffbits(bits(o)[pos], ref[i][0])
+            if variant == 0:
+                assert np.array_equal(ids.cpu().numpy()[pos], ref[i][1])
+                assert np.array_equal(w.cpu().numpy()[pos].view(np.uint32), ref[i][2])
+    else:
+        x, pos = I.embed_probes(probes, T, rep)
+        o, ids, w = fwd(cfg, L, x, variant)
+        ob, ib, wb = bits(o), ids.cpu().numpy(), w.cpu().numpy().view(np.uint32)
+        for i in range(n):
+            ndiff += _diffbits(ob[pos[i]], ref[i][0])
+            if variant == 0:
+                assert np.array_equal(ib[pos[i]], ref[i][1])
+                assert np.array_equal(wb[pos[i]], ref[i][2])
+    return ndiff
+
+
+def _diffbits(a, b):
+    return int(np.unpackbits(np.bitwise_xor(np.asarray(a), np.asarray(b)).view(np.uint8)).sum())
+
+
+def test_mid_sweep_bitwise_invariance():
+    """16 fixed probes among random co-tokens at T in {1, 7, 128, 1024, 4096},
+    3 co-token seeds x 2 placements: 0 differing bits against each probe alone."""
+    cfg = I.CONFIGS["mid"]
+    L = layer(cfg)
+    probes = I.probes(cfg.H, 16, DEV)
+    ref = _probe_reference(cfg, L, probes)
+    for T in I.MID_SWEEP_T:
+        for rep in range(6):
+            nd = _check_probes(cfg, L, probes, ref, T, rep)
+            assert nd == 0, (T, rep, nd)
+        log(f"[invariance] mid T={T}: 0 differing bits over 6 batches")
+
+
+def test_large_layer_bitwise_invariance():
+    """Probes alone vs embedded in the full 16384-token large batch."""
+    cfg = I.CONFIGS["large"]
+    L = layer(cfg)
+    probes = I.probes(cfg.H, 16, DEV)
+    ref = _probe_reference(cfg, L, probes)
+    for T, rep in [(cfg.T, 0), (cfg.T, 1), (1000, 2)]:
+        assert _check_probes(cfg, L, probes, ref, T, rep) == 0
+    log("[invariance] large: 0 differing bits at T=16384 (2 placements) and T=1000")
+
+
+def test_position_within_tile_does_not_matter():
+    """One probe at each of 128 positions (every row slot of a token tile)."""
+    cfg = _cfg("mid", T=256)
+    L = layer(cfg)
+    probe = I.probes(cfg.H, 1, DEV)
+    ref = _probe_reference(cfg, L, probe)
+    x0 = I.make_tokens(cfg.T, cfg.H, 4242, "cpu").to(DEV)
+    for pos in range(0, 256, 2):
+        x = x0.clone()
+        x[pos] = probe[0]
+        o, ids, w = fwd(cfg, L, x)
+        assert np.array_equal(bits(o)[pos], ref[0][0]), pos
+    log("[invariance] probe bit-identical at 128 row positions")
+
+
+def test_run_to_run_determinism():
+    cfg = _cfg("mid", T=2048)
+    L = layer(cfg)
+    x = I.make_x(cfg, DEV)
+    a = bits(fwd(cfg, L, x)[0])
+    for _ in range(3):
+        assert np.array_equal(bits(fwd(cfg, L, x)[0]), a)
+
+
+def _k3_vs(ref_out, test_out, P):
+    """Schulman's k3 KL estimator of a downstream fp32 log-softmax over a vocab
+    projection: mean over the test distribution of (r - 1) - ln r, with
+    r = p_ref / p_test, in fp64."""
+    zr = (P @ torch.from_numpy(ref_out).double()).numpy()
+    zt = (P @ torch.from_numpy(test_out).double()).numpy()
+    zr = zr.astype(np.float32).astype(np.float64)
+    zt = zt.astype(np.float32).astype(np.float64)
+    lr = zr - (zr.max() + np.log(np.exp(zr - zr.max()).sum()))
+    lt = zt - (zt.max() + np.log(np.exp(zt - zt.max()).sum()))
+    logr = lr - lt
+    return float(np.sum(np.exp(lt) * (np.expm1(logr) - logr)))
+
+
+def test_decode_probe_invariant_and_variant_drift():
+    """Decode steps (T in {1, 4, 16, 64}) with the same probe each step: the
+    invariant path gives 0 differing bits and k3 = 0 exactly; the split-K
+    variant drifts."""
+    cfg = I.CONFIGS["dec"]
+    L = layer(cfg)
+    probe = I.probes(cfg.H, 1, DEV)
+    ref_inv = bits(fwd(cfg, L, probe, 0)[0])[0]
+    ref_var = bits(fwd(cfg, L, probe, 1)[0])[0]
+    g = torch.Generator().manual_seed(I.PROJ_SEED)
+    P = torch.randn((65536, cfg.H), generator=g).to(torch.bfloat16).double()
+    drift_bits, drift_k3 = 0, 0.0
+    for T in I.DEC_SWEEP_T:
+        for step in range(3):
+            x = I.make_tokens(T, cfg.H, I.COTOKEN_SEED_BASE + 13 * T + step, "cpu").to(DEV)
+            x[T // 2] = probe[0]
+            o_inv = bits(fwd(cfg, L, x, 0)[0])[T // 2]
+            assert np.array_equal(o_inv, ref_inv), (T, step)
+            o_var = bits(fwd(cfg, L, x, 1)[0])[T // 2]
+            drift_bits += _diffbits(o_var, ref_var)
+            if step == 0:
+                k3_inv = _k3_vs(I.bits_to_bf16(ref_inv).float().numpy(),
+                                I.bits_to_bf16(o_inv).float().numpy(), P)
+                assert k3_inv == 0.0
+                drift_k3 = max(drift_k3, _k3_vs(I.bits_to_bf16(ref_var).float().numpy(),
+                                                I.bits_to_bf16(o_var).float().numpy(), P))
+    log(f"[decode] invariant: 0 differing bits, k3 = 0; split-K variant: "
+        f"{drift_bits} differing bits, max k3 {drift_k3:.3e} (threshold 1e-3)")
+    assert drift_bits > 0
