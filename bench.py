@@ -47,11 +47,30 @@ def parse():
     ap.add_argument("--cpu-sample", type=int, default=None,
                     help="tokens of the oracle CPU baseline (0 disables)")
     ap.add_argument("--no-check", action="store_true", help="skip the probe invariance check")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run 3 plain device copies of MIB MiB (HBM counter calibration)")
     return ap.parse_args()
+
+
+def calibrate_copy(mib):
+    """Three device-to-device copies of a known size: the reference that the
+    FETCH_SIZE / WRITE_SIZE counters are scaled against."""
+    import torch
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n * 4, "copies": 3}), flush=True)
 
 
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (the MoE layer forward on one "
               "MI355X); --gpus must be 1", file=sys.stderr)

@@ -44,7 +44,16 @@ constexpr int kWaveT = kTileTok / 2;     // 64 token rows per wave
 constexpr int kMB = kWaveW / 16;         // 8 MFMA blocks along weights
 constexpr int kNB = kWaveT / 16;         // 4 MFMA blocks along tokens
 constexpr int kRowBytes = kTileK * 2;    // 128 bytes per staged row
-constexpr int kGroupM = 8;               // token tiles per raster group
+#ifndef MOE_GROUP_M
+#define MOE_GROUP_M 8
+#endif
+#ifndef MOE_XCD_REMAP
+#define MOE_XCD_REMAP 1
+#endif
+#ifndef MOE_BLOCKS_PER_CU
+#define MOE_BLOCKS_PER_CU 2
+#endif
+constexpr int kGroupM = MOE_GROUP_M;     // token tiles per raster group
 constexpr int kXcds = 8;
 
 constexpr int MODE_GATE_UP = 0;
@@ -94,7 +103,8 @@ __global__ __launch_bounds__(kThreads, 2) void expert_gemm_kernel(GemmParams P) 
     const int total = total_m * P.n_tiles;
     const int nblk = gridDim.x;
     const int per_xcd = nblk / kXcds;
-    const int slot = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+    const int slot = MOE_XCD_REMAP ? (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds
+                                   : (int)blockIdx.x;
     const int KT = P.K / kTileK;
 
     for (int base = 0; base < total; base += nblk) {
@@ -333,7 +343,7 @@ constexpr size_t kSmemBytes = (size_t)(kTileW + kTileTok) * kRowBytes;  // 48 KB
 
 int persistent_blocks() {
     int cu = device_cu_count();
-    int b = cu * 2;
+    int b = cu * MOE_BLOCKS_PER_CU;
     b = (b + kXcds - 1) / kXcds * kXcds;
     return b < kXcds ? kXcds : b;
 }
