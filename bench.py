@@ -28,6 +28,11 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, HERE)
 
 METRIC = "MoE-layer tokens/s + MFMA util; bitwise-identical output across batch sizes"
+
+# HBM bytes per launch of the gate/up kernel from rocprofv3 FETCH_SIZE (x2.0) and
+# WRITE_SIZE (x1.0) on the large workload (profiles/expert_gemm_large_T16384.md),
+# valid only for the kernel source they were taken on.
+TRAFFIC = {"kernel_sha256_prefix": "f7cda264f454d135", "workload": "large", "bytes": 53.48e9}
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 
@@ -50,6 +55,19 @@ def parse():
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 3 plain device copies of MIB MiB (HBM counter calibration)")
     return ap.parse_args()
+
+
+def traffic_bytes(workload, T):
+    """Profiled HBM bytes per gate/up launch, or None if the kernel source has
+    changed since the counters were taken (or for another workload)."""
+    import hashlib
+    src = os.path.join(HERE, "serve_router_gemm_amd", "csrc", "moe_gemm.hip")
+    with open(src, "rb") as f:
+        h = hashlib.sha256(f.read()).hexdigest()
+    if (not h.startswith(TRAFFIC["kernel_sha256_prefix"]) or workload != TRAFFIC["workload"]
+            or T != 16384):
+        return None
+    return TRAFFIC["bytes"]
 
 
 def calibrate_copy(mib):
@@ -209,7 +227,8 @@ def main():
         "roofline": {"kernel": "expert_gemm_kernel<gate_up> (moe_expert_gate_up)",
                      "bound": "mfma", "achieved": round(gu_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(gu_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(gu_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_bytes(cfg.name, T)},
         "stages_ms": {n: round(v, 4) for n, v in stage_ms.items()},
         "grouped_gemm_tflops": round(grouped_tflops, 2),
         "grouped_gemm_mfma_frac": round(grouped_tflops / PEAK_BF16_TFLOPS, 4),
