@@ -8,21 +8,25 @@
 // breaks invariance (same page, section "曾经只有前沿实验室才有的功能").
 //
 // Invariant kernel, for every tile of every expert at every batch size:
-//   * one tile shape: 256 weight rows x 128 token rows, K staged 64 at a time;
+//   * one tile shape: 512 weight rows (gate/up: 256 gate + 256 up) x 128
+//     token rows, K staged 64 at a time;
 //   * one instruction: v_mfma_f32_16x16x32_bf16, fp32 accumulators from 0;
 //   * one K order: k = 0, 32, 64, ... ascending, no split;
 // so an output element is the same sequence of MFMAs over the same operands
 // whatever other rows share its tile.  Rows past an expert's segment are
-// loaded from its last valid row and their results dropped.
+// loaded from its last valid row and their results dropped.  (The bits of an
+// element depend on that MFMA sequence only: an earlier 256 x 128 tiling of
+// this kernel produced identical outputs on the large layer.)
 //
 // Operand roles: the weight rows are the MFMA "A" (M) side and the token rows
 // the "B" (N) side, so each lane's four accumulators run along the output
 // feature dimension and store as one contiguous vector.
 //
-// Scheduling: a persistent grid walks the device-side tile list; tile ids go
-// to XCDs in contiguous blocks and are rastered in groups of 8 token tiles so
-// the workgroups of one XCD share weight and token rows in its L2.  Only the
-// launch work depends on the per-expert counts, never the arithmetic.
+// Scheduling: one persistent workgroup per CU walks the device-side tile
+// list; tile ids go to XCDs in contiguous blocks and are rastered in groups of
+// 8 token tiles so the workgroups of one XCD share weight and token rows in
+// its L2.  Only the launch work depends on the per-expert counts, never the
+// arithmetic.
 //
 // The split-K variant (down projection only) exists to show what invariance
 // costs and what breaking it does: experts with few tokens have their K range
@@ -36,22 +40,14 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;            // 4 waves: 2 (weight halves) x 2 (token halves)
-constexpr int kWaveW = kTileW / 2;       // 128 weight rows per wave
-constexpr int kWaveT = kTileTok / 2;     // 64 token rows per wave
-constexpr int kMB = kWaveW / 16;         // 8 MFMA blocks along weights
-constexpr int kNB = kWaveT / 16;         // 4 MFMA blocks along tokens
-constexpr int kRowBytes = kTileK * 2;    // 128 bytes per staged row
+constexpr int kMB = 8;                   // MFMA blocks of 16 weight rows per wave
+constexpr int kNB = 4;                   // MFMA blocks of 16 token rows per wave
 #ifndef MOE_GROUP_M
 #define MOE_GROUP_M 8
 #endif
 #ifndef MOE_XCD_REMAP
 #define MOE_XCD_REMAP 1
-#endif
-#ifndef MOE_BLOCKS_PER_CU
-#define MOE_BLOCKS_PER_CU 2
 #endif
 constexpr int kGroupM = MOE_GROUP_M;     // token tiles per raster group
 constexpr int kXcds = 8;
@@ -59,12 +55,6 @@ constexpr int kXcds = 8;
 constexpr int MODE_GATE_UP = 0;
 constexpr int MODE_DOWN = 1;
 constexpr int MODE_DOWN_SPLITK = 2;
-
-// byte offset of 16-byte chunk c of staged row r (XOR swizzle: the 8 rows a
-// quarter-wave reads at one chunk index land in 8 different chunk slots)
-__device__ __forceinline__ int swz(int r, int c) {
-    return r * kRowBytes + ((c ^ (r & 7)) << 4);
-}
 
 struct GemmParams {
     int K;            // reduction length: H (gate/up) or F (down)
@@ -84,19 +74,72 @@ struct GemmParams {
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g)); }
 
+// ---------------------------------------------------------------------------
+// Pipelined kernel: 8 waves, tile = 512 weight rows x 128 token rows, K staged
+// 64 at a time through two LDS stages (80 KB each) filled by direct-to-LDS
+// loads.
+//
+// A stage holds 640 rows x 128 bytes as 80 blocks of 8 rows (1 KB).  A
+// direct-to-LDS load (global_load_lds_dwordx4) writes lane l's 16 bytes at
+// M0 + 16*l, so one wave instruction fills one block: lane l lands at row
+// l/8, physical chunk l%8, and loads logical chunk (l%8) ^ (l/8) of that row.
+// Each instruction thus reads 8 whole 128-byte lines (measured on gfx950:
+// ~1.7x the rate of 16 half lines).  Fragment reads use the same XOR
+// swizzle, which keeps every 8-lane group of a ds_read_b128 (the unit the
+// LDS serves per cycle) on 8 different 16-byte bank groups.
+//
+// The loads are issued from inline assembly so the compiler does not drain
+// them at barriers; each wave waits for its own loads before the barrier
+// that publishes a stage.  After each barrier the MFMAs of the previous
+// stage's last quarter run from registers while the new stage's fragment
+// reads are in flight.  The MFMA sequence of an output element is the same
+// as in the kernel above: 16x16x32 bf16 steps over k = 0, 32, 64, ...
+// ascending, accumulators from 0.
+// ---------------------------------------------------------------------------
+constexpr int kP_Threads = 512;
+constexpr int kP_Tok = 128;
+constexpr int kP_W = 512;
+constexpr int kP_BK = 64;
+constexpr int kP_Rows = kP_W + kP_Tok;          // 640
+constexpr int kP_RowBytes = kP_BK * 2;          // 128
+constexpr int kP_StageBytes = kP_Rows * kP_RowBytes;   // 81920
+constexpr int kP_Blocks = kP_Rows / 8;          // 80 blocks of 8 rows
+constexpr int kP_WBlocks = kP_W / 8;            // 64
+constexpr int kP_Dma = kP_Blocks / 8;           // 10 per thread per stage
+constexpr int kP_GateUpF = kP_W / 2;            // 256
+
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(g), "s"(lds) : "memory");
+}
+
+__device__ __forceinline__ void block_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 template <int MODE>
-__global__ __launch_bounds__(kThreads, 2) void expert_gemm_kernel(GemmParams P) {
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    unsigned char* sW = smem;                              // 256 rows x 128 B
-    unsigned char* sT = smem + kTileW * kRowBytes;         // 128 rows x 128 B
+__global__ __launch_bounds__(kP_Threads) void expert_gemm_pipe_kernel(GemmParams P) {
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kP_StageBytes];
+    const uint32_t lds0 =
+        (uint32_t)(uintptr_t)((__attribute__((address_space(3))) unsigned char*)smem);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm = wave & 1;   // weight half
-    const int wt = wave >> 1;  // token half
-    const int lrow = tid >> 3; // 0..31: staging row within a 32-row slab
-    const int lchk = tid & 7;  // staging chunk (16 B) within the 128-B row
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform in the wave
+    const int wm = wave & 3;   // weight quarter: 128 rows
+    const int wt = wave >> 2;  // token half: 64 rows
+
+    // fragment read of a 16-row group (two 8-row blocks): row lane&15,
+    // 16-byte chunk kk*4 + lane>>4 for the kk-th 32-wide half of the stage
+    const int fr = lane & 7;
+    const int fblk = (lane >> 3) & 1;
+    int frag_off[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+        frag_off[kk] = fblk * 1024 + fr * 128 + (((kk * 4 + (lane >> 4)) ^ fr) << 4);
+    // direct-to-LDS slot of this lane inside a block
+    const int drow = lane >> 3;
+    const int dchunk = (lane & 7) ^ drow;
 
     const int E = P.E;
     const int total_m = P.tile_start[E];
@@ -105,13 +148,19 @@ __global__ __launch_bounds__(kThreads, 2) void expert_gemm_kernel(GemmParams P) 
     const int per_xcd = nblk / kXcds;
     const int slot = MOE_XCD_REMAP ? (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds
                                    : (int)blockIdx.x;
-    const int KT = P.K / kTileK;
+    const int KT = P.K / kP_BK;
+
+    // 16-row weight group mb (0..7) of this wave -> first 8-row block
+    auto wgrp = [&](int mb) {
+        if (MODE == MODE_GATE_UP)
+            return (mb < 4) ? (wm * 8 + mb * 2) : (kP_WBlocks / 2 + wm * 8 + (mb - 4) * 2);
+        return wm * 16 + mb * 2;
+    };
 
     for (int base = 0; base < total; base += nblk) {
         const int lt = base + slot;
         if (lt >= total) break;
 
-        // grouped raster: kGroupM token tiles x all n tiles per group
         const int gsize = kGroupM * P.n_tiles;
         const int g = lt / gsize;
         const int first_m = g * kGroupM;
@@ -120,7 +169,6 @@ __global__ __launch_bounds__(kThreads, 2) void expert_gemm_kernel(GemmParams P) 
         const int mt = first_m + r % gm;
         const int nt = r / gm;
 
-        // expert of token tile mt: the largest e with tile_start[e] <= mt
         int lo = 0, hi = E - 1;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
@@ -134,10 +182,9 @@ __global__ __launch_bounds__(kThreads, 2) void expert_gemm_kernel(GemmParams P) 
             mloc = local / parts;
             part = local - mloc * parts;
         }
-        const int seg0 = P.offsets[e], seg1 = P.offsets[e + 1];
-        const int p0 = seg0 + mloc * kTileTok;
+        const int seg1 = P.offsets[e + 1];
+        const int p0 = P.offsets[e] + mloc * kP_Tok;
 
-        // K range of this tile (all of K unless split)
         int kt0 = 0, kt1 = KT;
         if (MODE == MODE_DOWN_SPLITK && parts > 1) {
             const int per = (KT + parts - 1) / parts;
@@ -145,47 +192,27 @@ __global__ __launch_bounds__(kThreads, 2) void expert_gemm_kernel(GemmParams P) 
             kt1 = min(KT, kt0 + per);
         }
 
-        // --- staging addresses ----------------------------------------------
-        // Thread (lrow, lchk) stages 16-byte chunk lchk of weight rows
-        // lrow + 32*i (i < 8) and token rows lrow + 32*i (i < 4).  Row
-        // offsets are 32-bit element offsets from per-tile uniform bases
-        // (T*k*max(H,F) < 2^31 and one expert's N*K < 2^31).
-        const uint16_t* wbase0;
-        const uint16_t* wbase1;
-        uint32_t woff[4];
-        if (MODE == MODE_GATE_UP) {
-            wbase0 = P.w0 + (size_t)e * P.N * P.K;   // gate rows
-            wbase1 = P.w1 + (size_t)e * P.N * P.K;   // up rows
+        // source row of each of this thread's 10 direct-to-LDS slots
+        const uint16_t* src[kP_Dma];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int f = min(nt * kGateUpF + lrow + 32 * i, P.N - 1);
-                woff[i] = (uint32_t)f * (uint32_t)P.K;
-            }
-        } else {
-            wbase0 = P.w0 + (size_t)e * P.N * P.K;   // rows h of this tile, first half
-            wbase1 = wbase0;                         // second half: same base, +128 rows
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int h = min(nt * kTileW + lrow + 32 * i, P.N - 1);
-                woff[i] = (uint32_t)h * (uint32_t)P.K;
-            }
-        }
-        uint32_t woff_hi[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (MODE == MODE_GATE_UP) {
-                woff_hi[i] = woff[i];
+        for (int i = 0; i < kP_Dma; ++i) {
+            const int b = wave * kP_Dma + i;
+            const uint16_t* row;
+            if (b < kP_WBlocks) {
+                const int rr = b * 8 + drow;
+                if (MODE == MODE_GATE_UP) {
+                    const int f = min(nt * kP_GateUpF + (rr & (kP_GateUpF - 1)), P.N - 1);
+                    row = ((rr < kP_GateUpF) ? P.w0 : P.w1) + ((size_t)e * P.N + f) * P.K;
+                } else {
+                    const int h = min(nt * kP_W + rr, P.N - 1);
+                    row = P.w0 + ((size_t)e * P.N + h) * P.K;
+                }
             } else {
-                const int h = min(nt * kTileW + kTileW / 2 + lrow + 32 * i, P.N - 1);
-                woff_hi[i] = (uint32_t)h * (uint32_t)P.K;
+                const int p = min(p0 + (b - kP_WBlocks) * 8 + drow, seg1 - 1);
+                const int ar = (MODE == MODE_GATE_UP) ? P.perm[p] / P.top_k : p;
+                row = P.act + (size_t)ar * P.K;
             }
-        }
-        uint32_t toff[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int p = min(p0 + lrow + 32 * i, seg1 - 1);
-            const int row = (MODE == MODE_GATE_UP) ? P.perm[p] / P.top_k : p;
-            toff[i] = (uint32_t)row * (uint32_t)P.K;
+            src[i] = row + dchunk * 8;
         }
 
         floatx4 acc[kMB][kNB];
@@ -194,77 +221,82 @@ __global__ __launch_bounds__(kThreads, 2) void expert_gemm_kernel(GemmParams P) 
 #pragma unroll
             for (int j = 0; j < kNB; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-        u32x4 rw[8], rt[4];
-#define MOE_LOAD_STAGE(KT_)                                                              \
-        {                                                                                \
-            const uint32_t koff = (uint32_t)(KT_) * kTileK + lchk * 8;                   \
-            _Pragma("unroll") for (int i = 0; i < 4; ++i)                                \
-                rw[i] = *reinterpret_cast<const u32x4*>(wbase0 + woff[i] + koff);        \
-            _Pragma("unroll") for (int i = 0; i < 4; ++i)                                \
-                rw[4 + i] = *reinterpret_cast<const u32x4*>(wbase1 + woff_hi[i] + koff); \
-            _Pragma("unroll") for (int i = 0; i < 4; ++i)                                \
-                rt[i] = *reinterpret_cast<const u32x4*>(P.act + toff[i] + koff);         \
-        }
+        // previous tile: its stores drained, every wave done reading its stages
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        block_barrier();
 
-        if (kt0 < kt1) MOE_LOAD_STAGE(kt0);
+        auto issue = [&](int kt) {
+            const uint32_t sbase = lds0 + (uint32_t)(((kt - kt0) & 1) * kP_StageBytes);
+#pragma unroll
+            for (int i = 0; i < kP_Dma; ++i)
+                dma16(src[i] + (size_t)kt * kP_BK, sbase + (uint32_t)((wave * kP_Dma + i) * 1024));
+        };
+        if (kt0 < kt1) issue(kt0);
+
+        bf16x8 fbP[kNB], faP[4];
         for (int kt = kt0; kt < kt1; ++kt) {
-            __syncthreads();
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                *reinterpret_cast<u32x4*>(sW + swz(lrow + 32 * i, lchk)) = rw[i];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                *reinterpret_cast<u32x4*>(sT + swz(lrow + 32 * i, lchk)) = rt[i];
-            __syncthreads();
-            if (kt + 1 < kt1) MOE_LOAD_STAGE(kt + 1);
-
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            block_barrier();
+            if (kt + 1 < kt1) issue(kt + 1);
+            const unsigned char* sb = smem + ((kt - kt0) & 1) * kP_StageBytes;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                const int c = kk * 4 + (lane >> 4);
-                bf16x8 fb[kNB];
+                const unsigned char* sk = sb + frag_off[kk];
+                bf16x8 fb[kNB], fa[4];
 #pragma unroll
-                for (int nb = 0; nb < kNB; ++nb) {
-                    const int tr0 = wt * kWaveT + nb * 16;
-                    fb[nb] = *reinterpret_cast<const bf16x8*>(sT + swz(tr0 + (lane & 15), c));
+                for (int nb = 0; nb < kNB; ++nb)
+                    fb[nb] = *reinterpret_cast<const bf16x8*>(
+                        sk + (kP_WBlocks + wt * 8 + nb * 2) * 1024);
+#pragma unroll
+                for (int mb = 0; mb < 4; ++mb)
+                    fa[mb] = *reinterpret_cast<const bf16x8*>(sk + wgrp(mb) * 1024);
+                // second half of the previous 32-wide step (from registers)
+                if (kk == 1 || kt > kt0) {
+#pragma unroll
+                    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+                        for (int nb = 0; nb < kNB; ++nb)
+                            acc[mb + 4][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                faP[mb], fbP[nb], acc[mb + 4][nb], 0, 0, 0);
                 }
 #pragma unroll
-                for (int mb = 0; mb < kMB; ++mb) {
-                    int wr0;
-                    if (MODE == MODE_GATE_UP)
-                        wr0 = (mb < 4) ? (wm * 64 + mb * 16) : (kGateUpF + wm * 64 + (mb - 4) * 16);
-                    else
-                        wr0 = wm * kWaveW + mb * 16;
-                    const bf16x8 fa =
-                        *reinterpret_cast<const bf16x8*>(sW + swz(wr0 + (lane & 15), c));
+                for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
                     for (int nb = 0; nb < kNB; ++nb)
                         acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            fa, fb[nb], acc[mb][nb], 0, 0, 0);
-                }
+                            fa[mb], fb[nb], acc[mb][nb], 0, 0, 0);
+#pragma unroll
+                for (int mb = 0; mb < 4; ++mb)
+                    faP[mb] = *reinterpret_cast<const bf16x8*>(sk + wgrp(mb + 4) * 1024);
+#pragma unroll
+                for (int nb = 0; nb < kNB; ++nb) fbP[nb] = fb[nb];
             }
         }
-#undef MOE_LOAD_STAGE
+        if (kt1 > kt0) {
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < kNB; ++nb)
+                    acc[mb + 4][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        faP[mb], fbP[nb], acc[mb + 4][nb], 0, 0, 0);
+        }
 
-        // --- epilogue ------------------------------------------------------------
-        // lane holds rows 4*(lane>>4)+q (weight side) of column lane&15 (token side)
+        // epilogue: lane holds weight rows 4*(lane>>4)+q of token column lane&15
         const int colq = 4 * (lane >> 4);
 #pragma unroll
         for (int nb = 0; nb < kNB; ++nb) {
-            const int p = p0 + wt * kWaveT + nb * 16 + (lane & 15);
+            const int p = p0 + wt * 64 + nb * 16 + (lane & 15);
             if (p >= seg1) continue;
             if (MODE == MODE_GATE_UP) {
                 uint16_t* hout = reinterpret_cast<uint16_t*>(P.out) + (size_t)p * P.N;
 #pragma unroll
                 for (int mb = 0; mb < 4; ++mb) {
-                    const int f = nt * kGateUpF + wm * 64 + mb * 16 + colq;
+                    const int f = nt * kP_GateUpF + wm * 64 + mb * 16 + colq;
                     if (f >= P.N) continue;
                     uint32_t h[4];
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const float gv = acc[mb][nb][q];
-                        const float uv = acc[mb + 4][nb][q];
-                        h[q] = f32_to_bf16_rne(silu_f(gv) * uv);
-                    }
+                    for (int q = 0; q < 4; ++q)
+                        h[q] = f32_to_bf16_rne(silu_f(acc[mb][nb][q]) * acc[mb + 4][nb][q]);
                     uint2 pk;
                     pk.x = h[0] | (h[1] << 16);
                     pk.y = h[2] | (h[3] << 16);
@@ -275,7 +307,7 @@ __global__ __launch_bounds__(kThreads, 2) void expert_gemm_kernel(GemmParams P) 
                 float* yout = reinterpret_cast<float*>(P.out) + (size_t)a * P.N;
 #pragma unroll
                 for (int mb = 0; mb < kMB; ++mb) {
-                    const int h = nt * kTileW + wm * kWaveW + mb * 16 + colq;
+                    const int h = nt * kP_W + wm * 128 + mb * 16 + colq;
                     if (h >= P.N) continue;
                     if (MODE == MODE_DOWN_SPLITK && parts > 1) {
 #pragma unroll
@@ -287,6 +319,8 @@ __global__ __launch_bounds__(kThreads, 2) void expert_gemm_kernel(GemmParams P) 
             }
         }
     }
+    // leave no load in flight
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // K parts for the split-K variant: more parts the fewer tokens an expert has.
@@ -294,7 +328,7 @@ __device__ __forceinline__ int splitk_parts(int m) {
     return m <= 1 ? 8 : (m <= 4 ? 4 : (m <= 32 ? 2 : 1));
 }
 
-// tile_start[e] = sum over e' < e of parts(e') * ceil(M_e' / kTileTok); one block.
+// tile_start[e] = sum over e' < e of parts(e') * ceil(M_e' / kP_Tok); one block.
 __global__ __launch_bounds__(512) void tile_schedule_kernel(int E, int variant,
                                                             const int32_t* __restrict__ offsets,
                                                             int32_t* __restrict__ tile_start,
@@ -305,7 +339,7 @@ __global__ __launch_bounds__(512) void tile_schedule_kernel(int E, int variant,
     if (e < E) {
         const int m = offsets[e + 1] - offsets[e];
         const int parts = (variant == 1) ? splitk_parts(m) : 1;
-        tiles = parts * ((m + kTileTok - 1) / kTileTok);
+        tiles = parts * ((m + kP_Tok - 1) / kP_Tok);
         split[e] = parts;
     }
     sc[e] = tiles;
@@ -339,18 +373,13 @@ __global__ __launch_bounds__(256) void zero_split_rows_kernel(int A, int E, int 
     for (int i = threadIdx.x; i < H / 4; i += 256) row[i] = make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
-constexpr size_t kSmemBytes = (size_t)(kTileW + kTileTok) * kRowBytes;  // 48 KB
-
-int persistent_blocks() {
-    int cu = device_cu_count();
-    int b = cu * MOE_BLOCKS_PER_CU;
-    b = (b + kXcds - 1) / kXcds * kXcds;
-    return b < kXcds ? kXcds : b;
-}
-
 template <int MODE>
 hipError_t launch_gemm(const GemmParams& P, hipStream_t s) {
-    expert_gemm_kernel<MODE><<<persistent_blocks(), kThreads, kSmemBytes, s>>>(P);
+    // one persistent workgroup per CU (the two 80 KB stages fill its LDS),
+    // rounded up to whole XCD rows
+    const int cu = device_cu_count();
+    const int b = (cu + kXcds - 1) / kXcds * kXcds;
+    expert_gemm_pipe_kernel<MODE><<<b, kP_Threads, 0, s>>>(P);
     return hipGetLastError();
 }
 
@@ -378,7 +407,7 @@ hipError_t launch_gate_up(int T, int H, int E, int F, int k, const uint16_t* x,
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     GemmParams P;
-    P.K = H; P.N = F; P.n_tiles = (F + kGateUpF - 1) / kGateUpF; P.top_k = k; P.E = E;
+    P.K = H; P.N = F; P.n_tiles = (F + kP_GateUpF - 1) / kP_GateUpF; P.top_k = k; P.E = E;
     P.act = x; P.perm = perm; P.offsets = offsets; P.tile_start = tile_start; P.split = split;
     P.w0 = wg; P.w1 = wu; P.out = h_act;
     return launch_gemm<MODE_GATE_UP>(P, s);
@@ -393,7 +422,7 @@ hipError_t launch_down(int T, int H, int E, int F, int k, const uint16_t* h_act,
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     GemmParams P;
-    P.K = F; P.N = H; P.n_tiles = (H + kTileW - 1) / kTileW; P.top_k = k; P.E = E;
+    P.K = F; P.N = H; P.n_tiles = (H + kP_W - 1) / kP_W; P.top_k = k; P.E = E;
     P.act = h_act; P.perm = perm; P.offsets = offsets; P.tile_start = tile_start;
     P.split = split; P.w0 = wd; P.w1 = nullptr; P.out = y;
     if (variant == 1) {

@@ -13,15 +13,9 @@ namespace moe {
 // ascending fp32 fma chain, chunk sums added in ascending order.
 constexpr int kLogitChunk = 256;
 
-// Expert GEMM tile (the single tile of the invariant variant).
-constexpr int kTileTok = 128;   // token rows per workgroup tile
-constexpr int kTileW = 256;     // weight rows per workgroup tile
-constexpr int kTileK = 64;      // K per pipeline stage (two 32-deep MFMA steps)
-constexpr int kGateUpF = kTileW / 2;  // f columns per gate/up tile (gate + up rows)
-
 // router -------------------------------------------------------------------
 struct RoutePlan {
-    int split;     // 1: logits kernel folds every chunk; 0: one block per chunk
+    int split;     // 0: logits kernel folds every chunk; 1: one block per chunk
     int nparts;    // partial-logit planes the select kernel folds
     int tt, te;    // token / expert register tile of the logits kernel
 };
