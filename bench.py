@@ -224,7 +224,7 @@ def main():
                    "variant": "invariant" if args.variant == 0 else "splitk",
                    "active_experts": int((counts_np > 0).sum()),
                    "max_expert_tokens": int(counts_np.max())},
-        "roofline": {"kernel": "expert_gemm_kernel<gate_up> (moe_expert_gate_up)",
+        "roofline": {"kernel": "expert_gemm_pipe_kernel<0> (moe_expert_gate_up)",
                      "bound": "mfma", "achieved": round(gu_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(gu_tflops / PEAK_BF16_TFLOPS, 4),

@@ -8,15 +8,15 @@
 // breaks invariance (same page, section "曾经只有前沿实验室才有的功能").
 //
 // Invariant kernel, for every tile of every expert at every batch size:
-//   * one tile shape: 512 weight rows (gate/up: 256 gate + 256 up) x 128
+//   * one tile shape: 256 weight rows (gate/up: 128 gate + 128 up) x 256
 //     token rows, K staged 64 at a time;
 //   * one instruction: v_mfma_f32_16x16x32_bf16, fp32 accumulators from 0;
 //   * one K order: k = 0, 32, 64, ... ascending, no split;
 // so an output element is the same sequence of MFMAs over the same operands
 // whatever other rows share its tile.  Rows past an expert's segment are
 // loaded from its last valid row and their results dropped.  (The bits of an
-// element depend on that MFMA sequence only: an earlier 256 x 128 tiling of
-// this kernel produced identical outputs on the large layer.)
+// element depend on that MFMA sequence only: 256 x 128 and 512 x 128 tilings
+// of this kernel produced identical outputs on the large layer.)
 //
 // Operand roles: the weight rows are the MFMA "A" (M) side and the token rows
 // the "B" (N) side, so each lane's four accumulators run along the output
@@ -75,11 +75,11 @@ struct GemmParams {
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g)); }
 
 // ---------------------------------------------------------------------------
-// Pipelined kernel: 8 waves, tile = 512 weight rows x 128 token rows, K staged
-// 64 at a time through two LDS stages (80 KB each) filled by direct-to-LDS
-// loads.
+// Pipelined kernel: 8 waves, tile = 256 weight rows x 256 token rows, K staged
+// 64 at a time through two LDS stages (64 KB each) filled by direct-to-LDS
+// loads.  Each wave computes 128 weight rows x 64 token rows.
 //
-// A stage holds 640 rows x 128 bytes as 80 blocks of 8 rows (1 KB).  A
+// A stage holds 512 rows x 128 bytes as 64 blocks of 8 rows (1 KB).  A
 // direct-to-LDS load (global_load_lds_dwordx4) writes lane l's 16 bytes at
 // M0 + 16*l, so one wave instruction fills one block: lane l lands at row
 // l/8, physical chunk l%8, and loads logical chunk (l%8) ^ (l/8) of that row.
@@ -90,23 +90,32 @@ __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g));
 //
 // The loads are issued from inline assembly so the compiler does not drain
 // them at barriers; each wave waits for its own loads before the barrier
-// that publishes a stage.  After each barrier the MFMAs of the previous
+// that publishes a stage.  A wave stalls at a load instruction until the
+// CU's address unit accepts it (about 16 cycles per 1 KB instruction on
+// gfx950), so only one wave per SIMD issues loads: the other wave of the
+// SIMD starts its MFMAs at once and keeps the matrix core busy meanwhile
+// (measured: 5% faster than every wave issuing an eighth of the loads).  After each barrier the MFMAs of the previous
 // stage's last quarter run from registers while the new stage's fragment
 // reads are in flight.  The MFMA sequence of an output element is the same
 // as in the kernel above: 16x16x32 bf16 steps over k = 0, 32, 64, ...
 // ascending, accumulators from 0.
 // ---------------------------------------------------------------------------
 constexpr int kP_Threads = 512;
-constexpr int kP_Tok = 128;
-constexpr int kP_W = 512;
+constexpr int kP_Tok = 256;
+constexpr int kP_W = 256;
 constexpr int kP_BK = 64;
-constexpr int kP_Rows = kP_W + kP_Tok;          // 640
+constexpr int kP_Rows = kP_W + kP_Tok;          // 512
 constexpr int kP_RowBytes = kP_BK * 2;          // 128
-constexpr int kP_StageBytes = kP_Rows * kP_RowBytes;   // 81920
-constexpr int kP_Blocks = kP_Rows / 8;          // 80 blocks of 8 rows
-constexpr int kP_WBlocks = kP_W / 8;            // 64
-constexpr int kP_Dma = kP_Blocks / 8;           // 10 per thread per stage
-constexpr int kP_GateUpF = kP_W / 2;            // 256
+constexpr int kP_StageBytes = kP_Rows * kP_RowBytes;   // 65536
+constexpr int kP_Blocks = kP_Rows / 8;          // 64 blocks of 8 rows
+constexpr int kP_WBlocks = kP_W / 8;            // 32
+#ifndef MOE_ISSUERS
+#define MOE_ISSUERS 4
+#endif
+constexpr int kP_Issuers = MOE_ISSUERS;         // waves that issue the stage loads
+constexpr int kP_Dma = kP_Blocks / kP_Issuers;  // loads per issuing thread per stage
+constexpr int kP_WDma = kP_WBlocks / kP_Issuers;   // the first of them: weight blocks
+constexpr int kP_GateUpF = kP_W / 2;            // 128
 
 __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
@@ -126,8 +135,8 @@ __global__ __launch_bounds__(kP_Threads) void expert_gemm_pipe_kernel(GemmParams
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform in the wave
-    const int wm = wave & 3;   // weight quarter: 128 rows
-    const int wt = wave >> 2;  // token half: 64 rows
+    const int wm = wave & 1;   // weight half: 128 rows (gate/up: 64 gate + 64 up)
+    const int wt = wave >> 1;  // token quarter: 64 rows
 
     // fragment read of a 16-row group (two 8-row blocks): row lane&15,
     // 16-byte chunk kk*4 + lane>>4 for the kk-th 32-wide half of the stage
@@ -192,11 +201,22 @@ __global__ __launch_bounds__(kP_Threads) void expert_gemm_pipe_kernel(GemmParams
             kt1 = min(KT, kt0 + per);
         }
 
-        // source row of each of this thread's 10 direct-to-LDS slots
+        // Rows of the token tile that hold tokens of this expert (>= 1); the
+        // rest is padding.  An 8-row token block with no valid row is not
+        // loaded (its LDS rows keep stale data that only reaches dropped
+        // results), and a wave whose 64 token rows are all padding skips its
+        // MFMAs.  A valid row's MFMA sequence is the same either way.
+        const int valid = seg1 - p0;
+        const int ntb = (valid + 7) >> 3;                 // token blocks to load
+        const bool active = wt * 64 < valid;              // uniform in the wave
+
+        // source row of each of this thread's direct-to-LDS slots: slot i of
+        // issuing wave w fills block i*kP_Issuers + w (weight blocks first)
+        const int iw = wave % kP_Issuers;
         const uint16_t* src[kP_Dma];
 #pragma unroll
         for (int i = 0; i < kP_Dma; ++i) {
-            const int b = wave * kP_Dma + i;
+            const int b = i * kP_Issuers + iw;
             const uint16_t* row;
             if (b < kP_WBlocks) {
                 const int rr = b * 8 + drow;
@@ -227,9 +247,12 @@ __global__ __launch_bounds__(kP_Threads) void expert_gemm_pipe_kernel(GemmParams
 
         auto issue = [&](int kt) {
             const uint32_t sbase = lds0 + (uint32_t)(((kt - kt0) & 1) * kP_StageBytes);
+            if (wave >= kP_Issuers) return;
 #pragma unroll
-            for (int i = 0; i < kP_Dma; ++i)
-                dma16(src[i] + (size_t)kt * kP_BK, sbase + (uint32_t)((wave * kP_Dma + i) * 1024));
+            for (int i = 0; i < kP_Dma; ++i) {
+                if (i >= kP_WDma && (i - kP_WDma) * kP_Issuers + iw >= ntb) continue;
+                dma16(src[i] + (size_t)kt * kP_BK, sbase + (uint32_t)((i * kP_Issuers + iw) * 1024));
+            }
         };
         if (kt0 < kt1) issue(kt0);
 
@@ -238,6 +261,7 @@ __global__ __launch_bounds__(kP_Threads) void expert_gemm_pipe_kernel(GemmParams
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             block_barrier();
             if (kt + 1 < kt1) issue(kt + 1);
+            if (!active) continue;
             const unsigned char* sb = smem + ((kt - kt0) & 1) * kP_StageBytes;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
@@ -272,7 +296,7 @@ __global__ __launch_bounds__(kP_Threads) void expert_gemm_pipe_kernel(GemmParams
                 for (int nb = 0; nb < kNB; ++nb) fbP[nb] = fb[nb];
             }
         }
-        if (kt1 > kt0) {
+        if (kt1 > kt0 && active) {
 #pragma unroll
             for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
@@ -375,7 +399,7 @@ __global__ __launch_bounds__(256) void zero_split_rows_kernel(int A, int E, int 
 
 template <int MODE>
 hipError_t launch_gemm(const GemmParams& P, hipStream_t s) {
-    // one persistent workgroup per CU (the two 80 KB stages fill its LDS),
+    // one persistent workgroup per CU (the two 64 KB stages hold its LDS),
     // rounded up to whole XCD rows
     const int cu = device_cu_count();
     const int b = (cu + kXcds - 1) / kXcds * kXcds;
