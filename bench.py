@@ -10,9 +10,10 @@ bitwise against moe_forward before timing), so HIP events on the launch stream
 can time each stage inside the timed region.
 
 Prints one JSON line: tokens/s, the dominant kernel's roofline fraction, the
-oracle's CPU baseline on a bounded sample, and the batch-invariance check of
-16 probe tokens embedded in the batch (differing bits against each probe
-alone; must be 0).
+oracle's CPU baseline on a bounded sample, the batch-invariance check of 16
+probe tokens embedded in the batch (differing bits against each probe alone;
+must be 0), and the same step with the split-K down projection (its time
+relative to the invariant step, and how many outputs it moves).
 """
 from __future__ import annotations
 
@@ -184,6 +185,43 @@ def main():
     ms_step = wall * 1000.0 / K
     value = T / (ms_step / 1000.0)
 
+    # The same step with the split-K down projection (load-dependent K split,
+    # fp32 atomics): the throughput invariance costs, and how many output
+    # elements move when the split changes the summation order.
+    variant_res = None
+    if args.variant == 0:
+        out_inv = out.clone()
+        ws_dv = M.workspace(M.OP_DOWN, T, H, E, F, k, 1)
+
+        def step_variant(ev=None):
+            M.route(x, L["w_router"], k, cfg.score, cfg.renorm, bias=bias, topk_ids=ids,
+                    topk_w=w, ws=ws_r)
+            M.permute(ids, E, counts, offsets, perm, inv, ws=ws_p)
+            M.expert_gate_up(x, perm, offsets, L["w_gate"], L["w_up"], k, h_act=h_act, ws=ws_g)
+            if ev is not None:
+                ev[0].record(stream)
+            M.expert_down(h_act, perm, offsets, L["w_down"], k, variant=1, y=y, ws=ws_dv)
+            if ev is not None:
+                ev[1].record(stream)
+            M.combine(y, w, out=out)
+
+        for _ in range(2):
+            step_variant()
+        KV = min(K, 10)
+        evv = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(KV)]
+        torch.cuda.synchronize()
+        tv = time.perf_counter()
+        for i in range(KV):
+            step_variant(evv[i])
+        torch.cuda.synchronize()
+        ms_var = (time.perf_counter() - tv) * 1000.0 / KV
+        down_var = float(np.mean([evv[i][0].elapsed_time(evv[i][1]) for i in range(KV)]))
+        moved = int((out.view(torch.int16) != out_inv.view(torch.int16)).sum().item())
+        variant_res = {"ms_per_step": round(ms_var, 4), "down_ms": round(down_var, 4),
+                       "invariant_over_variant_throughput": round(ms_var / ms_step, 4),
+                       "out_elements_differing": moved, "out_elements": T * H}
+        out.copy_(out_inv)
+
     counts_np = counts.cpu().numpy()
     gu_flops = 4.0 * A * H * F
     dn_flops = 2.0 * A * H * F
@@ -234,6 +272,7 @@ def main():
         "grouped_gemm_mfma_frac": round(grouped_tflops / PEAK_BF16_TFLOPS, 4),
         "combine_hbm_frac": round(comb_gbs / PEAK_HBM_GBS, 4),
         "probe_bits_differing": inv_bits,
+        "splitk_variant": variant_res,
     }
 
     # oracle on the host cores, bounded sample of the same workload

@@ -65,7 +65,8 @@ struct GemmParams {
     const uint16_t* act;       // gate/up: x [T,H]; down: h_act [A,F]
     const int32_t* perm;
     const int32_t* offsets;    // [E+1]
-    const int32_t* tile_start; // [E+1] prefix of token tiles (x split parts)
+    const int32_t* tile_start; // [E+1] prefix of long token tiles (x split parts)
+    const int32_t* tail;       // [1+E] count, then experts whose last tile is short
     const int32_t* split;      // [E] K parts per expert (split-K variant)
     const uint16_t* w0;        // w_gate or w_down [E, N, K]
     const uint16_t* w1;        // w_up (gate/up only)
@@ -151,7 +152,8 @@ __global__ __launch_bounds__(kP_Threads) void expert_gemm_pipe_kernel(GemmParams
     const int dchunk = (lane & 7) ^ drow;
 
     const int E = P.E;
-    const int total_m = P.tile_start[E];
+    const int total_long = P.tile_start[E];
+    const int total_m = total_long + P.tail[0];
     const int total = total_m * P.n_tiles;
     const int nblk = gridDim.x;
     const int per_xcd = nblk / kXcds;
@@ -178,13 +180,20 @@ __global__ __launch_bounds__(kP_Threads) void expert_gemm_pipe_kernel(GemmParams
         const int mt = first_m + r % gm;
         const int nt = r / gm;
 
-        int lo = 0, hi = E - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (P.tile_start[mid] <= mt) lo = mid; else hi = mid - 1;
+        int e, local;
+        if (mt < total_long) {
+            int lo = 0, hi = E - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (P.tile_start[mid] <= mt) lo = mid; else hi = mid - 1;
+            }
+            e = lo;
+            local = mt - P.tile_start[e];
+        } else {
+            // a short last tile: the list holds them after all long tiles
+            e = P.tail[1 + mt - total_long];
+            local = (P.offsets[e + 1] - P.offsets[e] - 1) / kP_Tok;
         }
-        const int e = lo;
-        const int local = mt - P.tile_start[e];
         int parts = 1, part = 0, mloc = local;
         if (MODE == MODE_DOWN_SPLITK) {
             parts = P.split[e];
@@ -352,30 +361,59 @@ __device__ __forceinline__ int splitk_parts(int m) {
     return m <= 1 ? 8 : (m <= 4 ? 4 : (m <= 32 ? 2 : 1));
 }
 
-// tile_start[e] = sum over e' < e of parts(e') * ceil(M_e' / kP_Tok); one block.
-__global__ __launch_bounds__(512) void tile_schedule_kernel(int E, int variant,
-                                                            const int32_t* __restrict__ offsets,
-                                                            int32_t* __restrict__ tile_start,
-                                                            int32_t* __restrict__ split) {
-    __shared__ int sc[512];
-    const int e = threadIdx.x;
-    int tiles = 0;
-    if (e < E) {
-        const int m = offsets[e + 1] - offsets[e];
-        const int parts = (variant == 1) ? splitk_parts(m) : 1;
-        tiles = parts * ((m + kP_Tok - 1) / kP_Tok);
-        split[e] = parts;
-    }
-    sc[e] = tiles;
-    __syncthreads();
+// The token-tile list.  A tile whose valid rows fill at most half of it
+// (<= 128 of 256) runs with half of its waves and takes about half as long.
+// Such short tiles (the last tile of an expert, at most one per expert) are
+// listed after every long tile, so that the 32 workgroups of an XCD, which
+// start a round of tiles together, finish it together too and stay in step
+// through K: that is what lets them share weight and token rows in L2.
+// (Measured on the large layer: L2 hit rate 48% -> 62% and gate/up 3%
+// faster.  The down projection keeps expert order: there a short tile moved
+// away from its expert's long tiles no longer shares their weights, which
+// cost more than the lockstep gained.)
+//   tile_start[e] = number of long tiles of experts e' < e (x split parts);
+//   tail[0] = number of short tiles, tail[1..] = their experts, ascending.
+// With reorder = 0 (and in the split-K variant) every tile is listed as long,
+// in expert order.  One block.
+__device__ __forceinline__ void block_scan_512(int* sc, int e) {
     for (int d = 1; d < 512; d <<= 1) {
         const int v = (e >= d) ? sc[e - d] : 0;
         __syncthreads();
         sc[e] += v;
         __syncthreads();
     }
-    if (e < E) tile_start[e] = sc[e] - tiles;
-    if (e == E - 1) tile_start[E] = sc[e];
+}
+
+__global__ __launch_bounds__(512) void tile_schedule_kernel(int E, int variant, int reorder,
+                                                            const int32_t* __restrict__ offsets,
+                                                            int32_t* __restrict__ tile_start,
+                                                            int32_t* __restrict__ split,
+                                                            int32_t* __restrict__ tail) {
+    __shared__ int sl[512], ss[512];
+    const int e = threadIdx.x;
+    int nlong = 0, nshort = 0;
+    if (e < E) {
+        const int m = offsets[e + 1] - offsets[e];
+        const int parts = (variant == 1) ? splitk_parts(m) : 1;
+        const int ntile = (m + kP_Tok - 1) / kP_Tok;
+        const int rem = m % kP_Tok;
+        nshort = (reorder && variant == 0 && rem != 0 && rem <= kP_Tok / 2) ? 1 : 0;
+        nlong = parts * ntile - nshort;
+        split[e] = parts;
+    }
+    sl[e] = nlong;
+    ss[e] = nshort;
+    __syncthreads();
+    block_scan_512(sl, e);
+    block_scan_512(ss, e);
+    if (e < E) {
+        tile_start[e] = sl[e] - nlong;
+        if (nshort) tail[1 + ss[e] - 1] = e;
+    }
+    if (e == E - 1) {
+        tile_start[E] = sl[e];
+        tail[0] = ss[e];
+    }
 }
 
 // Zero the y rows of experts whose down projection is split (they are summed
@@ -418,7 +456,7 @@ int device_cu_count() {
     return cu;
 }
 
-size_t gemm_sched_ws_bytes(int E) { return (size_t)(2 * E + 1) * sizeof(int32_t); }
+size_t gemm_sched_ws_bytes(int E) { return (size_t)(3 * E + 2) * sizeof(int32_t); }
 
 hipError_t launch_gate_up(int T, int H, int E, int F, int k, const uint16_t* x,
                           const int32_t* perm, const int32_t* offsets, const uint16_t* wg,
@@ -427,12 +465,14 @@ hipError_t launch_gate_up(int T, int H, int E, int F, int k, const uint16_t* x,
     (void)T;
     int32_t* tile_start = sched_ws;
     int32_t* split = sched_ws + E + 1;
-    tile_schedule_kernel<<<1, 512, 0, s>>>(E, 0, offsets, tile_start, split);
+    int32_t* tail = sched_ws + 2 * E + 1;
+    tile_schedule_kernel<<<1, 512, 0, s>>>(E, 0, 1, offsets, tile_start, split, tail);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     GemmParams P;
     P.K = H; P.N = F; P.n_tiles = (F + kP_GateUpF - 1) / kP_GateUpF; P.top_k = k; P.E = E;
     P.act = x; P.perm = perm; P.offsets = offsets; P.tile_start = tile_start; P.split = split;
+    P.tail = tail;
     P.w0 = wg; P.w1 = wu; P.out = h_act;
     return launch_gemm<MODE_GATE_UP>(P, s);
 }
@@ -442,13 +482,14 @@ hipError_t launch_down(int T, int H, int E, int F, int k, const uint16_t* h_act,
                        float* y, int variant, int32_t* sched_ws, hipStream_t s) {
     int32_t* tile_start = sched_ws;
     int32_t* split = sched_ws + E + 1;
-    tile_schedule_kernel<<<1, 512, 0, s>>>(E, variant, offsets, tile_start, split);
+    int32_t* tail = sched_ws + 2 * E + 1;
+    tile_schedule_kernel<<<1, 512, 0, s>>>(E, variant, 0, offsets, tile_start, split, tail);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     GemmParams P;
     P.K = F; P.N = H; P.n_tiles = (H + kP_W - 1) / kP_W; P.top_k = k; P.E = E;
     P.act = h_act; P.perm = perm; P.offsets = offsets; P.tile_start = tile_start;
-    P.split = split; P.w0 = wd; P.w1 = nullptr; P.out = y;
+    P.split = split; P.tail = tail; P.w0 = wd; P.w1 = nullptr; P.out = y;
     if (variant == 1) {
         const int A = T * k;
         zero_split_rows_kernel<<<A, 256, 0, s>>>(A, E, H, perm, offsets, split, y);

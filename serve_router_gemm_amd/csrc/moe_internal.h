@@ -33,7 +33,7 @@ hipError_t launch_permute(int A, int E, const int32_t* ids, int32_t* counts,
                           int32_t* ws, hipStream_t s);
 
 // expert GEMMs ---------------------------------------------------------------
-size_t gemm_sched_ws_bytes(int E);  // tile_start [E+1] + split [E]
+size_t gemm_sched_ws_bytes(int E);  // tile_start [E+1] + split [E] + short-tile list [1+E]
 hipError_t launch_gate_up(int T, int H, int E, int F, int k, const uint16_t* x,
                           const int32_t* perm, const int32_t* offsets,
                           const uint16_t* wg, const uint16_t* wu, uint16_t* h_act,
