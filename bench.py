@@ -33,7 +33,7 @@ METRIC = "MoE-layer tokens/s + MFMA util; bitwise-identical output across batch 
 # HBM bytes per launch of the gate/up kernel from rocprofv3 FETCH_SIZE (x2.0) and
 # WRITE_SIZE (x1.0) on the large workload (profiles/expert_gemm_large_T16384.md),
 # valid only for the kernel source they were taken on.
-TRAFFIC = {"kernel_sha256_prefix": "a3dbd4b00f7c8500", "workload": "large", "bytes": 21.57e9}
+TRAFFIC = {"kernel_sha256_prefix": "98a8c257a206144a", "workload": "large", "bytes": 23.75e9}
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 
