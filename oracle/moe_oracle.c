@@ -490,3 +490,88 @@ int orc_forward_tokens(int n, const int32_t* tokens, int H, int E, int F, int k,
     free(ids); free(w); free(y);
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* D8: the downstream measurement of a decode step                           */
+/* ------------------------------------------------------------------------ */
+/*
+ * Bit-identical layer outputs are a means; what training and serving compare
+ * is the log-probability a model assigns to the next token, and a KL
+ * estimate ("k3") between two runs judged against a small threshold (the
+ * best2ai.com page on numerical alignment and MoE routing, sections
+ * "数值差异如何扰乱学习" and "混合专家模型更难对齐").  The pages fix neither
+ * the projection's order nor the sums.  Reading taken here: the same pinned
+ * order as D1, and fixed chunked sums.
+ *   z[t,v]    = the D1 chain of out[t,:] against proj[v,:] (bf16 x bf16, fp32);
+ *   m         = max_v z[t,v];
+ *   S         = +0; for each chunk of 256 consecutive v (ascending): s = +0,
+ *               s = s + expf(z_v - m) for v ascending; S = S + s   (fp32);
+ *   logp[t,v] = z[t,v] - (m + logf(S))                               (fp32);
+ *   k3        (Schulman's estimator, r = p_ref / p_test):
+ *               d_v = logp_ref[v] - logp_test[v] (fp64), r - 1 = expm1(d_v),
+ *               ln r = d_v; mean = sum_v exp(logp_test[v]) * (expm1(d_v) - d_v)
+ *               in fp64, summed in the same chunked order as S; greedy = the
+ *               lowest v with the largest logp_test, and the k3 term there
+ *               (unweighted).  The mean is the KL divergence of p_test from
+ *               p_ref; identical inputs give exactly 0.
+ */
+
+#define ORC_SUM_CHUNK 256
+
+void orc_lm_head_logits(int T, int H, int V, const uint16_t* h, const uint16_t* proj,
+                        float* z, int nthreads)
+{
+    orc_router_logits(T, H, V, h, proj, z, nthreads);
+}
+
+static void log_softmax_row(const float* z, int V, float* logp)
+{
+    float m = -INFINITY;
+    for (int v = 0; v < V; ++v) m = z[v] > m ? z[v] : m;
+    float S = 0.0f;
+    for (int c0 = 0; c0 < V; c0 += ORC_SUM_CHUNK) {
+        int c1 = c0 + ORC_SUM_CHUNK < V ? c0 + ORC_SUM_CHUNK : V;
+        float s = 0.0f;
+        for (int v = c0; v < c1; ++v) s = s + expf(z[v] - m);
+        S = S + s;
+    }
+    float lse = m + logf(S);
+    for (int v = 0; v < V; ++v) logp[v] = z[v] - lse;
+}
+
+void orc_log_softmax(int T, int V, const float* z, float* logp, int nthreads)
+{
+    int nt = set_threads(nthreads);
+    (void)nt;
+#pragma omp parallel for num_threads(nt) schedule(dynamic, 1)
+    for (int t = 0; t < T; ++t)
+        log_softmax_row(z + (int64_t)t * V, V, logp + (int64_t)t * V);
+}
+
+static double k3_term(float ref, float test)
+{
+    double d = (double)ref - (double)test;
+    return expm1(d) - d;
+}
+
+void orc_k3(int T, int V, const float* logp_ref, const float* logp_test, double* mean,
+            double* greedy_k3, int32_t* greedy)
+{
+    for (int t = 0; t < T; ++t) {
+        const float* r = logp_ref + (int64_t)t * V;
+        const float* q = logp_test + (int64_t)t * V;
+        double S = 0.0;
+        for (int c0 = 0; c0 < V; c0 += ORC_SUM_CHUNK) {
+            int c1 = c0 + ORC_SUM_CHUNK < V ? c0 + ORC_SUM_CHUNK : V;
+            double s = 0.0;
+            for (int v = c0; v < c1; ++v) s = s + exp((double)q[v]) * k3_term(r[v], q[v]);
+            S = S + s;
+        }
+        int best = 0;
+        for (int v = 1; v < V; ++v)
+            if (q[v] > q[best]) best = v;
+        mean[t] = S;
+        greedy[t] = best;
+        greedy_k3[t] = k3_term(r[best], q[best]);
+    }
+}

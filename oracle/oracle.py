@@ -60,6 +60,9 @@ def _declare(L):
     L.orc_forward_tokens.restype = i32
     L.orc_forward_tokens.argtypes = [i32, P, i32, i32, i32, i32, i32, i32, P, P, P, P, P,
                                      P, P, P, P, P, i32]
+    L.orc_lm_head_logits.argtypes = [i32, i32, i32, P, P, P, i32]
+    L.orc_log_softmax.argtypes = [i32, i32, P, P, i32]
+    L.orc_k3.argtypes = [i32, i32, P, P, P, P, P]
 
 
 def _p(a):
@@ -218,3 +221,41 @@ def forward_tokens(tokens, x, wr, wg, wu, wd, k, score, renorm=True, bias=None, 
     if rc != 0:
         raise ValueError(f"orc_forward_tokens rc={rc}")
     return out, ids, w, gap
+
+
+# ---------------------------------------------------------------------------
+# D8: downstream measurement of a decode step (LM head, log-softmax, k3)
+# ---------------------------------------------------------------------------
+
+def lm_head_logits(h, proj, nthreads=0) -> np.ndarray:
+    """z [T,V] fp32 of bf16 rows h [T,H] against a bf16 projection [V,H], in the
+    pinned chunked order of the router logits."""
+    h, proj = _u16(h), _u16(proj)
+    T, H = h.shape
+    V = proj.shape[0]
+    z = np.empty((T, V), dtype=np.float32)
+    lib().orc_lm_head_logits(T, H, V, _p(h), _p(proj), _p(z), nthreads)
+    return z
+
+
+def log_softmax(z, nthreads=0) -> np.ndarray:
+    """fp32 log-softmax over the last axis with fixed chunked sums."""
+    z = _c(z, np.float32)
+    T, V = z.shape
+    out = np.empty_like(z)
+    lib().orc_log_softmax(T, V, _p(z), _p(out), nthreads)
+    return out
+
+
+def k3(logp_ref, logp_test):
+    """Schulman's k3 per row: (mean over p_test in fp64, k3 at the greedy token,
+    greedy token index)."""
+    r = _c(logp_ref, np.float32)
+    q = _c(logp_test, np.float32)
+    assert r.shape == q.shape and r.ndim == 2
+    T, V = q.shape
+    mean = np.empty(T, dtype=np.float64)
+    gk3 = np.empty(T, dtype=np.float64)
+    g = np.empty(T, dtype=np.int32)
+    lib().orc_k3(T, V, _p(r), _p(q), _p(mean), _p(gk3), _p(g))
+    return mean, gk3, g

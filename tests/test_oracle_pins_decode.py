@@ -1,0 +1,166 @@
+"""Pins of the oracle's downstream measurement of a decode step (no GPU).
+
+The LM-head logits, the fp32 log-softmax and Schulman's k3 estimator are
+checked against numpy's ordered sums, fp64 library routines within derived
+error bounds, closed forms and hand-built cases.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import scipy.special as sps
+import torch
+
+from oracle import oracle as O
+from serve_router_gemm_amd import inputs as I
+
+U = 2.0 ** -24
+
+
+def bits(t):
+    return I.bf16_bits(t)
+
+
+def _bf16_rows(n, d, seed, scale=1.0):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn((n, d), generator=g) * scale).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("H,V", [(256, 37), (320, 300), (1024, 129)])
+def test_lm_head_logits_are_the_chunked_fp32_chain(H, V):
+    """z[t,v]: 256-wide chunks of h, each an ascending fp32 running sum from
+    +0, chunk sums added in ascending order (numpy float32 cumsum adds left to
+    right with one rounding per step; bf16 x bf16 products are exact)."""
+    h = _bf16_rows(3, H, 1)
+    p = _bf16_rows(V, H, 2, 0.05)
+    z = O.lm_head_logits(bits(h), bits(p))
+    hf, pf = h.float().numpy(), p.float().numpy()
+    for t in range(3):
+        for v in range(V):
+            prod = (hf[t] * pf[v]).astype(np.float32)
+            parts = [np.cumsum(prod[c:c + 256], dtype=np.float32)[-1] for c in range(0, H, 256)]
+            ref = np.cumsum(np.array(parts, dtype=np.float32), dtype=np.float32)[-1]
+            assert z[t, v].view(np.uint32) == np.float32(ref).view(np.uint32), (t, v)
+
+
+def test_lm_head_logits_exact_on_dyadic_rows():
+    """Rows of small integers times powers of two: every partial sum is exact,
+    so z equals the exact integer dot product whatever the order."""
+    rng = np.random.default_rng(3)
+    H, V = 768, 50
+    h = rng.integers(-8, 9, size=(2, H)).astype(np.float32)
+    p = (rng.integers(-8, 9, size=(V, H)) * 0.25).astype(np.float32)
+    z = O.lm_head_logits(bits(torch.from_numpy(h).to(torch.bfloat16)),
+                         bits(torch.from_numpy(p).to(torch.bfloat16)))
+    assert np.array_equal(z.astype(np.float64), h.astype(np.float64) @ p.astype(np.float64).T)
+
+
+def _ls_bound(z, logp, chunk=256):
+    """First-order bound of |fp32 log-softmax - exact|: the positive chunked sum
+    S of exp(z - m) has relative error <= (chunk - 1 + nchunks + 2) u (the
+    additions plus the error of expf on each term); logf, the add of m and the
+    final subtraction each add half an ulp of their result."""
+    V = z.shape[-1]
+    nch = (V + chunk - 1) // chunk
+    m = z.max(axis=-1, keepdims=True).astype(np.float64)
+    lnS = sps.logsumexp(z.astype(np.float64) - m, axis=-1, keepdims=True)
+    rel = (min(chunk, V) - 1 + nch + 2) * U
+    return rel + U * (np.abs(lnS) + np.abs(m + lnS) + np.abs(logp.astype(np.float64))) + 1e-12
+
+
+@pytest.mark.parametrize("V", [1, 7, 256, 1000, 4096, 65536])
+def test_log_softmax_within_fp64_library_bound(V):
+    rng = np.random.default_rng(V)
+    z = (rng.standard_normal((4, V)) * 3).astype(np.float32)
+    z[1] *= 10.0            # a peaked row
+    logp = O.log_softmax(z)
+    exact = z.astype(np.float64) - sps.logsumexp(z.astype(np.float64), axis=-1, keepdims=True)
+    err = np.abs(logp.astype(np.float64) - exact)
+    bound = _ls_bound(z, logp)
+    assert np.all(err <= bound), float((err / bound).max())
+    # normalised within the same bound
+    tot = np.exp(logp.astype(np.float64)).sum(axis=-1)
+    assert np.all(np.abs(tot - 1.0) <= bound.max(axis=-1) * 1.01 + 2 * V * U)
+
+
+def test_log_softmax_constant_row_and_shift():
+    V = 1000
+    z = np.zeros((2, V), dtype=np.float32)
+    z[1] += np.float32(5.0)
+    logp = O.log_softmax(z)
+    # exp(0) = 1 exactly, S = V exactly, so logp = -(logf(V)) (to the rounding
+    # of m + logf(V) for the shifted row)
+    ref = np.float32(-math.log(V))
+    assert np.all(np.abs(logp[0] - ref) <= np.abs(np.spacing(ref)))
+    assert np.all(np.abs(logp[1] - ref) <= 2 * np.abs(np.spacing(np.float32(5.0 + math.log(V)))))
+
+
+def test_log_softmax_sum_order_is_chunked():
+    """The sum of exp is taken in 256-wide chunks: a row built so that the
+    chunked and the single running sum differ gives the chunked result."""
+    V = 512
+    # one term of 1, then terms of ~1e-8: each is lost when added to 1 (below
+    # half an ulp of 1) but 256 of them summed on their own are not
+    z = np.full((1, V), np.float32(math.log(1e-8)), dtype=np.float32)
+    z[0, 0] = 0.0
+    logp = O.log_softmax(z)
+    t = np.float32(math.exp(float(z[0, 1])))
+    # single running sum: 1 + tiny rounds back to 1 every step
+    s_single = np.float32(1.0)
+    for _ in range(V - 1):
+        s_single = np.float32(s_single + t)
+    # chunked: chunk 0 = 1 (+ 255 small terms, each lost), chunk 1 = 256 of them
+    c1 = np.cumsum(np.full(256, t, dtype=np.float32), dtype=np.float32)[-1]
+    s_chunk = np.float32(np.float32(1.0) + c1)
+    assert s_single != s_chunk
+    got_S = np.exp(-np.float64(logp[0, 0]))   # logp_0 = -log S
+    assert abs(got_S - float(s_chunk)) < abs(got_S - float(s_single))
+
+
+def _rows(seed, V, scale):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((3, V)) * scale).astype(np.float32)
+
+
+@pytest.mark.parametrize("V", [2, 300, 65536])
+def test_k3_mean_is_generalized_kl_divergence(V):
+    """sum_v p_test (r - 1 - ln r) with r = p_ref / p_test equals
+    sum_v [p_test ln(p_test/p_ref) - p_test + p_ref], which scipy.special.kl_div
+    evaluates elementwise (a library routine)."""
+    ref = O.log_softmax(_rows(1, V, 2.0))
+    test = O.log_softmax(_rows(2, V, 2.0))
+    mean, gk3, g = O.k3(ref, test)
+    pr, pt = np.exp(ref.astype(np.float64)), np.exp(test.astype(np.float64))
+    lib = sps.kl_div(pt, pr).sum(axis=-1)
+    assert np.allclose(mean, lib, rtol=1e-9, atol=1e-15)
+    assert np.all(mean > 0)
+    # greedy token and its term
+    for t in range(3):
+        v = int(np.argmax(test[t]))
+        assert g[t] == v
+        r = pr[t, v] / pt[t, v]
+        assert math.isclose(gk3[t], (r - 1) - math.log(r), rel_tol=1e-9, abs_tol=1e-15)
+
+
+def test_k3_identical_is_exactly_zero_and_two_point_closed_form():
+    lp = O.log_softmax(_rows(5, 4096, 3.0))
+    mean, gk3, _ = O.k3(lp, lp)
+    assert np.all(mean == 0.0) and np.all(gk3 == 0.0)
+    # two outcomes: KL(Bern(a) || Bern(b))
+    a, b = 0.3, 0.6
+    test = np.log(np.array([[a, 1 - a]], dtype=np.float32))
+    ref = np.log(np.array([[b, 1 - b]], dtype=np.float32))
+    mean, _, g = O.k3(ref, test)
+    pa, pb = np.exp(test.astype(np.float64))[0], np.exp(ref.astype(np.float64))[0]
+    kl = pa[0] * math.log(pa[0] / pb[0]) + pa[1] * math.log(pa[1] / pb[1]) - pa.sum() + pb.sum()
+    assert math.isclose(mean[0], kl, rel_tol=1e-12)
+    assert g[0] == 1
+
+
+def test_k3_greedy_tie_takes_lowest_index():
+    test = np.log(np.array([[0.1, 0.4, 0.1, 0.4]], dtype=np.float32))
+    ref = np.log(np.array([[0.25, 0.25, 0.25, 0.25]], dtype=np.float32))
+    _, _, g = O.k3(ref, test)
+    assert g[0] == 1
