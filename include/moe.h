@@ -192,6 +192,47 @@ int moe_forward(int T, int H, int E, int F, int top_k, int score, int renormaliz
                 uint16_t* out, int32_t* topk_ids, float* topk_w, int variant,
                 void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * The measurement downstream of a decode step.  What training and serving
+ * finally compare is the log-probability of the next token and a KL estimate
+ * (k3) between two runs, judged against a 0.001 threshold (best2ai.com page
+ * on numerical alignment and MoE routing, sections "数值差异如何扰乱学习" and
+ * "混合专家模型更难对齐").  The pages fix neither the projection's order nor
+ * the sums; these entry points pin both, so a token's results never depend
+ * on what else is in the call.  Limits: H a multiple of 64 in [64, 65536];
+ * 1 <= V <= 2^20; 0 <= T; T*V < 2^31.  No workspace.
+ * ------------------------------------------------------------------------ */
+
+/* Vocabulary projection (LM head) of layer outputs:
+ *   z[t,v] = sum_i h[t,i] * proj[v,i] in fp32, in the logits' order (i in
+ *   chunks of 256, each an ascending fp32 fma chain from +0, chunk sums added
+ *   in ascending order).
+ *   h [device] [T,H] bf16; proj [device] [V,H] bf16; z [device] out [T,V]. */
+int moe_lm_head_logits(int T, int H, int V, const uint16_t* h, const uint16_t* proj,
+                       float* z, void* stream);
+
+/* fp32 log-softmax over v with fixed sums:
+ *   m = max_v z; S = +0, for each chunk of 256 consecutive v (ascending):
+ *   s = +0, s = s + expf(z_v - m) for v ascending, S = S + s;
+ *   logp[t,v] = z[t,v] - (m + logf(S)).
+ *   z [device] [T,V] fp32; logp [device] out [T,V] fp32; logp == z allowed
+ *   (in place).  NaN inputs give NaN rows. */
+int moe_log_softmax(int T, int V, const float* z, float* logp, void* stream);
+
+/* Schulman's k3 estimator, r = p_ref / p_test, per row t:
+ *   d_v = logp_ref[t,v] - logp_test[t,v] (fp64),
+ *   k3_mean[t]   = sum_v exp(logp_test[t,v]) * (expm1(d_v) - d_v) in fp64,
+ *                  summed in the log-softmax's chunked order (this is the
+ *                  KL divergence of p_test from p_ref; identical rows give
+ *                  exactly 0);
+ *   greedy[t]    = the lowest v with the largest logp_test[t,v] (0 if
+ *                  logp_test[t,0] is NaN; other NaNs are skipped);
+ *   k3_greedy[t] = expm1(d) - d at v = greedy[t] (unweighted).
+ *   logp_ref, logp_test [device] [T,V] fp32; k3_mean, k3_greedy [device] out
+ *   [T] fp64; greedy [device] out [T] int32. */
+int moe_k3(int T, int V, const float* logp_ref, const float* logp_test, double* k3_mean,
+           double* k3_greedy, int32_t* greedy, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

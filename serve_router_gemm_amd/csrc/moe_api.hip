@@ -280,3 +280,45 @@ int moe_forward(int T, int H, int E, int F, int top_k, int score, int renormaliz
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// decode-step measurement
+// ---------------------------------------------------------------------------
+
+namespace {
+int check_vocab(int T, int V) {
+    if (T < 0 || V < 1 || V > moe::kMaxVocab) return MOE_ERR_SHAPE;
+    return ((long)T * (long)V > kMaxElems) ? MOE_ERR_SHAPE : 0;
+}
+}  // namespace
+
+int moe_lm_head_logits(int T, int H, int V, const uint16_t* h, const uint16_t* proj, float* z,
+                       void* stream) {
+    MOE_TRY(check_vocab(T, V));
+    MOE_TRY(check_dim(H));
+    if ((long)T * H > kMaxElems || (long)V * H > kMaxElems) return MOE_ERR_SHAPE;
+    if (T == 0) return MOE_OK;
+    if (!h || !proj || !z) return MOE_ERR_NULL;
+    if (!aligned16(h) || !aligned16(proj) || !aligned16(z)) return MOE_ERR_ALIGN;
+    return hip_rc(moe::launch_lm_logits(T, H, V, h, proj, z, S(stream)));
+}
+
+int moe_log_softmax(int T, int V, const float* z, float* logp, void* stream) {
+    MOE_TRY(check_vocab(T, V));
+    if (T == 0) return MOE_OK;
+    if (!z || !logp) return MOE_ERR_NULL;
+    if (!aligned16(z) || !aligned16(logp)) return MOE_ERR_ALIGN;
+    return hip_rc(moe::launch_log_softmax(T, V, z, logp, S(stream)));
+}
+
+int moe_k3(int T, int V, const float* logp_ref, const float* logp_test, double* k3_mean,
+           double* k3_greedy, int32_t* greedy, void* stream) {
+    MOE_TRY(check_vocab(T, V));
+    if (T == 0) return MOE_OK;
+    if (!logp_ref || !logp_test || !k3_mean || !k3_greedy || !greedy) return MOE_ERR_NULL;
+    if (!aligned16(logp_ref) || !aligned16(logp_test) || !aligned16(k3_mean) ||
+        !aligned16(k3_greedy) || !aligned16(greedy))
+        return MOE_ERR_ALIGN;
+    return hip_rc(moe::launch_k3(T, V, logp_ref, logp_test, k3_mean, k3_greedy, greedy,
+                                 S(stream)));
+}

@@ -42,6 +42,15 @@ hipError_t launch_down(int T, int H, int E, int F, int k, const uint16_t* h_act,
                        const int32_t* perm, const int32_t* offsets, const uint16_t* wd,
                        float* y, int variant, int32_t* sched_ws, hipStream_t s);
 
+// decode-step measurement: vocabulary projection, log-softmax, k3 ------------
+constexpr int kSumChunk = 256;     // fixed chunk of the vocabulary sums
+constexpr int kMaxVocab = 1 << 20;
+hipError_t launch_lm_logits(int T, int H, int V, const uint16_t* h, const uint16_t* proj,
+                            float* z, hipStream_t s);
+hipError_t launch_log_softmax(int T, int V, const float* z, float* logp, hipStream_t s);
+hipError_t launch_k3(int T, int V, const float* logp_ref, const float* logp_test,
+                     double* mean, double* greedy_k3, int32_t* greedy, hipStream_t s);
+
 // combine ------------------------------------------------------------------
 hipError_t launch_combine(int T, int H, int k, const float* y, const float* w,
                           uint16_t* out, hipStream_t s);

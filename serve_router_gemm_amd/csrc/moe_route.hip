@@ -243,6 +243,16 @@ size_t route_ws_bytes(int T, int H, int E) {
     return (size_t)p.nparts * (size_t)T * (size_t)E * sizeof(float);
 }
 
+// Vocabulary projection of a decode step (z = h . proj^T) in the router's
+// pinned order: the same kernel, folded, one register tile per thread (one
+// token per thread for the few-token batches of decoding).  Each z depends
+// only on its own row pair, so the tile never changes its bits.
+hipError_t launch_lm_logits(int T, int H, int V, const uint16_t* h, const uint16_t* proj,
+                            float* z, hipStream_t s) {
+    if (T <= 8) return launch_logits<1, 4, false>(T, H, V, h, proj, z, s);
+    return launch_logits<8, 4, false>(T, H, V, h, proj, z, s);
+}
+
 hipError_t launch_route(int T, int H, int E, int k, int score, int renorm, const uint16_t* x,
                         const uint16_t* wr, const float* bias, int32_t* ids, float* w,
                         float* part_ws, hipStream_t s) {

@@ -43,6 +43,9 @@ SIGNATURES = {
     "moe_combine": (_I, [_I, _I, _I, _P, _P, _P, _P]),
     "moe_forward": (_I, [_I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I,
                          _P, _Z, _P]),
+    "moe_lm_head_logits": (_I, [_I, _I, _I, _P, _P, _P, _P]),
+    "moe_log_softmax": (_I, [_I, _I, _P, _P, _P]),
+    "moe_k3": (_I, [_I, _I, _P, _P, _P, _P, _P, _P]),
 }
 
 _lib = None
@@ -272,3 +275,45 @@ def forward(x, w_router, w_gate, w_up, w_down, top_k, score=SCORE_SOFTMAX, renor
     if return_routing:
         return out, topk_ids, topk_w
     return out
+
+
+def lm_head_logits(h, proj, z=None, stream=None):
+    """moe_lm_head_logits: z [T, V] fp32 = h [T, H] . proj [V, H]^T in the pinned order."""
+    T, H = h.shape
+    V = proj.shape[0]
+    _dev(h, "h", torch.bfloat16, (T, H))
+    _dev(proj, "proj", torch.bfloat16, (V, H))
+    if z is None:
+        z = torch.empty((T, V), dtype=torch.float32, device=h.device)
+    _dev(z, "z", torch.float32, (T, V))
+    rc = lib().moe_lm_head_logits(T, H, V, _ptr(h), _ptr(proj), _ptr(z), _stream(stream))
+    _check("moe_lm_head_logits", rc)
+    return z
+
+
+def log_softmax(z, out=None, stream=None):
+    """moe_log_softmax: fp32 log-softmax over the last axis (out may be z)."""
+    T, V = z.shape
+    _dev(z, "z", torch.float32, (T, V))
+    if out is None:
+        out = torch.empty_like(z)
+    _dev(out, "out", torch.float32, (T, V))
+    rc = lib().moe_log_softmax(T, V, _ptr(z), _ptr(out), _stream(stream))
+    _check("moe_log_softmax", rc)
+    return out
+
+
+def k3(logp_ref, logp_test, stream=None):
+    """moe_k3: -> (k3_mean [T] fp64, k3_greedy [T] fp64, greedy [T] int32)."""
+    T, V = logp_test.shape
+    _dev(logp_ref, "logp_ref", torch.float32, (T, V))
+    _dev(logp_test, "logp_test", torch.float32, (T, V))
+    dev = logp_test.device
+    mean = torch.empty(T, dtype=torch.float64, device=dev)
+    gk3 = torch.empty(T, dtype=torch.float64, device=dev)
+    g = torch.empty(T, dtype=torch.int32, device=dev)
+    rc = lib().moe_k3(T, V, _ptr(logp_ref), _ptr(logp_test), _ptr(mean), _ptr(gk3), _ptr(g),
+                      _stream(stream))
+    _check("moe_k3", rc)
+    return mean, gk3, g
+

@@ -19,7 +19,7 @@ OK, NULL, SHAPE, ALIGN, UNSUP, WS = 0, -1, -2, -3, -4, -5
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
 
 
 @pytest.fixture(scope="module")
@@ -153,3 +153,25 @@ def test_workspace_sizes(L):
     assert wb(M.OP_FORWARD, T, 100, E, F, k, 0) == 0
     assert wb(M.OP_FORWARD, T, H, E, F, k, 5) == 0
     assert wb(99, T, H, E, F, k, 0) == 0
+
+
+def test_decode_measurement_checks(L):
+    lm = L.moe_lm_head_logits
+    assert lm(4, 64, 100, None, FAKE, FAKE, None) == NULL
+    assert lm(4, 64, 100, FAKE, MIS, FAKE, None) == ALIGN
+    assert lm(4, 65, 100, FAKE, FAKE, FAKE, None) == UNSUP
+    assert lm(4, 64, 0, FAKE, FAKE, FAKE, None) == SHAPE
+    assert lm(4, 64, (1 << 20) + 1, FAKE, FAKE, FAKE, None) == SHAPE
+    assert lm(-1, 64, 100, FAKE, FAKE, FAKE, None) == SHAPE
+    assert lm(0, 64, 100, None, None, None, None) == OK
+    ls = L.moe_log_softmax
+    assert ls(4, 100, None, FAKE, None) == NULL
+    assert ls(4, 100, FAKE, MIS, None) == ALIGN
+    assert ls(4, 0, FAKE, FAKE, None) == SHAPE
+    assert ls(1 << 12, 1 << 20, FAKE, FAKE, None) == SHAPE       # T*V >= 2^31
+    assert ls(0, 100, None, None, None) == OK
+    k3 = L.moe_k3
+    assert k3(4, 100, FAKE, FAKE, FAKE, FAKE, None, None) == NULL
+    assert k3(4, 100, FAKE, FAKE, FAKE, MIS, FAKE, None) == ALIGN
+    assert k3(4, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None) == SHAPE
+    assert k3(0, 100, None, None, None, None, None, None) == OK

@@ -207,18 +207,10 @@ def test_run_to_run_determinism():
         assert np.array_equal(bits(fwd(cfg, L, x)[0]), a)
 
 
-def _k3_vs(ref_out, test_out, P):
-    """Schulman's k3 KL estimator of a downstream fp32 log-softmax over a vocab
-    projection: mean over the test distribution of (r - 1) - ln r, with
-    r = p_ref / p_test, in fp64."""
-    zr = (P @ torch.from_numpy(ref_out).double()).numpy()
-    zt = (P @ torch.from_numpy(test_out).double()).numpy()
-    zr = zr.astype(np.float32).astype(np.float64)
-    zt = zt.astype(np.float32).astype(np.float64)
-    lr = zr - (zr.max() + np.log(np.exp(zr - zr.max()).sum()))
-    lt = zt - (zt.max() + np.log(np.exp(zt - zt.max()).sum()))
-    logr = lr - lt
-    return float(np.sum(np.exp(lt) * (np.expm1(logr) - logr)))
+def _logp(out_row_bits, P):
+    """GPU log-probabilities of one layer output row (bf16 bits) over P."""
+    h = I.bits_to_bf16(out_row_bits).reshape(1, -1).to(DEV)
+    return M.log_softmax(M.lm_head_logits(h, P))
 
 
 def test_decode_probe_invariant_and_variant_drift():
@@ -231,7 +223,8 @@ def test_decode_probe_invariant_and_variant_drift():
     ref_inv = bits(fwd(cfg, L, probe, 0)[0])[0]
     ref_var = bits(fwd(cfg, L, probe, 1)[0])[0]
     g = torch.Generator().manual_seed(I.PROJ_SEED)
-    P = torch.randn((65536, cfg.H), generator=g).to(torch.bfloat16).double()
+    P = torch.randn((65536, cfg.H), generator=g).to(torch.bfloat16).to(DEV)
+    lp_inv, lp_var = _logp(ref_inv, P), _logp(ref_var, P)
     drift_bits, drift_k3 = 0, 0.0
     for T in I.DEC_SWEEP_T:
         for step in range(3):
@@ -242,11 +235,13 @@ def test_decode_probe_invariant_and_variant_drift():
             o_var = bits(fwd(cfg, L, x, 1)[0])[T // 2]
             drift_bits += _diffbits(o_var, ref_var)
             if step == 0:
-                k3_inv = _k3_vs(I.bits_to_bf16(ref_inv).float().numpy(),
-                                I.bits_to_bf16(o_inv).float().numpy(), P)
-                assert k3_inv == 0.0
-                drift_k3 = max(drift_k3, _k3_vs(I.bits_to_bf16(ref_var).float().numpy(),
-                                                I.bits_to_bf16(o_var).float().numpy(), P))
+                k3_inv, _, _ = M.k3(lp_inv, _logp(o_inv, P))
+                assert k3_inv.item() == 0.0
+                lv = _logp(o_var, P)
+                k3_var, _, _ = M.k3(lp_var, lv)
+                ok3, _, _ = O.k3(lp_var.cpu().numpy(), lv.cpu().numpy())
+                assert np.allclose(k3_var.cpu().numpy(), ok3, rtol=1e-9, atol=1e-18)
+                drift_k3 = max(drift_k3, k3_var.item())
     log(f"[decode] invariant: 0 differing bits, k3 = 0; split-K variant: "
         f"{drift_bits} differing bits, max k3 {drift_k3:.3e} (threshold 1e-3)")
     assert drift_bits > 0
