@@ -222,6 +222,42 @@ def main():
                        "out_elements_differing": moved, "out_elements": T * H}
         out.copy_(out_inv)
 
+    # Decode workload: the measurement downstream of the step (vocabulary
+    # projection, log-softmax, k3 of this batch against itself), timed on its
+    # own; the projection streams V x H bf16 weights.
+    decode_res = None
+    if cfg.name == "dec":
+        V = 65536
+        gp = torch.Generator().manual_seed(I.PROJ_SEED)
+        P = torch.randn((V, H), generator=gp).to(torch.bfloat16).to(dev)
+        z = torch.empty((T, V), dtype=torch.float32, device=dev)
+        lp = torch.empty_like(z)
+        for _ in range(2):
+            M.lm_head_logits(out, P, z=z)
+            M.log_softmax(z, out=lp)
+            M.k3(lp, lp)
+        KD = max(5, min(K, 20))
+        evd = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(KD)]
+        torch.cuda.synchronize()
+        for i in range(KD):
+            evd[i][0].record(stream)
+            M.lm_head_logits(out, P, z=z)
+            evd[i][1].record(stream)
+            M.log_softmax(z, out=lp)
+            evd[i][2].record(stream)
+            kmean, _, _ = M.k3(lp, lp)
+            evd[i][3].record(stream)
+        torch.cuda.synchronize()
+        dms = [float(np.mean([evd[i][j].elapsed_time(evd[i][j + 1]) for i in range(KD)]))
+               for j in range(3)]
+        proj_bytes = 2.0 * V * H
+        decode_res = {"vocab": V, "lm_head_ms": round(dms[0], 4),
+                      "lm_head_hbm_frac": round(proj_bytes / (dms[0] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                      "lm_head_valu_tflops": round(2.0 * T * V * H / (dms[0] * 1e-3) / 1e12, 2),
+                      "log_softmax_ms": round(dms[1], 4), "k3_ms": round(dms[2], 4),
+                      "k3_self": float(kmean.max().item())}
+        del P, z, lp
+
     counts_np = counts.cpu().numpy()
     gu_flops = 4.0 * A * H * F
     dn_flops = 2.0 * A * H * F
@@ -229,6 +265,23 @@ def main():
     grouped_tflops = (gu_flops + dn_flops) / ((stage_ms["gate_up"] + stage_ms["down"]) * 1e-3) / 1e12
     comb_bytes = 4.0 * A * H + 4.0 * A + 2.0 * T * H
     comb_gbs = comb_bytes / (stage_ms["combine"] * 1e-3) / 1e9
+
+    # The gate/up kernel's bound: MFMA at prefill sizes; at decode sizes
+    # (T <= 64) it streams the active experts' gate and up weights from HBM.
+    if cfg.name == "dec":
+        active = int((counts.cpu().numpy() > 0).sum())
+        gu_bytes = active * 2.0 * F * H * 2 + 2.0 * T * H + 2.0 * A * F
+        gu_gbs = gu_bytes / (stage_ms["gate_up"] * 1e-3) / 1e9
+        roofline = {"kernel": "expert_gemm_pipe_kernel<0> (moe_expert_gate_up)",
+                    "bound": "hbm", "achieved": round(gu_gbs, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(gu_gbs / PEAK_HBM_GBS, 4),
+                    "traffic": traffic_bytes(cfg.name, T)}
+    else:
+        roofline = {"kernel": "expert_gemm_pipe_kernel<0> (moe_expert_gate_up)",
+                    "bound": "mfma", "achieved": round(gu_tflops, 2),
+                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(gu_tflops / PEAK_BF16_TFLOPS, 4),
+                    "traffic": traffic_bytes(cfg.name, T)}
 
     # batch invariance of the embedded probes: each probe alone (T = 1) vs in the batch
     inv_bits = None
@@ -262,11 +315,7 @@ def main():
                    "variant": "invariant" if args.variant == 0 else "splitk",
                    "active_experts": int((counts_np > 0).sum()),
                    "max_expert_tokens": int(counts_np.max())},
-        "roofline": {"kernel": "expert_gemm_pipe_kernel<0> (moe_expert_gate_up)",
-                     "bound": "mfma", "achieved": round(gu_tflops, 2),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(gu_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic_bytes(cfg.name, T)},
+        "roofline": roofline,
         "stages_ms": {n: round(v, 4) for n, v in stage_ms.items()},
         "grouped_gemm_tflops": round(grouped_tflops, 2),
         "grouped_gemm_mfma_frac": round(grouped_tflops / PEAK_BF16_TFLOPS, 4),
@@ -274,6 +323,8 @@ def main():
         "probe_bits_differing": inv_bits,
         "splitk_variant": variant_res,
     }
+    if decode_res is not None:
+        res["decode_measure"] = decode_res
 
     # oracle on the host cores, bounded sample of the same workload
     nsample = args.cpu_sample
