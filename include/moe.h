@@ -192,6 +192,32 @@ int moe_forward(int T, int H, int E, int F, int top_k, int score, int renormaliz
                 uint16_t* out, int32_t* topk_ids, float* topk_w, int variant,
                 void* ws, size_t ws_bytes, void* stream);
 
+/* Router replay: the whole layer with each token's experts given instead of
+ * selected.  The pages describe recording the routing decisions taken while
+ * generating a rollout and reusing them in the trainer, so that both use the
+ * same experts (best2ai.com page on numerical alignment and MoE routing,
+ * sections "MoE 路由会放大这种不匹配" and "Fireworks 保持训练循环一致";
+ * Fireworks page "位级一致：前沿训练的差异化关键", section
+ * "曾经只有前沿实验室才有的功能", names it the popular MoE fix).
+ *   topk_ids [device] [T,k] int32: the recorded experts, in recorded slot
+ *     order.  An id outside [0,E) contributes nothing: its expert output is
+ *     0 and, when weights are recomputed, its weight is 0 and it is left out
+ *     of the renormalisation.
+ *   topk_w [device] [T,k] fp32, or NULL: the recorded weights.  When NULL,
+ *     the weights are recomputed from w_router for the given experts exactly
+ *     as moe_route computes them (score, renormalize; the bias only shapes
+ *     selection, so it is not an argument), and w_out [device] [T,k] (may be
+ *     NULL) receives them.  w_router may be NULL when topk_w is given.
+ *   Everything else as moe_forward; the workspace is moe_forward's
+ *   (moe_workspace_bytes(MOE_OP_FORWARD, ...)).
+ * Replaying the ids (and weights) that moe_forward returned for the same
+ * inputs gives an out bit-identical to moe_forward's. */
+int moe_forward_replay(int T, int H, int E, int F, int top_k, int score, int renormalize,
+                       const uint16_t* x, const uint16_t* w_router, const int32_t* topk_ids,
+                       const float* topk_w, const uint16_t* w_gate, const uint16_t* w_up,
+                       const uint16_t* w_down, uint16_t* out, float* w_out, int variant,
+                       void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------------------
  * The measurement downstream of a decode step.  What training and serving
  * finally compare is the log-probability of the next token and a KL estimate

@@ -193,6 +193,34 @@ static float sigmoid_key_f32(float l, float b)
     return s + b;
 }
 
+/* D4: the weights of the experts ids[0..k-1] from one token's logits, in
+ * fp64, rounded to fp32 once.  An id outside [0,E) (router replay only) gets
+ * weight 0 and is left out of the renormalisation; a zero sum gives zeros. */
+static void weights_for(const float* logits, int E, int k, int score, int renorm,
+                        const int32_t* ids, float* w)
+{
+    double p[16];
+    if (score == ORC_SOFTMAX) {
+        double m = -INFINITY;
+        for (int e = 0; e < E; ++e)
+            if ((double)logits[e] > m) m = (double)logits[e];
+        double S = 0.0;
+        for (int e = 0; e < E; ++e) S += exp((double)logits[e] - m);
+        for (int j = 0; j < k; ++j)
+            p[j] = (ids[j] >= 0 && ids[j] < E) ? exp((double)logits[ids[j]] - m) / S : 0.0;
+    } else {
+        for (int j = 0; j < k; ++j)
+            p[j] = (ids[j] >= 0 && ids[j] < E) ? 1.0 / (1.0 + exp(-(double)logits[ids[j]])) : 0.0;
+    }
+    if (renorm) {
+        double D = 0.0;
+        for (int j = 0; j < k; ++j) D += p[j];
+        for (int j = 0; j < k; ++j) w[j] = D > 0.0 ? (float)(p[j] / D) : 0.0f;
+    } else {
+        for (int j = 0; j < k; ++j) w[j] = (float)p[j];
+    }
+}
+
 /* D1..D4 for one token. scratch: 2*E floats + E bytes. */
 static void route_one(const uint16_t* xrow, const uint16_t* wr, const float* bias,
                       int H, int E, int k, int score, int renorm,
@@ -220,25 +248,7 @@ static void route_one(const uint16_t* xrow, const uint16_t* wr, const float* bia
         }
     }
 
-    /* D4 weights in fp64 */
-    double p[16];
-    if (score == ORC_SOFTMAX) {
-        double m = -INFINITY;
-        for (int e = 0; e < E; ++e)
-            if ((double)logits[e] > m) m = (double)logits[e];
-        double S = 0.0;
-        for (int e = 0; e < E; ++e) S += exp((double)logits[e] - m);
-        for (int j = 0; j < k; ++j) p[j] = exp((double)logits[ids[j]] - m) / S;
-    } else {
-        for (int j = 0; j < k; ++j) p[j] = 1.0 / (1.0 + exp(-(double)logits[ids[j]]));
-    }
-    if (renorm) {
-        double D = 0.0;
-        for (int j = 0; j < k; ++j) D += p[j];
-        for (int j = 0; j < k; ++j) w[j] = (float)(p[j] / D);
-    } else {
-        for (int j = 0; j < k; ++j) w[j] = (float)p[j];
-    }
+    weights_for(logits, E, k, score, renorm, ids, w);
 }
 
 /* Route T tokens.  ids [T,k] int32, w [T,k] fp32, gap [T] fp64 (or NULL). */
@@ -574,4 +584,74 @@ void orc_k3(int T, int V, const float* logp_ref, const float* logp_test, double*
         greedy[t] = best;
         greedy_k3[t] = k3_term(r[best], q[best]);
     }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Router replay                                                             */
+/* ------------------------------------------------------------------------ */
+/*
+ * The pages describe router replay as recording the expert choices made
+ * while generating a rollout and reusing them in the trainer (best2ai.com
+ * page on numerical alignment and MoE routing, sections
+ * "MoE 路由会放大这种不匹配" and "Fireworks 保持训练循环一致").  Reading
+ * taken: the layer of D5..D7 with the experts of each slot given (ids
+ * [T,k], recorded slot order); the weights either given too, or those of D4
+ * for the given experts.  An id outside [0,E) contributes nothing (expert
+ * output 0; weight 0 when recomputed, and left out of the renormalisation).
+ * Evaluated token by token (no permutation), like orc_forward_tokens.
+ */
+int orc_replay_weights(int T, int H, int E, int k, int score, int renorm, const uint16_t* x,
+                       const uint16_t* wr, const int32_t* ids, float* w, int nthreads)
+{
+    if (k < 1 || k > 16) return -2;
+    int nt = set_threads(nthreads);
+    (void)nt;
+#pragma omp parallel num_threads(nt)
+    {
+        float* logits = (float*)malloc(sizeof(float) * (size_t)E);
+#pragma omp for schedule(dynamic, 4)
+        for (int t = 0; t < T; ++t) {
+            const uint16_t* xrow = x + (int64_t)t * H;
+            for (int e = 0; e < E; ++e) logits[e] = logit_one(xrow, wr + (int64_t)e * H, H);
+            weights_for(logits, E, k, score, renorm, ids + (int64_t)t * k, w + (int64_t)t * k);
+        }
+        free(logits);
+    }
+    return 0;
+}
+
+int orc_forward_replay(int T, int H, int E, int F, int k, int score, int renorm,
+                       const uint16_t* x, const uint16_t* wr, const int32_t* ids,
+                       const float* w_in, const uint16_t* wg, const uint16_t* wu,
+                       const uint16_t* wd, uint16_t* out, float* w_out, int nthreads)
+{
+    if (k < 1 || k > 16) return -2;
+    int nt = set_threads(nthreads);
+    (void)nt;
+    float* w = (float*)malloc(sizeof(float) * (size_t)T * k + 4);
+    float* y = (float*)malloc(sizeof(float) * ((size_t)T * k * H + 1));
+    if (w_in)
+        memcpy(w, w_in, sizeof(float) * (size_t)T * k);
+    else
+        orc_replay_weights(T, H, E, k, score, renorm, x, wr, ids, w, nthreads);
+#pragma omp parallel num_threads(nt)
+    {
+        double* act_d = (double*)malloc(sizeof(double) * (size_t)F);
+#pragma omp for schedule(dynamic, 1)
+        for (int r = 0; r < T * k; ++r) {
+            const int t = r / k;
+            const int e = ids[r];
+            if (e < 0 || e >= E) {
+                memset(y + (int64_t)r * H, 0, sizeof(float) * (size_t)H);
+                continue;
+            }
+            expert_one(x + (int64_t)t * H, e, H, F, wg, wu, wd, NULL, y + (int64_t)r * H, act_d);
+        }
+        free(act_d);
+    }
+    orc_combine(T, H, k, y, w, out);
+    if (w_out) memcpy(w_out, w, sizeof(float) * (size_t)T * k);
+    free(w);
+    free(y);
+    return 0;
 }

@@ -60,6 +60,11 @@ def _declare(L):
     L.orc_forward_tokens.restype = i32
     L.orc_forward_tokens.argtypes = [i32, P, i32, i32, i32, i32, i32, i32, P, P, P, P, P,
                                      P, P, P, P, P, i32]
+    L.orc_replay_weights.restype = i32
+    L.orc_replay_weights.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, P, i32]
+    L.orc_forward_replay.restype = i32
+    L.orc_forward_replay.argtypes = [i32, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P,
+                                     P, i32]
     L.orc_lm_head_logits.argtypes = [i32, i32, i32, P, P, P, i32]
     L.orc_log_softmax.argtypes = [i32, i32, P, P, i32]
     L.orc_k3.argtypes = [i32, i32, P, P, P, P, P]
@@ -259,3 +264,40 @@ def k3(logp_ref, logp_test):
     g = np.empty(T, dtype=np.int32)
     lib().orc_k3(T, V, _p(r), _p(q), _p(mean), _p(gk3), _p(g))
     return mean, gk3, g
+
+
+# ---------------------------------------------------------------------------
+# router replay
+# ---------------------------------------------------------------------------
+
+def replay_weights(x, wr, ids, score, renorm=True, nthreads=0) -> np.ndarray:
+    """D4 weights of the given experts ids [T,k] (ids outside [0,E) get 0)."""
+    x, wr = _u16(x), _u16(wr)
+    ids = _c(ids, np.int32)
+    T, H = x.shape
+    E = wr.shape[0]
+    k = ids.shape[1]
+    w = np.empty((T, k), dtype=np.float32)
+    rc = lib().orc_replay_weights(T, H, E, k, score, int(renorm), _p(x), _p(wr), _p(ids), _p(w),
+                                  nthreads)
+    if rc != 0:
+        raise ValueError(f"orc_replay_weights rc={rc}")
+    return w
+
+
+def forward_replay(x, wr, ids, wg, wu, wd, score, renorm=True, w=None, nthreads=0):
+    """The layer with the experts given (router replay): -> (out bf16 bits, weights used)."""
+    x, wg, wu, wd = _u16(x), _u16(wg), _u16(wu), _u16(wd)
+    wr = None if wr is None else _u16(wr)
+    ids = _c(ids, np.int32)
+    T, H = x.shape
+    E, F = wg.shape[0], wg.shape[1]
+    k = ids.shape[1]
+    w_in = None if w is None else _c(w, np.float32)
+    out = np.empty((T, H), dtype=np.uint16)
+    w_out = np.empty((T, k), dtype=np.float32)
+    rc = lib().orc_forward_replay(T, H, E, F, k, score, int(renorm), _p(x), _p(wr), _p(ids),
+                                  _p(w_in), _p(wg), _p(wu), _p(wd), _p(out), _p(w_out), nthreads)
+    if rc != 0:
+        raise ValueError(f"orc_forward_replay rc={rc}")
+    return out, w_out

@@ -281,6 +281,53 @@ int moe_forward(int T, int H, int E, int F, int top_k, int score, int renormaliz
 
 }  // extern "C"
 
+int moe_forward_replay(int T, int H, int E, int F, int top_k, int score, int renormalize,
+                       const uint16_t* x, const uint16_t* w_router, const int32_t* topk_ids,
+                       const float* topk_w, const uint16_t* w_gate, const uint16_t* w_up,
+                       const uint16_t* w_down, uint16_t* out, float* w_out, int variant,
+                       void* ws, size_t ws_bytes, void* stream) {
+    MOE_TRY(check_layer(T, H, E, F, top_k));
+    if (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID) return MOE_ERR_UNSUPPORTED;
+    if (renormalize != 0 && renormalize != 1) return MOE_ERR_UNSUPPORTED;
+    if (variant != MOE_GEMM_INVARIANT && variant != MOE_GEMM_SPLITK_VARIANT)
+        return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!x || !topk_ids || !w_gate || !w_up || !w_down || !out || !ws) return MOE_ERR_NULL;
+    if (!topk_w && !w_router) return MOE_ERR_NULL;
+    if (!aligned16(x) || !aligned16(topk_ids) || !aligned16(w_gate) || !aligned16(w_up) ||
+        !aligned16(w_down) || !aligned16(out) || !aligned16(ws) ||
+        (w_router && !aligned16(w_router)) || (topk_w && !aligned16(topk_w)) ||
+        (w_out && !aligned16(w_out)))
+        return MOE_ERR_ALIGN;
+    const FwdLayout L = fwd_layout(T, H, E, F, top_k);
+    if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    const int A = T * top_k;
+    int32_t* counts = reinterpret_cast<int32_t*>(at(ws, L.counts));
+    int32_t* offsets = reinterpret_cast<int32_t*>(at(ws, L.offsets));
+    int32_t* perm = reinterpret_cast<int32_t*>(at(ws, L.perm));
+    int32_t* inv = reinterpret_cast<int32_t*>(at(ws, L.inv_perm));
+    float* part = reinterpret_cast<float*>(at(ws, L.route));
+    int32_t* pws = reinterpret_cast<int32_t*>(at(ws, L.permute));
+    int32_t* sched = reinterpret_cast<int32_t*>(at(ws, L.sched));
+    uint16_t* hact = reinterpret_cast<uint16_t*>(at(ws, L.hact));
+    float* y = reinterpret_cast<float*>(at(ws, L.y));
+    hipStream_t s = S(stream);
+    const float* w = topk_w;
+    if (!topk_w) {
+        float* wr = w_out ? w_out : reinterpret_cast<float*>(at(ws, L.w));
+        MOE_TRY(hip_rc(moe::launch_route(T, H, E, top_k, score, renormalize, x, w_router,
+                                         nullptr, nullptr, wr, part, s, topk_ids)));
+        w = wr;
+    }
+    MOE_TRY(hip_rc(moe::launch_permute(A, E, topk_ids, counts, offsets, perm, inv, pws, s)));
+    MOE_TRY(hip_rc(moe::launch_gate_up(T, H, E, F, top_k, x, perm, offsets, w_gate, w_up, hact,
+                                       sched, s)));
+    MOE_TRY(hip_rc(moe::launch_down(T, H, E, F, top_k, hact, perm, offsets, w_down, y, variant,
+                                    sched, s)));
+    MOE_TRY(hip_rc(moe::launch_zero_unplaced(A, H, inv, y, s)));
+    return hip_rc(launch_combine(T, H, top_k, y, w, out, s));
+}
+
 // ---------------------------------------------------------------------------
 // decode-step measurement
 // ---------------------------------------------------------------------------

@@ -39,7 +39,23 @@ __global__ __launch_bounds__(256) void combine_kernel(int T, int H4, int k,
     out[idx] = o;
 }
 
+// Router replay may hand in expert ids outside [0,E); permute leaves those
+// assignments unplaced (inv_perm = -1) and no GEMM writes their y rows.  They
+// contribute nothing: their rows are set to 0 here (one block per row).
+__global__ __launch_bounds__(256) void zero_unplaced_kernel(int H4, const int32_t* __restrict__ inv_perm,
+                                                            float4* __restrict__ y) {
+    const int a = blockIdx.x;
+    if (inv_perm[a] >= 0) return;
+    float4* row = y + (size_t)a * H4;
+    for (int i = threadIdx.x; i < H4; i += 256) row[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
 }  // namespace
+
+hipError_t launch_zero_unplaced(int A, int H, const int32_t* inv_perm, float* y, hipStream_t s) {
+    zero_unplaced_kernel<<<A, 256, 0, s>>>(H / 4, inv_perm, reinterpret_cast<float4*>(y));
+    return hipGetLastError();
+}
 
 hipError_t launch_combine(int T, int H, int k, const float* y, const float* w, uint16_t* out,
                           hipStream_t s) {

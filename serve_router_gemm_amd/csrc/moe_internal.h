@@ -21,9 +21,12 @@ struct RoutePlan {
 };
 RoutePlan route_plan(int T, int H, int E);
 size_t route_ws_bytes(int T, int H, int E);
+// replay != nullptr: router replay -- the experts are read from replay [T,k]
+// (ids is not written) and only the weights w are computed.
 hipError_t launch_route(int T, int H, int E, int k, int score, int renorm,
                         const uint16_t* x, const uint16_t* wr, const float* bias,
-                        int32_t* ids, float* w, float* part_ws, hipStream_t s);
+                        int32_t* ids, float* w, float* part_ws, hipStream_t s,
+                        const int32_t* replay = nullptr);
 
 // permute ------------------------------------------------------------------
 int permute_chunk(int A);
@@ -52,6 +55,8 @@ hipError_t launch_k3(int T, int V, const float* logp_ref, const float* logp_test
                      double* mean, double* greedy_k3, int32_t* greedy, hipStream_t s);
 
 // combine ------------------------------------------------------------------
+// y rows of assignments that permute skipped (inv_perm = -1) are set to 0.
+hipError_t launch_zero_unplaced(int A, int H, const int32_t* inv_perm, float* y, hipStream_t s);
 hipError_t launch_combine(int T, int H, int k, const float* y, const float* w,
                           uint16_t* out, hipStream_t s);
 

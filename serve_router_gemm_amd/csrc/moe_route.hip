@@ -124,10 +124,15 @@ __global__ __launch_bounds__(kRouteThreads) void router_logits_kernel(
 
 constexpr int kSelMaxQ = 8;   // experts per lane: E <= 512
 
-// One wave per token: fold partial logits, keys, top-k, weights.
+// One wave per token: fold partial logits, keys, top-k, weights.  With
+// `replay` set (router replay), the experts of each slot are read from it
+// instead of selected, and only the weights are computed, by the same code:
+// replaying the ids this kernel chose reproduces its weights bit for bit.  A
+// replayed id outside [0,E) gets weight 0 and is left out of the sum.
 __global__ __launch_bounds__(256) void router_select_kernel(
     int T, int E, int k, int nparts, int score, int renorm, const float* __restrict__ part,
-    const float* __restrict__ bias, int32_t* __restrict__ ids, float* __restrict__ wout) {
+    const float* __restrict__ bias, const int32_t* __restrict__ replay,
+    int32_t* __restrict__ ids, float* __restrict__ wout) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;  // whole wave leaves together
@@ -157,6 +162,20 @@ __global__ __launch_bounds__(256) void router_select_kernel(
     int sel[16];
     float lsel[16];
     for (int j = 0; j < k; ++j) {
+        if (replay) {
+            const int e = replay[(size_t)t * k + j];
+            sel[j] = e;
+            float mine = 0.0f;
+            if (e >= 0 && e < E) {
+                const int qs = e >> 6, owner = e & 63;
+#pragma unroll
+                for (int q = 0; q < kSelMaxQ; ++q)
+                    if (q == qs) mine = lg[q];
+                mine = __shfl(mine, owner, 64);
+            }
+            lsel[j] = mine;
+            continue;
+        }
         uint64_t best = rk[0];
 #pragma unroll
         for (int q = 1; q < kSelMaxQ; ++q) best = rk[q] > best ? rk[q] : best;
@@ -196,14 +215,17 @@ __global__ __launch_bounds__(256) void router_select_kernel(
     } else {
         for (int j = 0; j < k; ++j) p[j] = 1.0f / (1.0f + expf(-lsel[j]));
     }
+    if (replay)
+        for (int j = 0; j < k; ++j)
+            if (sel[j] < 0 || sel[j] >= E) p[j] = 0.0f;
     if (renorm) {
         float D = 0.0f;
         for (int j = 0; j < k; ++j) D = D + p[j];
-        for (int j = 0; j < k; ++j) p[j] = p[j] / D;
+        for (int j = 0; j < k; ++j) p[j] = D > 0.0f ? p[j] / D : 0.0f;
     }
     for (int j = 0; j < k; ++j)
         if (lane == j) {
-            ids[(size_t)t * k + j] = sel[j];
+            if (!replay) ids[(size_t)t * k + j] = sel[j];
             wout[(size_t)t * k + j] = p[j];
         }
 }
@@ -255,7 +277,7 @@ hipError_t launch_lm_logits(int T, int H, int V, const uint16_t* h, const uint16
 
 hipError_t launch_route(int T, int H, int E, int k, int score, int renorm, const uint16_t* x,
                         const uint16_t* wr, const float* bias, int32_t* ids, float* w,
-                        float* part_ws, hipStream_t s) {
+                        float* part_ws, hipStream_t s, const int32_t* replay) {
     const RoutePlan p = route_plan(T, H, E);
     hipError_t err;
     if (p.split && p.tt == 1) {
@@ -273,7 +295,7 @@ hipError_t launch_route(int T, int H, int E, int k, int score, int renorm, const
     }
     if (err != hipSuccess) return err;
     router_select_kernel<<<(T + 3) / 4, 256, 0, s>>>(T, E, k, p.nparts, score, renorm, part_ws,
-                                                     bias, ids, w);
+                                                     bias, replay, ids, w);
     return hipGetLastError();
 }
 

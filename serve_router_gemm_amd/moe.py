@@ -43,6 +43,8 @@ SIGNATURES = {
     "moe_combine": (_I, [_I, _I, _I, _P, _P, _P, _P]),
     "moe_forward": (_I, [_I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I,
                          _P, _Z, _P]),
+    "moe_forward_replay": (_I, [_I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P,
+                                _P, _I, _P, _Z, _P]),
     "moe_lm_head_logits": (_I, [_I, _I, _I, _P, _P, _P, _P]),
     "moe_log_softmax": (_I, [_I, _I, _P, _P, _P]),
     "moe_k3": (_I, [_I, _I, _P, _P, _P, _P, _P, _P]),
@@ -275,6 +277,39 @@ def forward(x, w_router, w_gate, w_up, w_down, top_k, score=SCORE_SOFTMAX, renor
     if return_routing:
         return out, topk_ids, topk_w
     return out
+
+
+def forward_replay(x, topk_ids, w_gate, w_up, w_down, topk_w=None, w_router=None,
+                   score=SCORE_SOFTMAX, renormalize=True, variant=INVARIANT, ws=None,
+                   stream=None, return_weights=False):
+    """moe_forward_replay: the layer with recorded experts (router replay).
+
+    topk_w=None recomputes the weights from w_router for the given experts;
+    return_weights=True then also returns them."""
+    T, H = x.shape
+    E, F, _ = w_gate.shape
+    k = topk_ids.shape[1]
+    _dev(x, "x", torch.bfloat16, (T, H))
+    _dev(topk_ids, "topk_ids", torch.int32, (T, k))
+    _dev(w_gate, "w_gate", torch.bfloat16, (E, F, H))
+    _dev(w_up, "w_up", torch.bfloat16, (E, F, H))
+    _dev(w_down, "w_down", torch.bfloat16, (E, H, F))
+    if topk_w is not None:
+        _dev(topk_w, "topk_w", torch.float32, (T, k))
+    if w_router is not None:
+        _dev(w_router, "w_router", torch.bfloat16, (E, H))
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    w_out = None
+    if topk_w is None and return_weights:
+        w_out = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    need = workspace_bytes(OP_FORWARD, T, H, E, F, k, variant)
+    ws = _ws(ws, need, x.device)
+    rc = lib().moe_forward_replay(T, H, E, F, k, score, int(renormalize), _ptr(x),
+                                  _ptr(w_router), _ptr(topk_ids), _ptr(topk_w), _ptr(w_gate),
+                                  _ptr(w_up), _ptr(w_down), _ptr(out), _ptr(w_out), variant,
+                                  _ptr(ws), ws.numel(), _stream(stream))
+    _check("moe_forward_replay", rc)
+    return (out, w_out) if return_weights else out
 
 
 def lm_head_logits(h, proj, z=None, stream=None):
