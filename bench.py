@@ -222,6 +222,25 @@ def main():
                        "out_elements_differing": moved, "out_elements": T * H}
         out.copy_(out_inv)
 
+    # Router replay: the same layer with the recorded routing of the step (ids
+    # and weights) handed back in; must reproduce the routed output bitwise.
+    replay_res = None
+    if args.variant == 0:
+        ws_f = M.workspace(M.OP_FORWARD, T, H, E, F, k)
+        rep = M.forward_replay(x, ids, L["w_gate"], L["w_up"], L["w_down"], topk_w=w,
+                               score=cfg.score, renormalize=cfg.renorm, ws=ws_f)
+        same = bool(torch.equal(rep.view(torch.int16), out.view(torch.int16)))
+        KR = min(K, 10)
+        torch.cuda.synchronize()
+        tr = time.perf_counter()
+        for _ in range(KR):
+            M.forward_replay(x, ids, L["w_gate"], L["w_up"], L["w_down"], topk_w=w,
+                             score=cfg.score, renormalize=cfg.renorm, ws=ws_f)
+        torch.cuda.synchronize()
+        replay_res = {"ms_per_step": round((time.perf_counter() - tr) * 1000.0 / KR, 4),
+                      "out_bit_identical_to_routed": same}
+        del ws_f, rep
+
     # Decode workload: the measurement downstream of the step (vocabulary
     # projection, log-softmax, k3 of this batch against itself), timed on its
     # own; the projection streams V x H bf16 weights.
@@ -322,6 +341,7 @@ def main():
         "combine_hbm_frac": round(comb_gbs / PEAK_HBM_GBS, 4),
         "probe_bits_differing": inv_bits,
         "splitk_variant": variant_res,
+        "router_replay": replay_res,
     }
     if decode_res is not None:
         res["decode_measure"] = decode_res

@@ -175,3 +175,22 @@ def test_decode_measurement_checks(L):
     assert k3(4, 100, FAKE, FAKE, FAKE, MIS, FAKE, None) == ALIGN
     assert k3(4, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None) == SHAPE
     assert k3(0, 100, None, None, None, None, None, None) == OK
+
+
+def test_forward_replay_checks(L):
+    f = L.moe_forward_replay
+    # T, H, E, F, k, score, renorm, x, w_router, ids, w, wg, wu, wd, out, w_out, variant, ws, bytes
+    def call(T=4, H=64, E=8, F=64, k=2, score=0, renorm=1, x=FAKE, wr=FAKE, ids=FAKE, w=None,
+             wg=FAKE, wu=FAKE, wd=FAKE, out=FAKE, w_out=None, variant=0, ws=FAKE, nbytes=1 << 40):
+        return f(T, H, E, F, k, score, renorm, x, wr, ids, w, wg, wu, wd, out, w_out, variant,
+                 ws, nbytes, None)
+    assert call(ids=None) == NULL
+    assert call(wr=None, w=None) == NULL            # weights neither given nor computable
+    assert call(wr=None, w=FAKE, nbytes=0) == WS     # recorded weights: no router needed
+    assert call(w_out=MIS) == ALIGN
+    assert call(H=65) == UNSUP
+    assert call(score=3) == UNSUP
+    assert call(variant=2) == UNSUP
+    assert call(k=9) == SHAPE
+    assert call(nbytes=0) == WS
+    assert call(T=0, x=None, wr=None, ids=None, wg=None, wu=None, wd=None, out=None, ws=None) == OK
