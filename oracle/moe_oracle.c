@@ -655,3 +655,59 @@ int orc_forward_replay(int T, int H, int E, int F, int k, int score, int renorm,
     free(y);
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Large-k top-k (the sparse attention indexer's selection)                  */
+/* ------------------------------------------------------------------------ */
+/*
+ * A sparse attention indexer picks, for every query, the top 2048 keys; a
+ * top-k that is not deterministic changed what the trainer saw from what the
+ * rollout saw, and ties, sort stability, NaN handling and the index dtype
+ * all change the chosen set ("GLM Post-Training Beyond SFT", sections
+ * "DSA 的确定性为什么是 RL 问题", "迁移到 NPU 时" and the sparse/version
+ * contract; the Fireworks bit-level page, section
+ * "为什么比特级一致是一个复杂的问题", on the indexer returning one set in
+ * different orders).  Reading taken: the order of D3 (score descending,
+ * index ascending; -0 == +0; NaN below everything, NaNs by index) over the
+ * first lengths[q] scores of row q (all N when lengths is NULL); slot j holds
+ * the j-th; slots past min(k, lengths[q]) hold -1 (value NaN).  int32 ids.
+ * Plain comparison sort of the row's indices under that total order.
+ */
+static const float* g_topk_row;   /* comparator context (sort is per thread) */
+#ifdef _OPENMP
+#pragma omp threadprivate(g_topk_row)
+#endif
+
+static int topk_cmp(const void* pa, const void* pb)
+{
+    int a = *(const int32_t*)pa, b = *(const int32_t*)pb;
+    if (a == b) return 0;
+    return ranks_before(g_topk_row[a], a, g_topk_row[b], b) ? -1 : 1;
+}
+
+void orc_topk_large(int Q, int N, int k, const float* scores, const int32_t* lengths,
+                    int32_t* idx, float* vals, int nthreads)
+{
+    int nt = set_threads(nthreads);
+    (void)nt;
+#pragma omp parallel num_threads(nt)
+    {
+        int32_t* order = (int32_t*)malloc(sizeof(int32_t) * (size_t)(N > 0 ? N : 1));
+#pragma omp for schedule(dynamic, 1)
+        for (int q = 0; q < Q; ++q) {
+            int n = lengths ? lengths[q] : N;
+            if (n < 0) n = 0;
+            if (n > N) n = N;
+            const float* row = scores + (int64_t)q * N;
+            for (int i = 0; i < n; ++i) order[i] = i;
+            g_topk_row = row;
+            qsort(order, (size_t)n, sizeof(int32_t), topk_cmp);
+            for (int j = 0; j < k; ++j) {
+                int v = j < n ? order[j] : -1;
+                idx[(int64_t)q * k + j] = v;
+                if (vals) vals[(int64_t)q * k + j] = v >= 0 ? row[v] : NAN;
+            }
+        }
+        free(order);
+    }
+}

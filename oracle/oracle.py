@@ -66,6 +66,7 @@ def _declare(L):
     L.orc_forward_replay.argtypes = [i32, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P,
                                      P, i32]
     L.orc_lm_head_logits.argtypes = [i32, i32, i32, P, P, P, i32]
+    L.orc_topk_large.argtypes = [i32, i32, i32, P, P, P, P, i32]
     L.orc_log_softmax.argtypes = [i32, i32, P, P, i32]
     L.orc_k3.argtypes = [i32, i32, P, P, P, P, P]
 
@@ -301,3 +302,19 @@ def forward_replay(x, wr, ids, wg, wu, wd, score, renorm=True, w=None, nthreads=
     if rc != 0:
         raise ValueError(f"orc_forward_replay rc={rc}")
     return out, w_out
+
+
+# ---------------------------------------------------------------------------
+# large-k top-k (sparse attention indexer selection)
+# ---------------------------------------------------------------------------
+
+def topk_large(scores, k, lengths=None, nthreads=0):
+    """Top k of each row of scores [Q,N] (fp32) under the selection order of
+    D3, over the first lengths[q] entries: -> (idx [Q,k] int32, vals [Q,k])."""
+    s = _c(scores, np.float32)
+    Q, N = s.shape
+    ln = None if lengths is None else _c(lengths, np.int32)
+    idx = np.empty((Q, k), dtype=np.int32)
+    vals = np.empty((Q, k), dtype=np.float32)
+    lib().orc_topk_large(Q, N, k, _p(s), _p(ln), _p(idx), _p(vals), nthreads)
+    return idx, vals
