@@ -241,6 +241,26 @@ def main():
                       "out_bit_identical_to_routed": same}
         del ws_f, rep
 
+    # Sparse-indexer top-k at the pages' shape (top 2048 per query over a
+    # 128K-token context; 1024 queries), timed on its own.
+    topk_res = None
+    if cfg.name == "large":
+        Qs, Ns, ks = 1024, 131072, 2048
+        sc = torch.randn((Qs, Ns), generator=torch.Generator().manual_seed(3)).to(dev)
+        M.topk_large(sc, ks, want_vals=False)
+        evk = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        evk[0].record(stream)
+        for _ in range(5):
+            M.topk_large(sc, ks, want_vals=False)
+        evk[1].record(stream)
+        torch.cuda.synchronize()
+        tk_ms = evk[0].elapsed_time(evk[1]) / 5
+        topk_res = {"queries": Qs, "keys": Ns, "k": ks, "ms": round(tk_ms, 4),
+                    "scores_read_once_hbm_frac": round(Qs * Ns * 4.0 / (tk_ms * 1e-3) / 1e9
+                                                       / PEAK_HBM_GBS, 4)}
+        del sc
+
     # Decode workload: the measurement downstream of the step (vocabulary
     # projection, log-softmax, k3 of this batch against itself), timed on its
     # own; the projection streams V x H bf16 weights.
@@ -342,6 +362,7 @@ def main():
         "probe_bits_differing": inv_bits,
         "splitk_variant": variant_res,
         "router_replay": replay_res,
+        "indexer_topk": topk_res,
     }
     if decode_res is not None:
         res["decode_measure"] = decode_res

@@ -218,6 +218,27 @@ int moe_forward_replay(int T, int H, int E, int F, int top_k, int score, int ren
                        const uint16_t* w_down, uint16_t* out, float* w_out, int variant,
                        void* ws, size_t ws_bytes, void* stream);
 
+/* Large-k top-k of a sparse attention indexer: for every query row, the top
+ * k (2048 on the pages) of its scores.  A non-deterministic indexer top-k
+ * made the trainer see other tokens than the rollout, and ties at the
+ * boundary, sort stability, NaN handling and the index dtype all change the
+ * chosen set ("GLM Post-Training Beyond SFT", sections
+ * "DSA 的确定性为什么是 RL 问题" and "迁移到 NPU 时", and its sparse/version
+ * contract).  Order: score descending, then index ascending; -0 == +0; a
+ * NaN ranks below every other score (-inf included), NaNs by index.
+ *   scores [device] [Q,N] fp32;
+ *   lengths [device] [Q] int32 or NULL: row q considers scores[q, 0..len)
+ *     (clamped to [0,N]); NULL = all N (a causal indexer passes the prefix);
+ *   idx [device] out [Q,k] int32: slot j = the j-th selected index, slots
+ *     past min(k, len) = -1;
+ *   vals [device] out [Q,k] fp32 or NULL: the selected scores (NaN in
+ *     the -1 slots).
+ * Limits: 0 <= Q; 1 <= N <= 2^24; 1 <= k <= 4096; Q*N < 2^31.  Each row's
+ * result depends on that row only.  Per-shard lists merged under the same
+ * order give the same list as one call over the whole row. */
+int moe_topk_large(int Q, int N, int k, const float* scores, const int32_t* lengths,
+                   int32_t* idx, float* vals, void* stream);
+
 /* ------------------------------------------------------------------------
  * The measurement downstream of a decode step.  What training and serving
  * finally compare is the log-probability of the next token and a KL estimate

@@ -328,6 +328,18 @@ int moe_forward_replay(int T, int H, int E, int F, int top_k, int score, int ren
     return hip_rc(launch_combine(T, H, top_k, y, w, out, s));
 }
 
+int moe_topk_large(int Q, int N, int k, const float* scores, const int32_t* lengths,
+                   int32_t* idx, float* vals, void* stream) {
+    if (Q < 0 || N < 1 || N > (1 << 24) || k < 1 || k > moe::kMaxTopkLarge) return MOE_ERR_SHAPE;
+    if ((long)Q * N > kMaxElems || (long)Q * k > kMaxElems) return MOE_ERR_SHAPE;
+    if (Q == 0) return MOE_OK;
+    if (!scores || !idx) return MOE_ERR_NULL;
+    if (!aligned16(scores) || !aligned16(idx) || (lengths && !aligned16(lengths)) ||
+        (vals && !aligned16(vals)))
+        return MOE_ERR_ALIGN;
+    return hip_rc(moe::launch_topk_large(Q, N, k, scores, lengths, idx, vals, S(stream)));
+}
+
 // ---------------------------------------------------------------------------
 // decode-step measurement
 // ---------------------------------------------------------------------------

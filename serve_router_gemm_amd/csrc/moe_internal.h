@@ -54,6 +54,11 @@ hipError_t launch_log_softmax(int T, int V, const float* z, float* logp, hipStre
 hipError_t launch_k3(int T, int V, const float* logp_ref, const float* logp_test,
                      double* mean, double* greedy_k3, int32_t* greedy, hipStream_t s);
 
+// large-k top-k (sparse attention indexer) ------------------------------------
+constexpr int kMaxTopkLarge = 4096;
+hipError_t launch_topk_large(int Q, int N, int k, const float* scores, const int32_t* lengths,
+                             int32_t* idx, float* vals, hipStream_t s);
+
 // combine ------------------------------------------------------------------
 // y rows of assignments that permute skipped (inv_perm = -1) are set to 0.
 hipError_t launch_zero_unplaced(int A, int H, const int32_t* inv_perm, float* y, hipStream_t s);

@@ -1,0 +1,160 @@
+// moe_topk.hip -- the large-k top-k of a sparse attention indexer: the top
+// k (2048 on the pages) of every row of scores, exactly and in one order.
+//
+// A non-deterministic indexer top-k made the trainer attend to other tokens
+// than the rollout did; the selected set depends on ties at the boundary,
+// sort stability, NaN handling and the index dtype ("GLM Post-Training Beyond
+// SFT", sections "DSA 的确定性为什么是 RL 问题" and "迁移到 NPU 时", and the
+// sparse/version contract).  The order is the router top-k's: score
+// descending, index ascending, -0 == +0, NaN below everything (NaNs by
+// index).  It is a total order on (score, index), so the result is one
+// well-defined list whatever the thread schedule.
+//
+// One 1024-thread block per row.  With n > k valid scores:
+//   1. radix select on the 32-bit order-preserving code, 8 bits per pass from
+//      the top (LDS histograms, integer counts): the code c* of the k-th
+//      element and kk, how many elements equal to c* are taken;
+//   2. every element above c* is taken (LDS atomic slot; the slots are
+//      sorted next, so their order does not matter), and the kk lowest
+//      indices equal to c*, found by a block-wide scan in index order;
+//   3. a bitonic sort of the k 64-bit ranks (code << 32 | ~index) in LDS,
+//      descending.
+// With n <= k every valid element is taken and sorted; the rest is -1.
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kTkThreads = 1024;
+constexpr int kTkWaves = kTkThreads / kWave;
+
+__global__ __launch_bounds__(kTkThreads) void topk_large_kernel(
+    int N, int k, const float* __restrict__ scores, const int32_t* __restrict__ lengths,
+    int32_t* __restrict__ idx, float* __restrict__ vals) {
+    __shared__ uint64_t rk[kMaxTopkLarge];
+    __shared__ int hist[256];
+    __shared__ int wsum[kTkWaves];
+    __shared__ int s_bin, s_above, s_fill, s_run, s_done;
+
+    const int q = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid >> 6;
+    const float* row = scores + (size_t)q * N;
+    int n = lengths ? lengths[q] : N;
+    n = n < 0 ? 0 : (n > N ? N : n);
+    const int take = min(k, n);
+    int kp = 1;
+    while (kp < take) kp <<= 1;
+
+    for (int i = tid; i < kp; i += kTkThreads) rk[i] = 0;
+    if (tid == 0) s_fill = 0;
+    __syncthreads();
+
+    if (n <= k) {
+        for (int i = tid; i < n; i += kTkThreads) {
+            const int pos = atomicAdd(&s_fill, 1);
+            rk[pos] = sel_rank(row[i], i);
+        }
+    } else {
+        // 1. radix select: prefix/mask describe the code bits fixed so far,
+        //    need = how many of the elements matching them are still wanted
+        uint32_t prefix = 0, mask = 0;
+        int need = k;
+        for (int shift = 24; shift >= 0; shift -= 8) {
+            for (int b = tid; b < 256; b += kTkThreads) hist[b] = 0;
+            __syncthreads();
+            for (int i = tid; i < n; i += kTkThreads) {
+                const uint32_t c = key_code(row[i]);
+                if ((c & mask) == prefix) atomicAdd(&hist[(c >> shift) & 255u], 1);
+            }
+            __syncthreads();
+            if (tid == 0) {
+                int above = 0, b = 255;
+                for (; b > 0; --b) {
+                    if (above + hist[b] >= need) break;
+                    above += hist[b];
+                }
+                s_bin = b;
+                s_above = above;
+            }
+            __syncthreads();
+            prefix |= (uint32_t)s_bin << shift;
+            mask |= 255u << shift;
+            need -= s_above;
+            __syncthreads();
+        }
+        const uint32_t cstar = prefix;   // the k-th element's code; take `need` of them
+        // 2. elements above c* (any slot order), then the `need` lowest
+        //    indices equal to c*, in index order, after them
+        if (tid == 0) s_run = 0;
+        __syncthreads();
+        const int base_eq = k - need;
+        for (int i0 = 0; i0 < n; i0 += kTkThreads) {
+            const int i = i0 + tid;
+            uint32_t c = 0;
+            if (i < n) c = key_code(row[i]);
+            if (i < n && c > cstar) {
+                const int pos = atomicAdd(&s_fill, 1);
+                rk[pos] = ((uint64_t)c << 32) | (uint32_t)(~(uint32_t)i);
+            }
+            const bool eq = (i < n) && (c == cstar);
+            const uint64_t bal = __ballot(eq);
+            const int before_lane = __popcll(bal & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
+            if (lane == 0) wsum[wave] = __popcll(bal);
+            __syncthreads();
+            int before_wave = 0;
+            for (int w = 0; w < wave; ++w) before_wave += wsum[w];
+            const int run = s_run;
+            const int r = run + before_wave + before_lane;
+            if (eq && r < need) rk[base_eq + r] = ((uint64_t)c << 32) | (uint32_t)(~(uint32_t)i);
+            __syncthreads();
+            // One thread decides whether both parts are complete; s_fill is
+            // final for this pass of the loop here (its atomics came before
+            // the barrier above), and the decision is read by all after the
+            // next barrier, before anyone can change it again.
+            if (tid == 0) {
+                int tot = 0;
+                for (int w = 0; w < kTkWaves; ++w) tot += wsum[w];
+                s_run = run + tot;
+                s_done = (s_run >= need && s_fill >= base_eq) ? 1 : 0;
+            }
+            __syncthreads();
+            if (s_done) break;
+        }
+    }
+    __syncthreads();
+
+    // 3. bitonic sort of rk[0..kp) descending (zeros, the padding, sink)
+    for (int size = 2; size <= kp; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int t = tid; t < kp / 2; t += kTkThreads) {
+                const int i = 2 * stride * (t / stride) + (t % stride);
+                const int j = i + stride;
+                const uint64_t a = rk[i], b = rk[j];
+                const bool desc = (i & size) == 0;
+                if (desc ? (a < b) : (a > b)) { rk[i] = b; rk[j] = a; }
+            }
+            __syncthreads();
+        }
+    }
+
+    for (int j = tid; j < k; j += kTkThreads) {
+        int v = -1;
+        if (j < take) v = (int)(~(uint32_t)(rk[j] & 0xFFFFFFFFull));
+        idx[(size_t)q * k + j] = v;
+        if (vals) vals[(size_t)q * k + j] = v >= 0 ? row[v] : __int_as_float(0x7FC00000);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_topk_large(int Q, int N, int k, const float* scores, const int32_t* lengths,
+                             int32_t* idx, float* vals, hipStream_t s) {
+    topk_large_kernel<<<Q, kTkThreads, 0, s>>>(N, k, scores, lengths, idx, vals);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -45,6 +45,7 @@ SIGNATURES = {
                          _P, _Z, _P]),
     "moe_forward_replay": (_I, [_I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P,
                                 _P, _I, _P, _Z, _P]),
+    "moe_topk_large": (_I, [_I, _I, _I, _P, _P, _P, _P, _P]),
     "moe_lm_head_logits": (_I, [_I, _I, _I, _P, _P, _P, _P]),
     "moe_log_softmax": (_I, [_I, _I, _P, _P, _P]),
     "moe_k3": (_I, [_I, _I, _P, _P, _P, _P, _P, _P]),
@@ -351,4 +352,18 @@ def k3(logp_ref, logp_test, stream=None):
                       _stream(stream))
     _check("moe_k3", rc)
     return mean, gk3, g
+
+
+def topk_large(scores, k, lengths=None, want_vals=True, stream=None):
+    """moe_topk_large: -> (idx [Q,k] int32, vals [Q,k] fp32 or None)."""
+    Q, N = scores.shape
+    _dev(scores, "scores", torch.float32, (Q, N))
+    if lengths is not None:
+        _dev(lengths, "lengths", torch.int32, (Q,))
+    idx = torch.empty((Q, k), dtype=torch.int32, device=scores.device)
+    vals = torch.empty((Q, k), dtype=torch.float32, device=scores.device) if want_vals else None
+    rc = lib().moe_topk_large(Q, N, k, _ptr(scores), _ptr(lengths), _ptr(idx), _ptr(vals),
+                              _stream(stream))
+    _check("moe_topk_large", rc)
+    return idx, vals
 

@@ -194,3 +194,18 @@ def test_forward_replay_checks(L):
     assert call(k=9) == SHAPE
     assert call(nbytes=0) == WS
     assert call(T=0, x=None, wr=None, ids=None, wg=None, wu=None, wd=None, out=None, ws=None) == OK
+
+
+def test_topk_large_checks(L):
+    t = L.moe_topk_large
+    assert t(-1, 100, 10, FAKE, None, FAKE, None, None) == SHAPE
+    assert t(4, 0, 10, FAKE, None, FAKE, None, None) == SHAPE
+    assert t(4, 100, 0, FAKE, None, FAKE, None, None) == SHAPE
+    assert t(4, 100, 4097, FAKE, None, FAKE, None, None) == SHAPE
+    assert t(4, (1 << 24) + 1, 10, FAKE, None, FAKE, None, None) == SHAPE
+    assert t(1 << 8, 1 << 24, 10, FAKE, None, FAKE, None, None) == SHAPE     # Q*N >= 2^31
+    assert t(4, 100, 10, None, None, FAKE, None, None) == NULL
+    assert t(4, 100, 10, FAKE, None, None, None, None) == NULL
+    assert t(4, 100, 10, FAKE, MIS, FAKE, None, None) == ALIGN
+    assert t(4, 100, 10, FAKE, None, FAKE, MIS, None) == ALIGN
+    assert t(0, 100, 10, None, None, None, None, None) == OK
