@@ -711,3 +711,208 @@ void orc_topk_large(int Q, int N, int k, const float* scores, const int32_t* len
         free(order);
     }
 }
+
+/* ------------------------------------------------------------------------ */
+/* FP8 rollout path: e4m3 experts with block scales                          */
+/* ------------------------------------------------------------------------ */
+/*
+ * The pages' large-MoE recipe trains in BF16 and samples rollouts with FP8
+ * weights converted from the BF16 ones by the rollout's quantisation config,
+ * and asks that the gap between the two policies' log-probabilities keep
+ * being measured ("GLM Post-Training Beyond SFT", section on quantisation,
+ * "量化：三件事不要混为一谈").  The pages give no format or block shape.
+ * Reading taken:
+ *   e4m3      OCP E4M3FN: bias 7, 3 mantissa bits, subnormals, max 448, no
+ *             infinities; fp32 -> e4m3 rounds to nearest, ties to even; a
+ *             NaN stays NaN.  Values beyond 448 never occur (the scales keep
+ *             every value within range); they saturate to +-448 here.
+ *   scales    powers of two, per block: e = the smallest integer with
+ *             amax <= 448 * 2^e (amax = max |v| over the block; e = 0 for an
+ *             all-zero block), q = e4m3(v * 2^-e), v ~ q * 2^e.  Weight blocks
+ *             are 128 output rows x 128 K; activation blocks 1 row x 128 K.
+ *   GEMM      out = sum over K blocks kb ascending, in fp32, of
+ *             fp32(exact sum_{k in kb} qa*qw) * 2^(ea + ew); the products of
+ *             two e4m3 codes and their 128-term sum are exact in fp64.
+ *   expert    g, u by that GEMM (fp32); act = bf16(fp32(silu(g)*u)) with
+ *             silu in fp64; act is quantised by rows (1 x 128 blocks) for
+ *             the down GEMM; y = that GEMM, fp32.  Routing and combine are
+ *             those of D1..D7 (the router stays bf16).
+ */
+
+#define ORC_FP8_MAX 448.0f
+#define ORC_FP8_BLOCK 128
+
+/* e4m3 code -> value */
+float orc_e4m3_to_f32(uint8_t c)
+{
+    int s = c >> 7, ex = (c >> 3) & 15, m = c & 7;
+    float v;
+    if (ex == 15 && m == 7) return s ? -NAN : NAN;
+    if (ex == 0)
+        v = ldexpf((float)m, -9);                 /* subnormal: m/8 * 2^-6 */
+    else
+        v = ldexpf(1.0f + (float)m / 8.0f, ex - 7);
+    return s ? -v : v;
+}
+
+/* value -> e4m3 code: nearest, ties to even, saturating at +-448 */
+uint8_t orc_f32_to_e4m3(float v)
+{
+    if (isnan(v)) return 0x7F;
+    uint8_t s = signbit(v) ? 0x80 : 0;
+    double a = fabs((double)v);
+    if (a >= 448.0) return s | 0x7E;
+    /* the grid spacing at a: 2^(max(exponent, -6) - 3) */
+    int e;
+    if (a < ldexp(1.0, -6)) {
+        e = -6;
+    } else {
+        frexp(a, &e);
+        e -= 1;                                     /* a in [2^e, 2^(e+1)) */
+    }
+    double q = ldexp(1.0, e - 3);
+    double n = floor(a / q);
+    double r = a / q - n;                           /* exact: q is a power of two */
+    if (r > 0.5 || (r == 0.5 && fmod(n, 2.0) == 1.0)) n += 1.0;
+    double val = n * q;                             /* the rounded magnitude */
+    if (val >= 448.0) return s | 0x7E;
+    if (val == 0.0) return s;
+    int ve;
+    frexp(val, &ve);
+    ve -= 1;
+    if (ve < -6) {                                  /* subnormal code */
+        return s | (uint8_t)(int)(val / ldexp(1.0, -9));
+    }
+    int m = (int)((val / ldexp(1.0, ve) - 1.0) * 8.0);
+    return s | (uint8_t)(((ve + 7) << 3) | m);
+}
+
+/* smallest integer e with amax <= 448 * 2^e (0 for amax == 0) */
+int orc_fp8_block_exp(float amax)
+{
+    if (!(amax > 0.0f)) return 0;
+    int e = (int)floor(log2((double)amax / 448.0));
+    while ((double)amax > 448.0 * ldexp(1.0, e)) ++e;
+    while ((double)amax <= 448.0 * ldexp(1.0, e - 1)) --e;
+    return e;
+}
+
+/* Quantise bf16 rows [R,K] in blocks of block_rows x 128: q [R,K] codes,
+ * exps [R/block_rows, K/128] int8. */
+void orc_quantize_fp8(int R, int K, int block_rows, const uint16_t* src, uint8_t* q,
+                      int8_t* exps)
+{
+    int nkb = K / ORC_FP8_BLOCK;
+    for (int rb = 0; rb < R / block_rows; ++rb)
+        for (int kb = 0; kb < nkb; ++kb) {
+            float amax = 0.0f;
+            for (int r = rb * block_rows; r < (rb + 1) * block_rows; ++r)
+                for (int k = kb * ORC_FP8_BLOCK; k < (kb + 1) * ORC_FP8_BLOCK; ++k) {
+                    float a = fabsf(orc_bf16_to_f32(src[(int64_t)r * K + k]));
+                    if (a > amax) amax = a;
+                }
+            int e = orc_fp8_block_exp(amax);
+            exps[(int64_t)rb * nkb + kb] = (int8_t)e;
+            for (int r = rb * block_rows; r < (rb + 1) * block_rows; ++r)
+                for (int k = kb * ORC_FP8_BLOCK; k < (kb + 1) * ORC_FP8_BLOCK; ++k)
+                    q[(int64_t)r * K + k] =
+                        orc_f32_to_e4m3(ldexpf(orc_bf16_to_f32(src[(int64_t)r * K + k]), -e));
+        }
+}
+
+/* One output of the block-scaled GEMM: a row of codes (with its per-block
+ * exponents) against a weight row (with its block row's exponents). */
+static float fp8_dot(const uint8_t* aq, const int8_t* ae, const uint8_t* wq, const int8_t* we,
+                     int K)
+{
+    float acc = 0.0f;
+    for (int kb = 0; kb < K / ORC_FP8_BLOCK; ++kb) {
+        double s = 0.0;
+        for (int k = kb * ORC_FP8_BLOCK; k < (kb + 1) * ORC_FP8_BLOCK; ++k)
+            s += (double)orc_e4m3_to_f32(aq[k]) * (double)orc_e4m3_to_f32(wq[k]);
+        acc = acc + ldexpf((float)s, ae[kb] + we[kb]);
+    }
+    return acc;
+}
+
+/* FP8 expert FFN of n (token, expert) pairs.  xq [T,H] codes with xe
+ * [T,H/128]; wgq, wuq [E,F,H] codes with wge, wue [E,F/128,H/128]; wdq
+ * [E,H,F] codes with wde [E,H/128,F/128].  y [n,H] fp32; act [n,F] bf16 (or
+ * NULL). */
+int orc_expert_ffn_fp8(int n, const int32_t* tokens, const int32_t* experts, int H, int F,
+                       const uint8_t* xq, const int8_t* xe, const uint8_t* wgq,
+                       const int8_t* wge, const uint8_t* wuq, const int8_t* wue,
+                       const uint8_t* wdq, const int8_t* wde, float* y, uint16_t* act_o,
+                       int nthreads)
+{
+    if (H % ORC_FP8_BLOCK || F % ORC_FP8_BLOCK) return -4;
+    int nt = set_threads(nthreads);
+    (void)nt;
+    int nhb = H / ORC_FP8_BLOCK, nfb = F / ORC_FP8_BLOCK;
+#pragma omp parallel num_threads(nt)
+    {
+        uint16_t* act = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)F);
+        uint8_t* aq = (uint8_t*)malloc((size_t)F);
+        int8_t* ae = (int8_t*)malloc((size_t)nfb);
+#pragma omp for schedule(dynamic, 1)
+        for (int i = 0; i < n; ++i) {
+            int t = tokens[i], e = experts[i];
+            const uint8_t* xr = xq + (int64_t)t * H;
+            const int8_t* xer = xe + (int64_t)t * nhb;
+            for (int f = 0; f < F; ++f) {
+                int64_t row = (int64_t)e * F + f;
+                const int8_t* geb = wge + ((int64_t)e * nfb + f / ORC_FP8_BLOCK) * nhb;
+                const int8_t* ueb = wue + ((int64_t)e * nfb + f / ORC_FP8_BLOCK) * nhb;
+                float g = fp8_dot(xr, xer, wgq + row * H, geb, H);
+                float u = fp8_dot(xr, xer, wuq + row * H, ueb, H);
+                double gd = (double)g;
+                act[f] = orc_f32_to_bf16((float)(gd / (1.0 + exp(-gd)) * (double)u));
+            }
+            if (act_o) memcpy(act_o + (int64_t)i * F, act, sizeof(uint16_t) * (size_t)F);
+            orc_quantize_fp8(1, F, 1, act, aq, ae);
+            for (int h = 0; h < H; ++h) {
+                int64_t row = (int64_t)e * H + h;
+                const int8_t* deb = wde + ((int64_t)e * nhb + h / ORC_FP8_BLOCK) * nfb;
+                y[(int64_t)i * H + h] = fp8_dot(aq, ae, wdq + row * F, deb, F);
+            }
+        }
+        free(act); free(aq); free(ae);
+    }
+    return 0;
+}
+
+/* The FP8 layer for chosen tokens (per token, no permutation): routing of
+ * D1..D4 on the bf16 router, experts by orc_expert_ffn_fp8, combine D7.
+ * x [T,H] bf16 (routing) with xq/xe its quantised rows (experts). */
+int orc_forward_tokens_fp8(int n, const int32_t* tokens, int H, int E, int F, int k,
+                           int score, int renorm, const uint16_t* x, const uint16_t* wr,
+                           const float* bias, const uint8_t* xq, const int8_t* xe,
+                           const uint8_t* wgq, const int8_t* wge, const uint8_t* wuq,
+                           const int8_t* wue, const uint8_t* wdq, const int8_t* wde,
+                           uint16_t* out, int32_t* ids_o, float* w_o, int nthreads)
+{
+    if (k < 1 || k > E || k > 16) return -2;
+    int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)n * k + 4);
+    float* w = (float*)malloc(sizeof(float) * (size_t)n * k + 4);
+    int32_t* tok = (int32_t*)malloc(sizeof(int32_t) * (size_t)n * k + 4);
+    float* y = (float*)malloc(sizeof(float) * ((size_t)n * k * H + 1));
+    float* keys = (float*)malloc(sizeof(float) * (size_t)E * 2);
+    unsigned char* taken = (unsigned char*)malloc((size_t)E);
+    for (int i = 0; i < n; ++i) {
+        route_one(x + (int64_t)tokens[i] * H, wr, bias, H, E, k, score, renorm,
+                  ids + (int64_t)i * k, w + (int64_t)i * k, NULL, keys, keys + E, taken);
+        for (int j = 0; j < k; ++j) tok[i * k + j] = tokens[i];
+    }
+    int rc = orc_expert_ffn_fp8(n * k, tok, ids, H, F, xq, xe, wgq, wge, wuq, wue, wdq, wde, y,
+                                NULL, nthreads);
+    if (rc == 0) orc_combine(n, H, k, y, w, out);
+    if (ids_o) memcpy(ids_o, ids, sizeof(int32_t) * (size_t)n * k);
+    if (w_o) memcpy(w_o, w, sizeof(float) * (size_t)n * k);
+    free(ids); free(w); free(tok); free(y); free(keys); free(taken);
+    return rc;
+}
+
+void orc_f32_to_e4m3_array(const float* in, uint8_t* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_f32_to_e4m3(in[i]);
+}

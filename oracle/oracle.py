@@ -67,6 +67,17 @@ def _declare(L):
                                      P, i32]
     L.orc_lm_head_logits.argtypes = [i32, i32, i32, P, P, P, i32]
     L.orc_topk_large.argtypes = [i32, i32, i32, P, P, P, P, i32]
+    L.orc_e4m3_to_f32.restype = ctypes.c_float
+    L.orc_e4m3_to_f32.argtypes = [ctypes.c_uint8]
+    L.orc_f32_to_e4m3_array.argtypes = [P, P, i64]
+    L.orc_fp8_block_exp.restype = i32
+    L.orc_fp8_block_exp.argtypes = [ctypes.c_float]
+    L.orc_quantize_fp8.argtypes = [i32, i32, i32, P, P, P]
+    L.orc_expert_ffn_fp8.restype = i32
+    L.orc_expert_ffn_fp8.argtypes = [i32, P, P, i32, i32, P, P, P, P, P, P, P, P, P, P, i32]
+    L.orc_forward_tokens_fp8.restype = i32
+    L.orc_forward_tokens_fp8.argtypes = [i32, P, i32, i32, i32, i32, i32, i32, P, P, P, P, P,
+                                         P, P, P, P, P, P, P, P, P, i32]
     L.orc_log_softmax.argtypes = [i32, i32, P, P, i32]
     L.orc_k3.argtypes = [i32, i32, P, P, P, P, P]
 
@@ -318,3 +329,80 @@ def topk_large(scores, k, lengths=None, nthreads=0):
     vals = np.empty((Q, k), dtype=np.float32)
     lib().orc_topk_large(Q, N, k, _p(s), _p(ln), _p(idx), _p(vals), nthreads)
     return idx, vals
+
+
+# ---------------------------------------------------------------------------
+# FP8 rollout path (e4m3 experts, power-of-two block scales)
+# ---------------------------------------------------------------------------
+FP8_BLOCK = 128
+
+
+def e4m3_to_f32(codes) -> np.ndarray:
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    table = np.array([lib().orc_e4m3_to_f32(i) for i in range(256)], dtype=np.float32)
+    return table[c]
+
+
+def f32_to_e4m3(v) -> np.ndarray:
+    v = _c(v, np.float32)
+    out = np.empty(v.shape, dtype=np.uint8)
+    lib().orc_f32_to_e4m3_array(_p(v), _p(out), v.size)
+    return out
+
+
+def fp8_block_exp(amax: float) -> int:
+    return int(lib().orc_fp8_block_exp(float(amax)))
+
+
+def quantize_fp8(src, block_rows):
+    """bf16 bits [..., R, K] -> (codes uint8 [..., R, K], exps int8 [..., R/block_rows, K/128]),
+    each leading index quantised on its own."""
+    s = _u16(src)
+    *lead, R, K = s.shape
+    s2 = s.reshape(-1, R, K)
+    q = np.empty(s2.shape, dtype=np.uint8)
+    e = np.empty((s2.shape[0], R // block_rows, K // FP8_BLOCK), dtype=np.int8)
+    for i in range(s2.shape[0]):
+        lib().orc_quantize_fp8(R, K, block_rows, _p(s2[i]), _p(q[i]), _p(e[i]))
+    return q.reshape(*lead, R, K), e.reshape(*lead, R // block_rows, K // FP8_BLOCK)
+
+
+def expert_ffn_fp8(tokens, experts, xq, xe, wgq, wge, wuq, wue, wdq, wde, nthreads=0,
+                   want_act=False):
+    tokens = _c(tokens, np.int32).reshape(-1)
+    experts = _c(experts, np.int32).reshape(-1)
+    n = tokens.size
+    H = xq.shape[1]
+    F = wgq.shape[1]
+    args = [_c(a, np.uint8 if a.dtype == np.uint8 else np.int8)
+            for a in (xq, xe, wgq, wge, wuq, wue, wdq, wde)]
+    y = np.empty((n, H), dtype=np.float32)
+    act = np.empty((n, F), dtype=np.uint16) if want_act else None
+    rc = lib().orc_expert_ffn_fp8(n, _p(tokens), _p(experts), H, F, *[_p(a) for a in args],
+                                  _p(y), _p(act), nthreads)
+    if rc != 0:
+        raise ValueError(f"orc_expert_ffn_fp8 rc={rc}")
+    return (y, act) if want_act else y
+
+
+def forward_tokens_fp8(tokens, x, wr, xq, xe, wq, k, score, renorm=True, bias=None,
+                       nthreads=0):
+    """The FP8 layer for chosen tokens. wq = dict of quantised expert weights
+    (wgq, wge, wuq, wue, wdq, wde).  -> (out bf16 bits [n,H], ids, w)."""
+    x, wr = _u16(x), _u16(wr)
+    tokens = _c(tokens, np.int32).reshape(-1)
+    n = tokens.size
+    T, H = x.shape
+    E, F = wq["wgq"].shape[0], wq["wgq"].shape[1]
+    b = None if bias is None else _c(bias, np.float32)
+    out = np.empty((n, H), dtype=np.uint16)
+    ids = np.empty((n, k), dtype=np.int32)
+    w = np.empty((n, k), dtype=np.float32)
+    rc = lib().orc_forward_tokens_fp8(n, _p(tokens), H, E, F, k, score, int(renorm), _p(x),
+                                      _p(wr), _p(b), _p(_c(xq, np.uint8)), _p(_c(xe, np.int8)),
+                                      *[_p(_c(wq[n_], np.uint8 if n_.endswith("q") else np.int8))
+                                        for n_ in ("wgq", "wge", "wuq", "wue", "wdq", "wde")],
+                                      _p(out), _p(ids), _p(w), nthreads)
+    if rc != 0:
+        raise ValueError(f"orc_forward_tokens_fp8 rc={rc}")
+    return out, ids, w
