@@ -728,7 +728,8 @@ void orc_topk_large(int Q, int N, int k, const float* scores, const int32_t* len
  *             every value within range); they saturate to +-448 here.
  *   scales    powers of two, per block: e = the smallest integer with
  *             amax <= 448 * 2^e (amax = max |v| over the block; e = 0 for an
- *             all-zero block), q = e4m3(v * 2^-e), v ~ q * 2^e.  Weight blocks
+ *             all-zero block; clamped to [-127, 127], the range of a biased
+ *             scale byte), q = e4m3(v * 2^-e), v ~ q * 2^e.  Weight blocks
  *             are 128 output rows x 128 K; activation blocks 1 row x 128 K.
  *   GEMM      out = sum over K blocks kb ascending, in fp32, of
  *             fp32(exact sum_{k in kb} qa*qw) * 2^(ea + ew); the products of
@@ -787,13 +788,19 @@ uint8_t orc_f32_to_e4m3(float v)
     return s | (uint8_t)(((ve + 7) << 3) | m);
 }
 
-/* smallest integer e with amax <= 448 * 2^e (0 for amax == 0) */
+/* smallest integer e with amax <= 448 * 2^e (0 for amax == 0), clamped to
+ * [-127, 127]: the exponent is stored in a signed byte and carried as a
+ * biased scale byte (127 + e), whose range ends there.  A block whose amax is
+ * below 448 * 2^-127 takes e = -127 (its codes are then not full-range); an
+ * infinite amax takes 127. */
 int orc_fp8_block_exp(float amax)
 {
     if (!(amax > 0.0f)) return 0;
+    if (isinf(amax)) return 127;
     int e = (int)floor(log2((double)amax / 448.0));
     while ((double)amax > 448.0 * ldexp(1.0, e)) ++e;
     while ((double)amax <= 448.0 * ldexp(1.0, e - 1)) --e;
+    if (e < -127) e = -127;
     return e;
 }
 
@@ -833,6 +840,28 @@ static float fp8_dot(const uint8_t* aq, const int8_t* ae, const uint8_t* wq, con
         acc = acc + ldexpf((float)s, ae[kb] + we[kb]);
     }
     return acc;
+}
+
+/* The block-scaled GEMM alone: row i of codes aq [n,K] (exponents ae
+ * [n,K/128]) against the N weight rows of expert experts[i], wq [E,N,K] codes
+ * with we [E,N/128,K/128]: y [n,N] fp32. */
+int orc_fp8_gemm(int n, int K, int N, const uint8_t* aq, const int8_t* ae,
+                 const int32_t* experts, const uint8_t* wq, const int8_t* we, float* y,
+                 int nthreads)
+{
+    if (K % ORC_FP8_BLOCK || N % ORC_FP8_BLOCK) return -4;
+    int nt = set_threads(nthreads);
+    (void)nt;
+    int nkb = K / ORC_FP8_BLOCK, nnb = N / ORC_FP8_BLOCK;
+#pragma omp parallel for num_threads(nt) schedule(dynamic, 1)
+    for (int i = 0; i < n; ++i) {
+        int e = experts[i];
+        for (int o = 0; o < N; ++o)
+            y[(int64_t)i * N + o] =
+                fp8_dot(aq + (int64_t)i * K, ae + (int64_t)i * nkb, wq + ((int64_t)e * N + o) * K,
+                        we + ((int64_t)e * nnb + o / ORC_FP8_BLOCK) * nkb, K);
+    }
+    return 0;
 }
 
 /* FP8 expert FFN of n (token, expert) pairs.  xq [T,H] codes with xe

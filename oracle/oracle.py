@@ -75,6 +75,8 @@ def _declare(L):
     L.orc_quantize_fp8.argtypes = [i32, i32, i32, P, P, P]
     L.orc_expert_ffn_fp8.restype = i32
     L.orc_expert_ffn_fp8.argtypes = [i32, P, P, i32, i32, P, P, P, P, P, P, P, P, P, P, i32]
+    L.orc_fp8_gemm.restype = i32
+    L.orc_fp8_gemm.argtypes = [i32, i32, i32, P, P, P, P, P, P, i32]
     L.orc_forward_tokens_fp8.restype = i32
     L.orc_forward_tokens_fp8.argtypes = [i32, P, i32, i32, i32, i32, i32, i32, P, P, P, P, P,
                                          P, P, P, P, P, P, P, P, P, i32]
@@ -365,6 +367,21 @@ def quantize_fp8(src, block_rows):
     for i in range(s2.shape[0]):
         lib().orc_quantize_fp8(R, K, block_rows, _p(s2[i]), _p(q[i]), _p(e[i]))
     return q.reshape(*lead, R, K), e.reshape(*lead, R // block_rows, K // FP8_BLOCK)
+
+
+def fp8_gemm(aq, ae, experts, wq, we, nthreads=0) -> np.ndarray:
+    """Block-scaled GEMM: row i of codes aq [n,K] (exps ae [n,K/128]) against
+    the weight rows of expert experts[i] (wq [E,N,K], we [E,N/128,K/128])."""
+    aq, ae = _c(aq, np.uint8), _c(ae, np.int8)
+    wq, we = _c(wq, np.uint8), _c(we, np.int8)
+    experts = _c(experts, np.int32).reshape(-1)
+    n, K = aq.shape
+    N = wq.shape[1]
+    y = np.empty((n, N), dtype=np.float32)
+    rc = lib().orc_fp8_gemm(n, K, N, _p(aq), _p(ae), _p(experts), _p(wq), _p(we), _p(y), nthreads)
+    if rc != 0:
+        raise ValueError(f"orc_fp8_gemm rc={rc}")
+    return y
 
 
 def expert_ffn_fp8(tokens, experts, xq, xe, wgq, wge, wuq, wue, wdq, wde, nthreads=0,

@@ -190,3 +190,59 @@ def test_fp8_layer_close_to_bf16_layer():
     b = O.bf16_to_f32(out16).astype(np.float64)
     rel = np.linalg.norm(a - b) / np.linalg.norm(b)
     assert 1e-4 < rel < 0.1, rel
+
+
+def test_fp8_block_exponent_clamp():
+    """The exponent travels as a signed byte and a biased scale byte: tiny
+    blocks take -127 (and still quantise to the scaled e4m3 codes), an
+    infinite amax takes 127."""
+    tiny = np.float32(448.0 * 2.0 ** -130)
+    assert O.fp8_block_exp(tiny) == -127
+    assert O.fp8_block_exp(np.float32(448.0 * 2.0 ** -127)) == -127
+    assert O.fp8_block_exp(np.float32(448.0 * 2.0 ** -126)) == -126
+    assert O.fp8_block_exp(np.float32(np.inf)) == 127
+    assert O.fp8_block_exp(np.float32(3.0e38)) == 120           # largest finite bf16 range
+    v = torch.full((1, 128), 2.0 ** -128, dtype=torch.bfloat16)
+    v[0, 3] = -(2.0 ** -126)
+    q, e = O.quantize_fp8(bits(v), 1)
+    assert e[0, 0] == -127
+    lib = torch.from_numpy(np.ldexp(v.float().numpy(), 127).astype(np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(q, lib)
+    assert O.e4m3_to_f32(q[0, :1])[0] == 0.5 and O.e4m3_to_f32(q[0, 3:4])[0] == -2.0
+
+
+def test_fp8_gemm_alone_against_library_matmul():
+    """orc_fp8_gemm vs an fp64 library matmul of dequantised codes, block by
+    block (each block sum exact in fp64), added in fp32 in ascending block
+    order: equal bit for bit."""
+    rng = np.random.default_rng(11)
+    n, K, N, E = 7, 384, 256, 3
+    a = (rng.standard_normal((n, K)) * rng.choice([1e-3, 1.0, 30.0], (n, 1))).astype(np.float32)
+    w = (rng.standard_normal((E, N, K)) * 0.02).astype(np.float32)
+    aq, ae = O.quantize_fp8(O.f32_to_bf16(a), 1)
+    wq, we = O.quantize_fp8(O.f32_to_bf16(w), 128)
+    experts = rng.integers(0, E, n)
+    y = O.fp8_gemm(aq, ae, experts, wq, we)
+    a_deq = _deq(aq, ae, 1)
+    for i, e in enumerate(experts):
+        w_deq = _deq(wq[e], we[e], 128)                          # [N, K]
+        acc = np.zeros(N, np.float32)
+        for b in range(K // 128):
+            blk = a_deq[i, b * 128:(b + 1) * 128] @ w_deq[:, b * 128:(b + 1) * 128].T
+            acc = (acc + blk.astype(np.float32)).astype(np.float32)
+        assert np.array_equal(y[i], acc)
+
+
+def test_fp8_gemm_alone_exact_on_small_integers():
+    rng = np.random.default_rng(12)
+    n, K, N = 5, 256, 128
+    ai = rng.integers(-6, 7, (n, K)).astype(np.float32)
+    wi = rng.integers(-6, 7, (1, N, K)).astype(np.float32)
+    y = O.fp8_gemm(O.f32_to_e4m3(ai), np.zeros((n, 2), np.int8), np.zeros(n),
+                   O.f32_to_e4m3(wi), np.zeros((1, 1, 2), np.int8))
+    assert np.array_equal(y.astype(np.float64), ai.astype(np.float64) @ wi[0].T.astype(np.float64))
+    # exponents scale exactly: 2^(ea + ew)
+    y2 = O.fp8_gemm(O.f32_to_e4m3(ai), np.full((n, 2), 3, np.int8), np.zeros(n),
+                    O.f32_to_e4m3(wi), np.full((1, 1, 2), -5, np.int8))
+    assert np.array_equal(y2, y * np.float32(2.0 ** -2))
