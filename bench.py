@@ -35,6 +35,7 @@ METRIC = "MoE-layer tokens/s + MFMA util; bitwise-identical output across batch 
 # valid only for the kernel source they were taken on.
 TRAFFIC = {"kernel_sha256_prefix": "98a8c257a206144a", "workload": "large", "bytes": 23.75e9}
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0
 
 
@@ -261,6 +262,92 @@ def main():
                                                        / PEAK_HBM_GBS, 4)}
         del sc
 
+    # FP8 rollout path: the same step with e4m3 experts (weights quantised
+    # once, at load time, in 128 x 128 blocks; x and act by rows), staged as
+    # the entry points moe_forward_fp8 chains and checked bitwise against it;
+    # its output against the bf16 layer's, and probe invariance.
+    fp8_res, out8 = None, None
+    if args.variant == 0 and cfg.name in ("large", "dec"):
+        tq = time.perf_counter()
+        wq8 = M.quantize_weights_fp8(L["w_gate"], L["w_up"], L["w_down"])
+        torch.cuda.synchronize()
+        wq_s = time.perf_counter() - tq
+        xq = torch.empty((T, H), dtype=torch.uint8, device=dev)
+        xe = torch.empty((T, H // 128), dtype=torch.int8, device=dev)
+        aq = torch.empty((A, F), dtype=torch.uint8, device=dev)
+        ae = torch.empty((A, F // 128), dtype=torch.int8, device=dev)
+        out8 = torch.empty_like(out)
+        ws_g8 = M.workspace(M.OP_GATE_UP_FP8, T, H, E, F, k)
+        ws_d8 = M.workspace(M.OP_DOWN_FP8, T, H, E, F, k)
+
+        def step8(ev=None):
+            if ev is not None:
+                ev[0].record(stream)
+            M.route(x, L["w_router"], k, cfg.score, cfg.renorm, bias=bias, topk_ids=ids,
+                    topk_w=w, ws=ws_r)
+            if ev is not None:
+                ev[1].record(stream)
+            M.quantize_fp8(x, 1, q=xq, e=xe)
+            if ev is not None:
+                ev[2].record(stream)
+            M.permute(ids, E, counts, offsets, perm, inv, ws=ws_p)
+            if ev is not None:
+                ev[3].record(stream)
+            M.expert_gate_up_fp8(xq, xe, perm, offsets, wq8["wg_q"], wq8["wg_e"], wq8["wu_q"],
+                                 wq8["wu_e"], k, act_q=aq, act_e=ae, ws=ws_g8)
+            if ev is not None:
+                ev[4].record(stream)
+            M.expert_down_fp8(aq, ae, perm, offsets, wq8["wd_q"], wq8["wd_e"], k, y=y,
+                              ws=ws_d8)
+            if ev is not None:
+                ev[5].record(stream)
+            M.combine(y, w, out=out8)
+            if ev is not None:
+                ev[6].record(stream)
+
+        step8()
+        ref8 = M.forward_fp8(x, L["w_router"], wq8, k, cfg.score, cfg.renorm, bias=bias)
+        torch.cuda.synchronize()
+        assert torch.equal(out8.view(torch.int16), ref8.view(torch.int16)), \
+            "staged FP8 step differs from moe_forward_fp8"
+        del ref8
+        for _ in range(2):
+            step8()
+        K8 = max(3, min(K, 10))
+        ev8 = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(K8)]
+        torch.cuda.synchronize()
+        t8 = time.perf_counter()
+        for i in range(K8):
+            step8(ev8[i])
+        torch.cuda.synchronize()
+        ms8 = (time.perf_counter() - t8) * 1000.0 / K8
+        n8 = ["route", "quantize_x", "permute", "gate_up_fp8", "down_fp8", "combine"]
+        st8 = {n: float(np.mean([ev8[i][j].elapsed_time(ev8[i][j + 1]) for i in range(K8)]))
+               for j, n in enumerate(n8)}
+        gu8 = 4.0 * A * H * F / (st8["gate_up_fp8"] * 1e-3) / 1e12
+        dn8 = 2.0 * A * H * F / (st8["down_fp8"] * 1e-3) / 1e12
+        o8, o16 = out8.float(), out.float()
+        rel = float((o8 - o16).norm() / o16.norm())
+        nd8 = 0
+        b8 = out8.view(torch.int16).cpu().numpy()
+        for i in range(min(4, n_probe)):
+            p1 = M.forward_fp8(probes[i:i + 1].contiguous(), L["w_router"], wq8, k, cfg.score,
+                               cfg.renorm, bias=bias)
+            a1 = p1.view(torch.int16).cpu().numpy()[0]
+            b1 = b8[probe_pos[i]] if T >= 16 else b8[0]
+            nd8 += int(np.unpackbits(np.bitwise_xor(a1, b1).view(np.uint8)).sum())
+        fp8_res = {"ms_per_step": round(ms8, 4), "tokens_per_s": round(T / (ms8 * 1e-3), 1),
+                   "stages_ms": {n: round(v, 4) for n, v in st8.items()},
+                   "gate_up_fp8_tflops": round(gu8, 2),
+                   "gate_up_fp8_mfma_frac": round(gu8 / PEAK_FP8_TFLOPS, 4),
+                   "down_fp8_tflops": round(dn8, 2),
+                   "down_fp8_mfma_frac": round(dn8 / PEAK_FP8_TFLOPS, 4),
+                   "speedup_vs_bf16_step": round(ms_step / ms8, 3),
+                   "out_rel_diff_vs_bf16": round(rel, 5),
+                   "probe_bits_differing": nd8,
+                   "weight_quantise_s": round(wq_s, 3)}
+        del wq8, xq, xe, aq, ae, ws_g8, ws_d8
+
     # Decode workload: the measurement downstream of the step (vocabulary
     # projection, log-softmax, k3 of this batch against itself), timed on its
     # own; the projection streams V x H bf16 weights.
@@ -290,6 +377,16 @@ def main():
         dms = [float(np.mean([evd[i][j].elapsed_time(evd[i][j + 1]) for i in range(KD)]))
                for j in range(3)]
         proj_bytes = 2.0 * V * H
+        if out8 is not None:
+            # the gap the FP8 rollout leaves against the BF16 policy: k3 of the
+            # FP8 layer's next-token distribution against the BF16 layer's
+            lp8 = M.log_softmax(M.lm_head_logits(out8, P))
+            k3m, _, g8 = M.k3(lp, lp8)
+            _, _, g16 = M.k3(lp, lp)
+            fp8_res["decode_k3_vs_bf16"] = {
+                "k3_mean": float(k3m.mean().item()), "k3_max": float(k3m.max().item()),
+                "greedy_agree": float((g8 == g16).float().mean().item())}
+            del lp8
         decode_res = {"vocab": V, "lm_head_ms": round(dms[0], 4),
                       "lm_head_hbm_frac": round(proj_bytes / (dms[0] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                       "lm_head_valu_tflops": round(2.0 * T * V * H / (dms[0] * 1e-3) / 1e12, 2),
@@ -363,6 +460,7 @@ def main():
         "splitk_variant": variant_res,
         "router_replay": replay_res,
         "indexer_topk": topk_res,
+        "fp8_experts": fp8_res,
     }
     if decode_res is not None:
         res["decode_measure"] = decode_res

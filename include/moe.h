@@ -111,7 +111,10 @@ typedef enum moe_op {
     MOE_OP_DOWN = 3,
     MOE_OP_GROUPED_SWIGLU = 4,
     MOE_OP_COMBINE = 5,
-    MOE_OP_FORWARD = 6
+    MOE_OP_FORWARD = 6,
+    MOE_OP_GATE_UP_FP8 = 7,
+    MOE_OP_DOWN_FP8 = 8,
+    MOE_OP_FORWARD_FP8 = 9
 } moe_op;
 
 /* Bytes of device scratch the entry point `op` needs for these sizes
@@ -279,6 +282,80 @@ int moe_log_softmax(int T, int V, const float* z, float* logp, void* stream);
  *   [T] fp64; greedy [device] out [T] int32. */
 int moe_k3(int T, int V, const float* logp_ref, const float* logp_test, double* k3_mean,
            double* k3_greedy, int32_t* greedy, void* stream);
+
+/* ------------------------------------------------------------------------
+ * FP8 rollout path.  The pages' large-MoE recipe trains in BF16, samples
+ * rollouts with FP8 expert weights converted from the BF16 ones, and keeps
+ * measuring the gap between the two ("GLM Post-Training Beyond SFT",
+ * quantisation section).  They fix no format; the reading taken:
+ *   codes     OCP E4M3FN bytes (uint8): bias 7, 3 mantissa bits,
+ *             subnormals, largest 448, 0x7F/0xFF NaN; fp32 -> e4m3 rounds to
+ *             nearest, ties to even.
+ *   exponents one signed byte e per block, value ~ code * 2^e, e = the
+ *             smallest integer with max|v| <= 448 * 2^e over the block,
+ *             clamped to [-127, 127] (0 for an all-zero block, 127 if the
+ *             block holds an infinity).  Weight blocks are 128 output rows x
+ *             128 K, activation blocks 1 row x 128 K.
+ *   GEMM      out = fp32 sum over K blocks, ascending, of 2^(ea + ew) x the
+ *             block's sum of 128 code products; the matrix unit forms each
+ *             block sum in groups of 8 products aligned to the group's
+ *             largest (products more than 13 binades below it are cut
+ *             toward zero), so an output is within 7 * 2^-13 * sum over
+ *             groups of the largest |product| (times 2^(ea+ew)) plus fp32
+ *             roundings of the exact-block-sum value.
+ *   expert    g, u by the GEMM; act = bf16(silu(g) * u); act is quantised
+ *             by rows for the down GEMM.  Routing and combine are those of
+ *             the bf16 layer (the router stays bf16).
+ * Layouts: weights as the bf16 ones (w_gate/w_up codes [E,F,H] with
+ * exponents [E,F/128,H/128]; w_down codes [E,H,F] with [E,H/128,F/128]).
+ * Limits: those of the bf16 layer, and H, F multiples of 128 with the K side
+ * of each GEMM (H for gate/up, F for down) at most 8192 (else
+ * MOE_ERR_UNSUPPORTED / MOE_ERR_SHAPE).  Batch invariance holds as in the
+ * bf16 GEMMs: one tile, one instruction, ascending K blocks, no split.
+ * ------------------------------------------------------------------------ */
+
+/* Block quantiser: src [device] [R,K] bf16 -> q [device] out [R,K] e4m3 codes
+ * and exps [device] out [R/block_rows, K/128] int8.  Rows r*block_rows ..
+ * (r+1)*block_rows - 1 and 128 consecutive columns form a block (weights
+ * [E,N,K] pass R = E*N rows with block_rows = 128; activations pass
+ * block_rows = 1).  Limits: 0 <= R, 1 <= block_rows, R % block_rows == 0,
+ * K % 128 == 0, 128 <= K <= 65536, R*K <= 2^40 (a whole expert weight
+ * tensor in one call).  No workspace. */
+int moe_quantize_fp8(int R, int K, int block_rows, const uint16_t* src, uint8_t* q,
+                     int8_t* exps, void* stream);
+
+/* FP8 gate/up GEMM with the SwiGLU epilogue, quantising its output:
+ *   xq [device] [T,H] codes, xe [device] [T,H/128] exps (x quantised by
+ *   rows); perm, expert_offsets as moe_expert_gate_up; wg_q, wu_q [device]
+ *   [E,F,H] codes with wg_e, wu_e [device] [E,F/128,H/128];
+ *   act_q [device] out [T*k,F] codes and act_e [device] out [T*k,F/128]
+ *   exps of act = bf16(silu(g)*u), rows in permuted order;
+ *   act_bf16 [device] out [T*k,F] bf16 or NULL: act itself.
+ *   ws: moe_workspace_bytes(MOE_OP_GATE_UP_FP8, ...). */
+int moe_expert_gate_up_fp8(int T, int H, int E, int F, int top_k, const uint8_t* xq,
+                           const int8_t* xe, const int32_t* perm, const int32_t* expert_offsets,
+                           const uint8_t* wg_q, const int8_t* wg_e, const uint8_t* wu_q,
+                           const int8_t* wu_e, uint8_t* act_q, int8_t* act_e, uint16_t* act_bf16,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/* FP8 down GEMM: act_q [device] [T*k,F] codes with act_e [T*k,F/128] (rows
+ * in permuted order, as moe_expert_gate_up_fp8 writes them); wd_q [device]
+ * [E,H,F] codes with wd_e [E,H/128,F/128]; y [device] out [T*k,H] fp32 in
+ * assignment order.  ws: moe_workspace_bytes(MOE_OP_DOWN_FP8, ...). */
+int moe_expert_down_fp8(int T, int H, int E, int F, int top_k, const uint8_t* act_q,
+                        const int8_t* act_e, const int32_t* perm, const int32_t* expert_offsets,
+                        const uint8_t* wd_q, const int8_t* wd_e, float* y, void* ws,
+                        size_t ws_bytes, void* stream);
+
+/* The FP8 layer: bf16 routing (as moe_forward), x quantised by rows,
+ * permute, the two FP8 GEMMs, the fixed-order combine.  Weights are passed
+ * quantised (moe_quantize_fp8 once, at load time).  topk_ids / topk_w as in
+ * moe_forward.  ws: moe_workspace_bytes(MOE_OP_FORWARD_FP8, ...). */
+int moe_forward_fp8(int T, int H, int E, int F, int top_k, int score, int renormalize,
+                    const uint16_t* x, const uint16_t* w_router, const float* bias,
+                    const uint8_t* wg_q, const int8_t* wg_e, const uint8_t* wu_q,
+                    const int8_t* wu_e, const uint8_t* wd_q, const int8_t* wd_e, uint16_t* out,
+                    int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -80,6 +80,43 @@ FwdLayout fwd_layout(int T, int H, int E, int F, int top_k) {
     return L;
 }
 
+// FP8 path: H and F in 128-wide blocks, a GEMM's K side at most 8192.
+int check_layer_fp8(int T, int H, int E, int F, int top_k) {
+    MOE_TRY(check_layer(T, H, E, F, top_k));
+    if (H % moe::kFp8Block || F % moe::kFp8Block) return MOE_ERR_UNSUPPORTED;
+    if (H > moe::kFp8MaxKB * moe::kFp8Block || F > moe::kFp8MaxKB * moe::kFp8Block)
+        return MOE_ERR_SHAPE;
+    return 0;
+}
+
+// Workspace layout of moe_forward_fp8.
+struct Fwd8Layout {
+    size_t ids, w, counts, offsets, perm, inv_perm, route, permute, sched, xq, xe, aq, ae, y,
+        total;
+};
+
+Fwd8Layout fwd8_layout(int T, int H, int E, int F, int top_k) {
+    const size_t A = (size_t)T * top_k;
+    Fwd8Layout L;
+    size_t o = 0;
+    L.ids = o; o += up(A * 4);
+    L.w = o; o += up(A * 4);
+    L.counts = o; o += up((size_t)E * 4);
+    L.offsets = o; o += up((size_t)(E + 1) * 4);
+    L.perm = o; o += up(A * 4);
+    L.inv_perm = o; o += up(A * 4);
+    L.route = o; o += up(moe::route_ws_bytes(T, H, E));
+    L.permute = o; o += up(moe::permute_ws_bytes((int)A, E));
+    L.sched = o; o += up(moe::gemm_sched_ws_bytes(E));
+    L.xq = o; o += up((size_t)T * H);
+    L.xe = o; o += up((size_t)T * (H / moe::kFp8Block));
+    L.aq = o; o += up(A * (size_t)F);
+    L.ae = o; o += up(A * (size_t)(F / moe::kFp8Block));
+    L.y = o; o += up(A * (size_t)H * 4);
+    L.total = o;
+    return L;
+}
+
 size_t swiglu_ws(int T, int E, int F, int top_k) {
     return up(moe::gemm_sched_ws_bytes(E)) + up((size_t)T * top_k * (size_t)F * 2);
 }
@@ -132,6 +169,13 @@ size_t moe_workspace_bytes(int op, int T, int H, int E, int F, int top_k, int va
         case MOE_OP_FORWARD:
             if (check_layer(T, H, E, F, top_k)) return 0;
             return fwd_layout(T, H, E, F, top_k).total;
+        case MOE_OP_GATE_UP_FP8:
+        case MOE_OP_DOWN_FP8:
+            if (variant != MOE_GEMM_INVARIANT || check_layer_fp8(T, H, E, F, top_k)) return 0;
+            return moe::gemm_sched_ws_bytes(E);
+        case MOE_OP_FORWARD_FP8:
+            if (variant != MOE_GEMM_INVARIANT || check_layer_fp8(T, H, E, F, top_k)) return 0;
+            return fwd8_layout(T, H, E, F, top_k).total;
         default:
             return 0;
     }
@@ -380,4 +424,103 @@ int moe_k3(int T, int V, const float* logp_ref, const float* logp_test, double* 
         return MOE_ERR_ALIGN;
     return hip_rc(moe::launch_k3(T, V, logp_ref, logp_test, k3_mean, k3_greedy, greedy,
                                  S(stream)));
+}
+
+// ---------------------------------------------------------------------------
+// FP8 rollout path
+// ---------------------------------------------------------------------------
+
+int moe_quantize_fp8(int R, int K, int block_rows, const uint16_t* src, uint8_t* q,
+                     int8_t* exps, void* stream) {
+    if (R < 0 || block_rows < 1 || K < moe::kFp8Block || K > 65536) return MOE_ERR_SHAPE;
+    if (K % moe::kFp8Block || R % block_rows) return MOE_ERR_SHAPE;
+    if ((long)R * K > (1L << 40)) return MOE_ERR_SHAPE;   // 64-bit offsets inside
+    if (R == 0) return MOE_OK;
+    if (!src || !q || !exps) return MOE_ERR_NULL;
+    if (!aligned16(src) || !aligned16(q) || !aligned16(exps)) return MOE_ERR_ALIGN;
+    return hip_rc(moe::launch_quantize_fp8(R, K, block_rows, src, q, exps, S(stream)));
+}
+
+int moe_expert_gate_up_fp8(int T, int H, int E, int F, int top_k, const uint8_t* xq,
+                           const int8_t* xe, const int32_t* perm, const int32_t* expert_offsets,
+                           const uint8_t* wg_q, const int8_t* wg_e, const uint8_t* wu_q,
+                           const int8_t* wu_e, uint8_t* act_q, int8_t* act_e, uint16_t* act_bf16,
+                           void* ws, size_t ws_bytes, void* stream) {
+    MOE_TRY(check_layer_fp8(T, H, E, F, top_k));
+    if (T == 0) return MOE_OK;
+    if (!xq || !xe || !perm || !expert_offsets || !wg_q || !wg_e || !wu_q || !wu_e || !act_q ||
+        !act_e || !ws)
+        return MOE_ERR_NULL;
+    if (!aligned16(xq) || !aligned16(xe) || !aligned16(perm) || !aligned16(expert_offsets) ||
+        !aligned16(wg_q) || !aligned16(wg_e) || !aligned16(wu_q) || !aligned16(wu_e) ||
+        !aligned16(act_q) || !aligned16(act_e) || !aligned16(ws) ||
+        (act_bf16 && !aligned16(act_bf16)))
+        return MOE_ERR_ALIGN;
+    if (ws_bytes < moe::gemm_sched_ws_bytes(E)) return MOE_ERR_WORKSPACE;
+    return hip_rc(moe::launch_gate_up_fp8(T, H, E, F, top_k, xq, xe, perm, expert_offsets, wg_q,
+                                          wg_e, wu_q, wu_e, act_q, act_e, act_bf16,
+                                          static_cast<int32_t*>(ws), S(stream)));
+}
+
+int moe_expert_down_fp8(int T, int H, int E, int F, int top_k, const uint8_t* act_q,
+                        const int8_t* act_e, const int32_t* perm, const int32_t* expert_offsets,
+                        const uint8_t* wd_q, const int8_t* wd_e, float* y, void* ws,
+                        size_t ws_bytes, void* stream) {
+    MOE_TRY(check_layer_fp8(T, H, E, F, top_k));
+    if (T == 0) return MOE_OK;
+    if (!act_q || !act_e || !perm || !expert_offsets || !wd_q || !wd_e || !y || !ws)
+        return MOE_ERR_NULL;
+    if (!aligned16(act_q) || !aligned16(act_e) || !aligned16(perm) ||
+        !aligned16(expert_offsets) || !aligned16(wd_q) || !aligned16(wd_e) || !aligned16(y) ||
+        !aligned16(ws))
+        return MOE_ERR_ALIGN;
+    if (ws_bytes < moe::gemm_sched_ws_bytes(E)) return MOE_ERR_WORKSPACE;
+    return hip_rc(moe::launch_down_fp8(T, H, E, F, top_k, act_q, act_e, perm, expert_offsets,
+                                       wd_q, wd_e, y, static_cast<int32_t*>(ws), S(stream)));
+}
+
+int moe_forward_fp8(int T, int H, int E, int F, int top_k, int score, int renormalize,
+                    const uint16_t* x, const uint16_t* w_router, const float* bias,
+                    const uint8_t* wg_q, const int8_t* wg_e, const uint8_t* wu_q,
+                    const int8_t* wu_e, const uint8_t* wd_q, const int8_t* wd_e, uint16_t* out,
+                    int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes, void* stream) {
+    MOE_TRY(check_layer_fp8(T, H, E, F, top_k));
+    if (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID) return MOE_ERR_UNSUPPORTED;
+    if (renormalize != 0 && renormalize != 1) return MOE_ERR_UNSUPPORTED;
+    if (score == MOE_SCORE_SOFTMAX && bias) return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!x || !w_router || !wg_q || !wg_e || !wu_q || !wu_e || !wd_q || !wd_e || !out || !ws)
+        return MOE_ERR_NULL;
+    if (!aligned16(x) || !aligned16(w_router) || !aligned16(wg_q) || !aligned16(wg_e) ||
+        !aligned16(wu_q) || !aligned16(wu_e) || !aligned16(wd_q) || !aligned16(wd_e) ||
+        !aligned16(out) || !aligned16(ws) || (bias && !aligned16(bias)) ||
+        (topk_ids && !aligned16(topk_ids)) || (topk_w && !aligned16(topk_w)))
+        return MOE_ERR_ALIGN;
+    const Fwd8Layout L = fwd8_layout(T, H, E, F, top_k);
+    if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    const int A = T * top_k;
+    int32_t* ids = topk_ids ? topk_ids : reinterpret_cast<int32_t*>(at(ws, L.ids));
+    float* w = topk_w ? topk_w : reinterpret_cast<float*>(at(ws, L.w));
+    int32_t* counts = reinterpret_cast<int32_t*>(at(ws, L.counts));
+    int32_t* offsets = reinterpret_cast<int32_t*>(at(ws, L.offsets));
+    int32_t* perm = reinterpret_cast<int32_t*>(at(ws, L.perm));
+    int32_t* inv = reinterpret_cast<int32_t*>(at(ws, L.inv_perm));
+    float* part = reinterpret_cast<float*>(at(ws, L.route));
+    int32_t* pws = reinterpret_cast<int32_t*>(at(ws, L.permute));
+    int32_t* sched = reinterpret_cast<int32_t*>(at(ws, L.sched));
+    uint8_t* xq = reinterpret_cast<uint8_t*>(at(ws, L.xq));
+    int8_t* xe = reinterpret_cast<int8_t*>(at(ws, L.xe));
+    uint8_t* aq = reinterpret_cast<uint8_t*>(at(ws, L.aq));
+    int8_t* ae = reinterpret_cast<int8_t*>(at(ws, L.ae));
+    float* y = reinterpret_cast<float*>(at(ws, L.y));
+    hipStream_t s = S(stream);
+    MOE_TRY(hip_rc(moe::launch_route(T, H, E, top_k, score, renormalize, x, w_router, bias, ids,
+                                     w, part, s)));
+    MOE_TRY(hip_rc(moe::launch_quantize_fp8(T, H, 1, x, xq, xe, s)));
+    MOE_TRY(hip_rc(moe::launch_permute(A, E, ids, counts, offsets, perm, inv, pws, s)));
+    MOE_TRY(hip_rc(moe::launch_gate_up_fp8(T, H, E, F, top_k, xq, xe, perm, offsets, wg_q, wg_e,
+                                           wu_q, wu_e, aq, ae, nullptr, sched, s)));
+    MOE_TRY(hip_rc(moe::launch_down_fp8(T, H, E, F, top_k, aq, ae, perm, offsets, wd_q, wd_e, y,
+                                        sched, s)));
+    return hip_rc(launch_combine(T, H, top_k, y, w, out, s));
 }

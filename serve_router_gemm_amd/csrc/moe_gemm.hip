@@ -32,6 +32,7 @@
 // costs and what breaking it does: experts with few tokens have their K range
 // cut into 2..8 parts, each summed on its own and added with fp32 atomics.
 #include "moe_device.h"
+#include "moe_gemm_tiles.h"
 #include "moe_internal.h"
 
 namespace moe {
@@ -43,14 +44,6 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMB = 8;                   // MFMA blocks of 16 weight rows per wave
 constexpr int kNB = 4;                   // MFMA blocks of 16 token rows per wave
-#ifndef MOE_GROUP_M
-#define MOE_GROUP_M 8
-#endif
-#ifndef MOE_XCD_REMAP
-#define MOE_XCD_REMAP 1
-#endif
-constexpr int kGroupM = MOE_GROUP_M;     // token tiles per raster group
-constexpr int kXcds = 8;
 
 constexpr int MODE_GATE_UP = 0;
 constexpr int MODE_DOWN = 1;
@@ -102,7 +95,7 @@ __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g));
 // ascending, accumulators from 0.
 // ---------------------------------------------------------------------------
 constexpr int kP_Threads = 512;
-constexpr int kP_Tok = 256;
+constexpr int kP_Tok = kTileTok;
 constexpr int kP_W = 256;
 constexpr int kP_BK = 64;
 constexpr int kP_Rows = kP_W + kP_Tok;          // 512
@@ -117,15 +110,6 @@ constexpr int kP_Issuers = MOE_ISSUERS;         // waves that issue the stage lo
 constexpr int kP_Dma = kP_Blocks / kP_Issuers;  // loads per issuing thread per stage
 constexpr int kP_WDma = kP_WBlocks / kP_Issuers;   // the first of them: weight blocks
 constexpr int kP_GateUpF = kP_W / 2;            // 128
-
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-                 :: "v"(g), "s"(lds) : "memory");
-}
-
-__device__ __forceinline__ void block_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 
 template <int MODE>
 __global__ __launch_bounds__(kP_Threads) void expert_gemm_pipe_kernel(GemmParams P) {
@@ -156,9 +140,7 @@ __global__ __launch_bounds__(kP_Threads) void expert_gemm_pipe_kernel(GemmParams
     const int total_m = total_long + P.tail[0];
     const int total = total_m * P.n_tiles;
     const int nblk = gridDim.x;
-    const int per_xcd = nblk / kXcds;
-    const int slot = MOE_XCD_REMAP ? (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds
-                                   : (int)blockIdx.x;
+    const int slot = tile_slot();
     const int KT = P.K / kP_BK;
 
     // 16-row weight group mb (0..7) of this wave -> first 8-row block
@@ -172,28 +154,9 @@ __global__ __launch_bounds__(kP_Threads) void expert_gemm_pipe_kernel(GemmParams
         const int lt = base + slot;
         if (lt >= total) break;
 
-        const int gsize = kGroupM * P.n_tiles;
-        const int g = lt / gsize;
-        const int first_m = g * kGroupM;
-        const int gm = min(total_m - first_m, kGroupM);
-        const int r = lt - g * gsize;
-        const int mt = first_m + r % gm;
-        const int nt = r / gm;
-
-        int e, local;
-        if (mt < total_long) {
-            int lo = 0, hi = E - 1;
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (P.tile_start[mid] <= mt) lo = mid; else hi = mid - 1;
-            }
-            e = lo;
-            local = mt - P.tile_start[e];
-        } else {
-            // a short last tile: the list holds them after all long tiles
-            e = P.tail[1 + mt - total_long];
-            local = (P.offsets[e + 1] - P.offsets[e] - 1) / kP_Tok;
-        }
+        const TileRef tr = tile_at(lt, total_m, total_long, P.n_tiles, E, P.tile_start, P.tail,
+                                   P.offsets);
+        const int e = tr.e, local = tr.local, nt = tr.nt;
         int parts = 1, part = 0, mloc = local;
         if (MODE == MODE_DOWN_SPLITK) {
             parts = P.split[e];
@@ -457,6 +420,13 @@ int device_cu_count() {
 }
 
 size_t gemm_sched_ws_bytes(int E) { return (size_t)(3 * E + 2) * sizeof(int32_t); }
+
+hipError_t launch_tile_schedule(int E, int variant, int reorder, const int32_t* offsets,
+                                int32_t* sched_ws, hipStream_t s) {
+    tile_schedule_kernel<<<1, 512, 0, s>>>(E, variant, reorder, offsets, sched_ws,
+                                           sched_ws + E + 1, sched_ws + 2 * E + 1);
+    return hipGetLastError();
+}
 
 hipError_t launch_gate_up(int T, int H, int E, int F, int k, const uint16_t* x,
                           const int32_t* perm, const int32_t* offsets, const uint16_t* wg,

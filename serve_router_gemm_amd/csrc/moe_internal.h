@@ -44,6 +44,24 @@ hipError_t launch_gate_up(int T, int H, int E, int F, int k, const uint16_t* x,
 hipError_t launch_down(int T, int H, int E, int F, int k, const uint16_t* h_act,
                        const int32_t* perm, const int32_t* offsets, const uint16_t* wd,
                        float* y, int variant, int32_t* sched_ws, hipStream_t s);
+// the tile list of the grouped GEMMs into sched_ws (gemm_sched_ws_bytes(E))
+hipError_t launch_tile_schedule(int E, int variant, int reorder, const int32_t* offsets,
+                                int32_t* sched_ws, hipStream_t s);
+
+// FP8 rollout path ------------------------------------------------------------
+constexpr int kFp8Block = 128;     // scale block: 128 K (x 128 rows for weights)
+constexpr int kFp8MaxKB = 64;      // K blocks a GEMM holds (K <= 8192)
+hipError_t launch_quantize_fp8(int R, int K, int block_rows, const uint16_t* src, uint8_t* q,
+                               int8_t* exps, hipStream_t s);
+hipError_t launch_gate_up_fp8(int T, int H, int E, int F, int k, const uint8_t* xq,
+                              const int8_t* xe, const int32_t* perm, const int32_t* offsets,
+                              const uint8_t* wgq, const int8_t* wge, const uint8_t* wuq,
+                              const int8_t* wue, uint8_t* aq, int8_t* ae, uint16_t* act_bf16,
+                              int32_t* sched_ws, hipStream_t s);
+hipError_t launch_down_fp8(int T, int H, int E, int F, int k, const uint8_t* aq,
+                           const int8_t* ae, const int32_t* perm, const int32_t* offsets,
+                           const uint8_t* wdq, const int8_t* wde, float* y, int32_t* sched_ws,
+                           hipStream_t s);
 
 // decode-step measurement: vocabulary projection, log-softmax, k3 ------------
 constexpr int kSumChunk = 256;     // fixed chunk of the vocabulary sums

@@ -21,7 +21,9 @@ SCORE_SIGMOID = 1
 INVARIANT = 0
 SPLITK_VARIANT = 1
 
-OP_ROUTE, OP_PERMUTE, OP_GATE_UP, OP_DOWN, OP_GROUPED_SWIGLU, OP_COMBINE, OP_FORWARD = range(7)
+(OP_ROUTE, OP_PERMUTE, OP_GATE_UP, OP_DOWN, OP_GROUPED_SWIGLU, OP_COMBINE, OP_FORWARD,
+ OP_GATE_UP_FP8, OP_DOWN_FP8, OP_FORWARD_FP8) = range(10)
+FP8_BLOCK = 128
 
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_ALIGN",
           -4: "MOE_ERR_UNSUPPORTED", -5: "MOE_ERR_WORKSPACE", -6: "MOE_ERR_HIP"}
@@ -49,6 +51,12 @@ SIGNATURES = {
     "moe_lm_head_logits": (_I, [_I, _I, _I, _P, _P, _P, _P]),
     "moe_log_softmax": (_I, [_I, _I, _P, _P, _P]),
     "moe_k3": (_I, [_I, _I, _P, _P, _P, _P, _P, _P]),
+    "moe_quantize_fp8": (_I, [_I, _I, _I, _P, _P, _P, _P]),
+    "moe_expert_gate_up_fp8": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                    _P, _P, _Z, _P]),
+    "moe_expert_down_fp8": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
+    "moe_forward_fp8": (_I, [_I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                             _P, _P, _P, _Z, _P]),
 }
 
 _lib = None
@@ -367,3 +375,127 @@ def topk_large(scores, k, lengths=None, want_vals=True, stream=None):
     _check("moe_topk_large", rc)
     return idx, vals
 
+
+
+# ---------------------------------------------------------------------------
+# FP8 rollout path
+# ---------------------------------------------------------------------------
+def quantize_fp8(src, block_rows, q=None, e=None, stream=None):
+    """moe_quantize_fp8: bf16 [..., R, K] -> (codes uint8 [..., R, K], exps int8
+    [..., R/block_rows, K/128]); the leading axes fold into rows (blocks never
+    cross them when R % block_rows == 0)."""
+    _dev(src, "src", torch.bfloat16)
+    *lead, R, K = src.shape
+    if R % block_rows:
+        raise ValueError("R must be a multiple of block_rows")
+    rows = src.numel() // K if src.numel() else 0
+    if q is None:
+        q = torch.empty(src.shape, dtype=torch.uint8, device=src.device)
+    if e is None:
+        e = torch.empty((*lead, R // block_rows, K // FP8_BLOCK), dtype=torch.int8,
+                        device=src.device)
+    _dev(q, "q", torch.uint8, src.shape)
+    _dev(e, "exps", torch.int8, (*lead, R // block_rows, K // FP8_BLOCK))
+    rc = lib().moe_quantize_fp8(rows, K, block_rows, _ptr(src), _ptr(q), _ptr(e),
+                                _stream(stream))
+    _check("moe_quantize_fp8", rc)
+    return q, e
+
+
+def quantize_weights_fp8(w_gate, w_up, w_down, stream=None) -> dict:
+    """The three expert weight tensors in 128 x 128 blocks -> dict of
+    wg_q, wg_e, wu_q, wu_e, wd_q, wd_e."""
+    wq = {}
+    wq["wg_q"], wq["wg_e"] = quantize_fp8(w_gate, FP8_BLOCK, stream=stream)
+    wq["wu_q"], wq["wu_e"] = quantize_fp8(w_up, FP8_BLOCK, stream=stream)
+    wq["wd_q"], wq["wd_e"] = quantize_fp8(w_down, FP8_BLOCK, stream=stream)
+    return wq
+
+
+def _check_wq(wq, E, F, H):
+    _dev(wq["wg_q"], "wg_q", torch.uint8, (E, F, H))
+    _dev(wq["wu_q"], "wu_q", torch.uint8, (E, F, H))
+    _dev(wq["wd_q"], "wd_q", torch.uint8, (E, H, F))
+    _dev(wq["wg_e"], "wg_e", torch.int8, (E, F // FP8_BLOCK, H // FP8_BLOCK))
+    _dev(wq["wu_e"], "wu_e", torch.int8, (E, F // FP8_BLOCK, H // FP8_BLOCK))
+    _dev(wq["wd_e"], "wd_e", torch.int8, (E, H // FP8_BLOCK, F // FP8_BLOCK))
+
+
+def expert_gate_up_fp8(xq, xe, perm, offsets, wg_q, wg_e, wu_q, wu_e, top_k, want_bf16=False,
+                       act_q=None, act_e=None, ws=None, stream=None):
+    """moe_expert_gate_up_fp8: -> (act_q [T*k,F] uint8, act_e [T*k,F/128] int8,
+    act bf16 [T*k,F] or None), rows in permuted order."""
+    T, H = xq.shape
+    E, F = wg_q.shape[0], wg_q.shape[1]
+    _dev(xq, "xq", torch.uint8)
+    _dev(xe, "xe", torch.int8, (T, H // FP8_BLOCK))
+    _dev(perm, "perm", torch.int32, (T * top_k,))
+    _dev(offsets, "expert_offsets", torch.int32, (E + 1,))
+    _dev(wg_q, "wg_q", torch.uint8, (E, F, H))
+    _dev(wu_q, "wu_q", torch.uint8, (E, F, H))
+    _dev(wg_e, "wg_e", torch.int8, (E, F // FP8_BLOCK, H // FP8_BLOCK))
+    _dev(wu_e, "wu_e", torch.int8, (E, F // FP8_BLOCK, H // FP8_BLOCK))
+    dev = xq.device
+    aq = torch.empty((T * top_k, F), dtype=torch.uint8, device=dev) if act_q is None else act_q
+    ae = torch.empty((T * top_k, F // FP8_BLOCK), dtype=torch.int8, device=dev) \
+        if act_e is None else act_e
+    _dev(aq, "act_q", torch.uint8, (T * top_k, F))
+    _dev(ae, "act_e", torch.int8, (T * top_k, F // FP8_BLOCK))
+    ab = torch.empty((T * top_k, F), dtype=torch.bfloat16, device=dev) if want_bf16 else None
+    ws = _ws(ws, workspace_bytes(OP_GATE_UP_FP8, T, H, E, F, top_k), dev)
+    rc = lib().moe_expert_gate_up_fp8(T, H, E, F, top_k, _ptr(xq), _ptr(xe), _ptr(perm),
+                                      _ptr(offsets), _ptr(wg_q), _ptr(wg_e), _ptr(wu_q),
+                                      _ptr(wu_e), _ptr(aq), _ptr(ae), _ptr(ab), _ptr(ws),
+                                      ws.numel(), _stream(stream))
+    _check("moe_expert_gate_up_fp8", rc)
+    return aq, ae, ab
+
+
+def expert_down_fp8(act_q, act_e, perm, offsets, wd_q, wd_e, top_k, y=None, ws=None,
+                    stream=None):
+    """moe_expert_down_fp8: -> y [T*k, H] fp32 (rows in assignment order)."""
+    A, F = act_q.shape
+    E, H = wd_q.shape[0], wd_q.shape[1]
+    T = A // top_k
+    _dev(act_q, "act_q", torch.uint8)
+    _dev(act_e, "act_e", torch.int8, (A, F // FP8_BLOCK))
+    _dev(perm, "perm", torch.int32, (A,))
+    _dev(offsets, "expert_offsets", torch.int32, (E + 1,))
+    _dev(wd_q, "wd_q", torch.uint8, (E, H, F))
+    _dev(wd_e, "wd_e", torch.int8, (E, H // FP8_BLOCK, F // FP8_BLOCK))
+    if y is None:
+        y = torch.empty((A, H), dtype=torch.float32, device=act_q.device)
+    _dev(y, "y", torch.float32, (A, H))
+    ws = _ws(ws, workspace_bytes(OP_DOWN_FP8, T, H, E, F, top_k), act_q.device)
+    rc = lib().moe_expert_down_fp8(T, H, E, F, top_k, _ptr(act_q), _ptr(act_e), _ptr(perm),
+                                   _ptr(offsets), _ptr(wd_q), _ptr(wd_e), _ptr(y), _ptr(ws),
+                                   ws.numel(), _stream(stream))
+    _check("moe_expert_down_fp8", rc)
+    return y
+
+
+def forward_fp8(x, w_router, wq, top_k, score=SCORE_SOFTMAX, renormalize=True, bias=None,
+                out=None, ws=None, stream=None, return_routing=False):
+    """moe_forward_fp8: the FP8 layer -> out [T, H] bf16 (and routing if asked).
+    wq: the dict of quantize_weights_fp8."""
+    T, H = x.shape
+    E, F = wq["wg_q"].shape[0], wq["wg_q"].shape[1]
+    _dev(x, "x", torch.bfloat16)
+    _dev(w_router, "w_router", torch.bfloat16, (E, H))
+    _check_wq(wq, E, F, H)
+    if bias is not None:
+        _dev(bias, "bias", torch.float32, (E,))
+    dev = x.device
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    _dev(out, "out", torch.bfloat16, (T, H))
+    ids = torch.empty((T, top_k), dtype=torch.int32, device=dev) if return_routing else None
+    w = torch.empty((T, top_k), dtype=torch.float32, device=dev) if return_routing else None
+    ws = _ws(ws, workspace_bytes(OP_FORWARD_FP8, T, H, E, F, top_k), dev)
+    rc = lib().moe_forward_fp8(T, H, E, F, top_k, int(score), int(bool(renormalize)), _ptr(x),
+                               _ptr(w_router), _ptr(bias), _ptr(wq["wg_q"]), _ptr(wq["wg_e"]),
+                               _ptr(wq["wu_q"]), _ptr(wq["wu_e"]), _ptr(wq["wd_q"]),
+                               _ptr(wq["wd_e"]), _ptr(out), _ptr(ids), _ptr(w), _ptr(ws),
+                               ws.numel(), _stream(stream))
+    _check("moe_forward_fp8", rc)
+    return (out, ids, w) if return_routing else out

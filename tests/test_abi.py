@@ -209,3 +209,53 @@ def test_topk_large_checks(L):
     assert t(4, 100, 10, FAKE, MIS, FAKE, None, None) == ALIGN
     assert t(4, 100, 10, FAKE, None, FAKE, MIS, None) == ALIGN
     assert t(0, 100, 10, None, None, None, None, None) == OK
+
+
+def test_fp8_checks(L):
+    q = L.moe_quantize_fp8
+    assert q(-1, 256, 1, FAKE, FAKE, FAKE, None) == SHAPE
+    assert q(4, 192, 1, FAKE, FAKE, FAKE, None) == SHAPE           # K not in 128-blocks
+    assert q(4, 0, 1, FAKE, FAKE, FAKE, None) == SHAPE
+    assert q(4, 256, 0, FAKE, FAKE, FAKE, None) == SHAPE
+    assert q(6, 256, 4, FAKE, FAKE, FAKE, None) == SHAPE           # R % block_rows
+    assert q(1 << 26, 1 << 15, 1, FAKE, FAKE, FAKE, None) == SHAPE  # R*K > 2^40
+    assert q(4, 256, 1, None, FAKE, FAKE, None) == NULL
+    assert q(4, 256, 1, FAKE, FAKE, MIS, None) == ALIGN
+    assert q(0, 256, 1, None, None, None, None) == OK
+    gu = L.moe_expert_gate_up_fp8
+    # T, H, E, F, k, xq, xe, perm, offs, wg_q, wg_e, wu_q, wu_e, aq, ae, ab, ws, bytes
+    def call_gu(T=4, H=256, E=8, F=256, k=2, xq=FAKE, ab=None, ws=FAKE, nbytes=1 << 20):
+        return gu(T, H, E, F, k, xq, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ab,
+                  ws, nbytes, None)
+    assert call_gu(H=192) == UNSUP                                  # 64-multiple, not 128
+    assert call_gu(F=320) == UNSUP
+    assert call_gu(H=8192 + 128) == SHAPE                           # K side > 8192
+    assert call_gu(xq=None) == NULL
+    assert call_gu(ab=MIS) == ALIGN
+    assert call_gu(nbytes=0) == WS
+    assert call_gu(T=0, xq=None, ws=None) == OK
+    dn = L.moe_expert_down_fp8
+    assert dn(4, 256, 8, 8192 + 128, 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20,
+              None) == SHAPE                                        # F is the K side here
+    assert dn(4, 256, 8, 256, 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == WS
+    assert dn(4, 256, 8, 256, 2, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20,
+              None) == NULL
+    f = L.moe_forward_fp8
+    def call_f(T=4, H=256, E=8, F=256, k=2, score=0, bias=None, x=FAKE, nbytes=1 << 40):
+        return f(T, H, E, F, k, score, 1, x, FAKE, bias, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                 FAKE, None, None, FAKE, nbytes, None)
+    assert call_f(score=0, bias=FAKE) == UNSUP
+    assert call_f(score=2) == UNSUP
+    assert call_f(x=None) == NULL
+    assert call_f(nbytes=0) == WS
+    assert call_f(H=192) == UNSUP
+    assert call_f(T=0, x=None) == OK
+    wb = L.moe_workspace_bytes
+    T, H, E, F, k = 16384, 6144, 256, 2048, 8
+    A = T * k
+    fwd8 = wb(M.OP_FORWARD_FP8, T, H, E, F, k, 0)
+    assert fwd8 >= A * H * 4 + A * F + T * H
+    assert fwd8 < wb(M.OP_FORWARD, T, H, E, F, k, 0)               # fp8 act is half the bytes
+    assert wb(M.OP_GATE_UP_FP8, T, H, E, F, k, 0) == wb(M.OP_GATE_UP, T, H, E, F, k, 0)
+    assert wb(M.OP_DOWN_FP8, T, H, E, F, k, 1) == 0                 # no split-K FP8 variant
+    assert wb(M.OP_FORWARD_FP8, T, 192, E, F, k, 0) == 0

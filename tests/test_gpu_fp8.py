@@ -1,0 +1,360 @@
+"""The FP8 rollout path on the GPU against the oracle (GPU required).
+
+The pages' large-MoE recipe samples rollouts with FP8 expert weights and keeps
+measuring the gap to the BF16 policy ("GLM Post-Training Beyond SFT",
+quantisation section).  Bars:
+  * block quantiser (weights 128 x 128, activations 1 x 128): codes and
+    exponents bit-exact;
+  * each FP8 GEMM, fed the oracle's codes: every output within the bound of
+    the matrix instruction's arithmetic (measured on gfx950: products added in
+    groups of 8, cut toward zero 13 binades below the group's largest; group
+    sums and the accumulator at fp32 precision):
+        |gpu - oracle| <= sum over K blocks of 2^(ea+ew) *
+                          (7 * 2^-13 * sum_groups max|p| + 2^-19 * sum|p|)
+                          + 2 (nkb + 1) 2^-24 * sum|p| 2^(ea+ew)
+    (the last term: the fp32 accumulation roundings of both sides);
+  * gate/up's bf16 act within that bound carried through silu(g)*u plus a
+    bf16 rounding on each side, and its codes exactly the quantiser's codes
+    of that act;
+  * the whole layer: routing bit-exact; out, whose act codes can differ from
+    the oracle's where the two act values straddle an e4m3 rounding point,
+    within 2^-7 of the oracle's norm-wise (the FP8-vs-BF16 gap is several
+    percent);
+  * batch invariance: probe rows bit-identical at every batch size.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from helpers import DEV, bits, gpu, layer, log
+from oracle import oracle as O
+from serve_router_gemm_amd import inputs as I
+
+pytestmark = gpu
+
+if torch.cuda.is_available():
+    from serve_router_gemm_amd import moe as M
+
+B = 128
+U = 2.0 ** -24
+
+
+def _np(t):
+    return t.cpu().numpy()
+
+
+def deq(q, e, block_rows):
+    """Dequantised codes (fp64)."""
+    v = O.e4m3_to_f32(q).astype(np.float64)
+    er = np.repeat(np.repeat(e.astype(np.float64), block_rows, axis=-2), B, axis=-1)
+    return v * np.exp2(er)
+
+
+def gemm_tol(a_row, w_mat):
+    """Per-output bound of one row (fp64 [K]) against weight rows [N, K]."""
+    K = a_row.shape[0]
+    nkb = K // B
+    p = np.abs(w_mat * a_row[None, :])                     # |products|, scaled
+    gmax = p.reshape(p.shape[0], K // 8, 8).max(axis=-1).sum(axis=-1)
+    psum = p.sum(axis=-1)
+    return 7 * 2.0 ** -13 * gmax + 2.0 ** -19 * psum + 2 * (nkb + 1) * U * psum
+
+
+def fp8_cfg(**kw):
+    base = dict(T=300, H=384, E=8, k=2, F=640)
+    base.update(kw)
+    return I.scaled(I.CONFIGS["tiny"], **base)
+
+
+def quantize_host(L):
+    wq = {}
+    wq["wgq"], wq["wge"] = O.quantize_fp8(bits(L["w_gate"]), B)
+    wq["wuq"], wq["wue"] = O.quantize_fp8(bits(L["w_up"]), B)
+    wq["wdq"], wq["wde"] = O.quantize_fp8(bits(L["w_down"]), B)
+    return wq
+
+
+def test_quantize_fp8_bit_exact():
+    g = torch.Generator(device="cpu").manual_seed(5)
+    w = (torch.randn((3, 384, 256), generator=g) * 0.02)
+    w[0, 5, 7] = 3.0                                  # outlier in one block
+    w[1, 128:256, 0:128] = 0.0                        # all-zero block
+    w[1, 0:128, 128:256] *= 1e-37                     # below 448 * 2^-127: clamped exponent
+    w[2, 300, 200] = float("inf")                     # an infinity
+    w[2, 10, 10] = float("nan")                       # a NaN
+    w[2, 11, 11] = -0.0
+    wb = w.to(torch.bfloat16)
+    a = (torch.randn((37, 384), generator=g) * torch.logspace(-3, 2, 37)[:, None]).to(torch.bfloat16)
+    for src, br in ((wb, B), (a, 1), (wb.reshape(-1, 256), 1)):
+        q, e = M.quantize_fp8(src.to(DEV), br)
+        rq, re = O.quantize_fp8(bits(src), br)
+        assert np.array_equal(_np(q), rq), "codes differ"
+        assert np.array_equal(_np(e), re), "exponents differ"
+    log("[fp8] quantiser bit-exact on weights (128x128) and activations (1x128), "
+        "incl. zero/tiny/inf/NaN blocks")
+
+
+def _routing(cfg, L, x):
+    ids, w = M.route(x, L["w_router"], cfg.k, cfg.score, cfg.renorm, bias=L["bias"])
+    counts, offsets, perm, inv = M.permute(ids, cfg.E)
+    return ids, w, offsets, perm
+
+
+@pytest.mark.parametrize("shape", [dict(), dict(T=37, H=256, F=384, E=5, k=3)],
+                         ids=["T300_H384_F640", "T37_H256_F384"])
+def test_down_fp8_within_bound(shape):
+    cfg = fp8_cfg(**shape)
+    L = layer(cfg)
+    x = I.make_x(cfg, DEV)
+    ids, _, offsets, perm = _routing(cfg, L, x)
+    A = cfg.T * cfg.k
+    g = torch.Generator(device="cpu").manual_seed(9)
+    act = (torch.randn((A, cfg.F), generator=g) *
+           torch.tensor([1e-3, 0.3, 1.0, 30.0])[torch.arange(A) % 4][:, None]).to(torch.bfloat16)
+    aq, ae = O.quantize_fp8(bits(act), 1)              # assignment order
+    wq = quantize_host(L)
+    perm_np = _np(perm)
+    y = M.expert_down_fp8(torch.from_numpy(aq[perm_np]).to(DEV),
+                          torch.from_numpy(ae[perm_np]).to(DEV), perm, offsets,
+                          torch.from_numpy(wq["wdq"]).to(DEV), torch.from_numpy(wq["wde"]).to(DEV),
+                          cfg.k)
+    y = _np(y)
+    experts = _np(ids).reshape(-1)
+    ref = O.fp8_gemm(aq, ae, experts, wq["wdq"], wq["wde"])
+    a_deq = deq(aq, ae, 1)
+    worst = 0.0
+    for a in range(A):
+        tol = gemm_tol(a_deq[a], deq(wq["wdq"][experts[a]], wq["wde"][experts[a]], B))
+        err = np.abs(y[a].astype(np.float64) - ref[a])
+        assert np.all(err <= tol), (a, float((err / tol).max()))
+        worst = max(worst, float((err / tol).max()))
+    same = float(np.mean(y == ref))
+    log(f"[fp8] down {shape or 'default'}: within bound (worst err/bound {worst:.3f}), "
+        f"{same:.3f} of outputs bit-identical to the oracle")
+
+
+def _gate_up_case(cfg):
+    L = layer(cfg)
+    x = I.make_x(cfg, DEV)
+    ids, w, offsets, perm = _routing(cfg, L, x)
+    xq, xe = M.quantize_fp8(x, 1)
+    wqd = M.quantize_weights_fp8(L["w_gate"], L["w_up"], L["w_down"])
+    aq, ae, ab = M.expert_gate_up_fp8(xq, xe, perm, offsets, wqd["wg_q"], wqd["wg_e"],
+                                      wqd["wu_q"], wqd["wu_e"], cfg.k, want_bf16=True)
+    return L, x, ids, w, offsets, perm, xq, xe, wqd, aq, ae, ab
+
+
+def _act_bound(g, u, tg, tu, act_ref):
+    """|act_gpu - act_ref| bound from g, u within tg, tu (silu' in [-0.1, 1.1]),
+    plus a bf16 rounding on each side (2^-8 relative of the larger)."""
+    silu = g / (1.0 + np.exp(-g))
+    return 1.1 * (np.abs(u) + tu) * tg + (np.abs(silu) + 1.1 * tg) * tu, 2.0 ** -8
+
+
+@pytest.mark.parametrize("shape", [dict(), dict(T=37, H=256, F=384, E=5, k=3)],
+                         ids=["T300_H384_F640", "T37_H256_F384"])
+def test_gate_up_fp8_within_bound(shape):
+    cfg = fp8_cfg(**shape)
+    L, x, ids, w, offsets, perm, xq, xe, wqd, aq, ae, ab = _gate_up_case(cfg)
+    wq = quantize_host(L)
+    for n_h, n_g in (("wgq", "wg_q"), ("wge", "wg_e"), ("wuq", "wu_q"), ("wue", "wu_e"),
+                     ("wdq", "wd_q"), ("wde", "wd_e")):
+        assert np.array_equal(_np(wqd[n_g]), wq[n_h]), n_g
+    xq_h, xe_h = O.quantize_fp8(bits(x), 1)
+    assert np.array_equal(_np(xq), xq_h) and np.array_equal(_np(xe), xe_h)
+    A = cfg.T * cfg.k
+    perm_np = _np(perm)
+    act_gpu = np.empty((A, cfg.F), np.uint16)
+    act_gpu[perm_np] = bits(ab)
+    aq_gpu = np.empty((A, cfg.F), np.uint8)
+    aq_gpu[perm_np] = _np(aq)
+    ae_gpu = np.empty((A, cfg.F // B), np.int8)
+    ae_gpu[perm_np] = _np(ae)
+    experts = _np(ids).reshape(-1)
+    toks = np.repeat(np.arange(cfg.T), cfg.k)
+    _, act_ref = O.expert_ffn_fp8(toks, experts, xq_h, xe_h, wq["wgq"], wq["wge"], wq["wuq"],
+                                  wq["wue"], wq["wdq"], wq["wde"], want_act=True)
+    g = O.fp8_gemm(xq_h[toks], xe_h[toks], experts, wq["wgq"], wq["wge"]).astype(np.float64)
+    u = O.fp8_gemm(xq_h[toks], xe_h[toks], experts, wq["wuq"], wq["wue"]).astype(np.float64)
+    x_deq = deq(xq_h, xe_h, 1)
+    ag = O.bf16_to_f32(act_gpu).astype(np.float64)
+    ar = O.bf16_to_f32(act_ref).astype(np.float64)
+    for a in range(A):
+        e = experts[a]
+        tg = gemm_tol(x_deq[toks[a]], deq(wq["wgq"][e], wq["wge"][e], B))
+        tu = gemm_tol(x_deq[toks[a]], deq(wq["wuq"][e], wq["wue"][e], B))
+        absb, rel = _act_bound(g[a], u[a], tg, tu, ar[a])
+        lim = absb + rel * np.maximum(np.abs(ag[a]), np.abs(ar[a])) + 1e-30
+        assert np.all(np.abs(ag[a] - ar[a]) <= lim), (a, float((np.abs(ag[a] - ar[a]) / lim).max()))
+    # the epilogue's codes are the quantiser's codes of its own act
+    q2, e2 = M.quantize_fp8(ab, 1)
+    assert torch.equal(q2, aq) and torch.equal(e2, ae)
+    # where the act rows agree bit for bit, the codes agree with the oracle's
+    same_rows = np.all(act_gpu == act_ref, axis=1)
+    rq, re = O.quantize_fp8(act_ref, 1)
+    assert np.array_equal(aq_gpu[same_rows], rq[same_rows])
+    assert np.array_equal(ae_gpu[same_rows], re[same_rows])
+    log(f"[fp8] gate/up {shape or 'default'}: act within bound; "
+        f"{float(np.mean(act_gpu == act_ref)):.4f} of act elements and "
+        f"{float(np.mean(same_rows)):.3f} of rows bit-identical; codes = quantiser(act)")
+
+
+FWD8_CASES = [
+    ("tiny_full", I.scaled(I.CONFIGS["tiny"]), None),
+    ("mid_T1024", I.scaled(I.CONFIGS["mid"], T=1024), 64),
+]
+
+
+@pytest.mark.parametrize("case", FWD8_CASES, ids=lambda c: c[0])
+def test_forward_fp8_parity(case):
+    name, cfg, nsample = case
+    log(f"[fp8] forward {name}: {I.describe(cfg)}")
+    L = layer(cfg)
+    x = I.make_x(cfg, DEV)
+    wqd = M.quantize_weights_fp8(L["w_gate"], L["w_up"], L["w_down"])
+    out, ids, w = M.forward_fp8(x, L["w_router"], wqd, cfg.k, cfg.score, cfg.renorm,
+                                bias=L["bias"], return_routing=True)
+    out16, ids16, w16 = M.forward(x, L["w_router"], L["w_gate"], L["w_up"], L["w_down"], cfg.k,
+                                  cfg.score, cfg.renorm, bias=L["bias"], return_routing=True)
+    torch.cuda.synchronize()
+    # routing: the bf16 router, the same kernel as the bf16 layer
+    assert torch.equal(ids, ids16)
+    assert torch.equal(w.view(torch.int32), w16.view(torch.int32))
+    rows = np.arange(cfg.T) if nsample is None else np.unique(
+        np.random.default_rng(4).choice(cfg.T, nsample, replace=False))
+    xb = bits(x)
+    wq = quantize_host(L)
+    xq_h, xe_h = O.quantize_fp8(xb, 1)
+    hb = {n: bits(L[n]) for n in ("w_router", "w_gate", "w_up", "w_down")}
+    bias = None if L["bias"] is None else _np(L["bias"])
+    ref8, rids, rw = O.forward_tokens_fp8(rows, xb, hb["w_router"], xq_h, xe_h, wq, cfg.k,
+                                          cfg.score, cfg.renorm, bias=bias)
+    ref16, _, _, _ = O.forward_tokens(rows, xb, hb["w_router"], hb["w_gate"], hb["w_up"],
+                                      hb["w_down"], cfg.k, cfg.score, cfg.renorm, bias=bias)
+    assert np.array_equal(_np(ids)[rows], rids)
+    o = O.bf16_to_f32(bits(out)[rows]).astype(np.float64)
+    r8 = O.bf16_to_f32(ref8).astype(np.float64)
+    r16 = O.bf16_to_f32(ref16).astype(np.float64)
+    rel = np.linalg.norm(o - r8) / np.linalg.norm(r8)
+    gap = np.linalg.norm(r8 - r16) / np.linalg.norm(r16)
+    same = float(np.mean(bits(out)[rows] == ref8))
+    log(f"[fp8] forward {name}: |gpu - oracle| / |oracle| = {rel:.2e}; FP8-vs-BF16 gap "
+        f"{gap:.2e}; {same:.4f} of outputs bit-identical")
+    assert rel <= 2.0 ** -7, rel
+    assert rel < 0.25 * gap, (rel, gap)
+
+
+def _fwd8(cfg, L, wqd, x):
+    return M.forward_fp8(x, L["w_router"], wqd, cfg.k, cfg.score, cfg.renorm, bias=L["bias"])
+
+
+def test_fp8_batch_invariance():
+    """16 probes among random co-tokens at T in {1, 7, 128, 1024, 4096}: 0
+    differing bits against each probe alone."""
+    cfg = I.CONFIGS["mid"]
+    L = layer(cfg)
+    wqd = M.quantize_weights_fp8(L["w_gate"], L["w_up"], L["w_down"])
+    probes = I.probes(cfg.H, 16, DEV)
+    ref = [bits(_fwd8(cfg, L, wqd, probes[i:i + 1].contiguous()))[0] for i in range(16)]
+    for T in I.MID_SWEEP_T:
+        for rep in range(2):
+            if T < 16:
+                for i in range(16):
+                    x = I.make_tokens(T, cfg.H, I.COTOKEN_SEED_BASE + 97 * rep + i, "cpu").to(DEV)
+                    pos = (rep * 5 + i) % T
+                    x[pos] = probes[i]
+                    assert np.array_equal(bits(_fwd8(cfg, L, wqd, x))[pos], ref[i]), (T, rep, i)
+            else:
+                x, pos = I.embed_probes(probes, T, rep)
+                ob = bits(_fwd8(cfg, L, wqd, x))
+                for i in range(16):
+                    assert np.array_equal(ob[pos[i]], ref[i]), (T, rep, i)
+        log(f"[fp8] invariance mid T={T}: 0 differing bits over 2 batches")
+
+
+def test_large_fp8_sampled():
+    """The large layer at T = 16384 in the launch configuration the benchmark
+    times: the GPU's weight codes of sampled experts bit-exact, and act and y of
+    sampled assignments against the oracle (y within the GEMM bound where the
+    act codes agree; the rest counted)."""
+    cfg = I.CONFIGS["large"]
+    L = layer(cfg)
+    x = I.make_x(cfg, DEV)
+    ids, w, offsets, perm = _routing(cfg, L, x)
+    xq, xe = M.quantize_fp8(x, 1)
+    wqd = M.quantize_weights_fp8(L["w_gate"], L["w_up"], L["w_down"])
+    aq, ae, ab = M.expert_gate_up_fp8(xq, xe, perm, offsets, wqd["wg_q"], wqd["wg_e"],
+                                      wqd["wu_q"], wqd["wu_e"], cfg.k, want_bf16=True)
+    y = M.expert_down_fp8(aq, ae, perm, offsets, wqd["wd_q"], wqd["wd_e"], cfg.k)
+    torch.cuda.synchronize()
+    ids_np = _np(ids)
+    perm_np = _np(perm)
+    counts = np.bincount(ids_np.reshape(-1), minlength=cfg.E)
+    active = np.nonzero(counts)[0]
+    busiest = active[np.argsort(-counts[active], kind="stable")][:2]
+    quietest = active[np.argsort(counts[active], kind="stable")][:2]
+    rng = np.random.default_rng(8)
+    picks = []
+    for e in list(busiest) + list(quietest):
+        a_of_e = np.nonzero(ids_np.reshape(-1) == e)[0]
+        picks.extend(rng.choice(a_of_e, size=min(3, len(a_of_e)), replace=False).tolist())
+    picks = np.array(sorted(set(picks)))
+    inv = np.empty_like(perm_np)
+    inv[perm_np] = np.arange(perm_np.size)
+    toks = picks // cfg.k
+    experts = ids_np.reshape(-1)[picks]
+    x_host = bits(x[torch.from_numpy(toks).to(DEV)])
+    xq_h, xe_h = O.quantize_fp8(x_host, 1)
+    assert np.array_equal(_np(xq[torch.from_numpy(toks).to(DEV)]), xq_h)
+    wq = {}
+    uniq = np.unique(experts)
+    for n_h, n_g, src in (("wg", "wg", "w_gate"), ("wu", "wu", "w_up"), ("wd", "wd", "w_down")):
+        wb = bits(L[src][torch.from_numpy(uniq).to(DEV)])
+        q_h, e_h = O.quantize_fp8(wb, B)
+        sel = torch.from_numpy(uniq).to(DEV)
+        assert np.array_equal(_np(wqd[n_g + "_q"][sel]), q_h), n_g
+        assert np.array_equal(_np(wqd[n_g + "_e"][sel]), e_h), n_g
+        wq[n_h + "q"], wq[n_h + "e"] = q_h, e_h
+    loc = np.searchsorted(uniq, experts)
+    y_ref, act_ref = O.expert_ffn_fp8(np.arange(len(picks)), loc, xq_h, xe_h, wq["wgq"],
+                                      wq["wge"], wq["wuq"], wq["wue"], wq["wdq"], wq["wde"],
+                                      want_act=True)
+    rows_p = inv[picks]
+    act_gpu = bits(ab[torch.from_numpy(rows_p).to(DEV)])
+    aq_gpu = _np(aq[torch.from_numpy(rows_p).to(DEV)])
+    ae_gpu = _np(ae[torch.from_numpy(rows_p).to(DEV)])
+    y_gpu = _np(y[torch.from_numpy(picks).to(DEV)]).astype(np.float64)
+    x_deq = deq(xq_h, xe_h, 1)
+    rq, re = O.quantize_fp8(act_ref, 1)
+    g = O.fp8_gemm(xq_h, xe_h, loc, wq["wgq"], wq["wge"]).astype(np.float64)
+    u = O.fp8_gemm(xq_h, xe_h, loc, wq["wuq"], wq["wue"]).astype(np.float64)
+    ag = O.bf16_to_f32(act_gpu).astype(np.float64)
+    ar = O.bf16_to_f32(act_ref).astype(np.float64)
+    # the down GEMM at this size, fed the oracle's act codes in the sampled rows
+    aq2, ae2 = aq.clone(), ae.clone()
+    sel_p = torch.from_numpy(rows_p).to(DEV)
+    aq2[sel_p] = torch.from_numpy(rq).to(DEV)
+    ae2[sel_p] = torch.from_numpy(re).to(DEV)
+    y2 = _np(M.expert_down_fp8(aq2, ae2, perm, offsets, wqd["wd_q"], wqd["wd_e"],
+                               cfg.k)[torch.from_numpy(picks).to(DEV)]).astype(np.float64)
+    worst_rel = 0.0
+    for i in range(len(picks)):
+        e = loc[i]
+        tg = gemm_tol(x_deq[i], deq(wq["wgq"][e], wq["wge"][e], B))
+        tu = gemm_tol(x_deq[i], deq(wq["wuq"][e], wq["wue"][e], B))
+        absb, rel = _act_bound(g[i], u[i], tg, tu, ar[i])
+        lim = absb + rel * np.maximum(np.abs(ag[i]), np.abs(ar[i])) + 1e-30
+        assert np.all(np.abs(ag[i] - ar[i]) <= lim), i
+        a_deq = deq(rq[i:i + 1], re[i:i + 1], 1)[0]
+        tol = gemm_tol(a_deq, deq(wq["wdq"][e], wq["wde"][e], B))
+        assert np.all(np.abs(y2[i] - y_ref[i]) <= tol), i
+        # end to end (own act codes): within the norm-wise bar of the layer
+        rel_y = np.linalg.norm(y_gpu[i] - y_ref[i]) / np.linalg.norm(y_ref[i])
+        assert rel_y <= 2.0 ** -7, (i, rel_y)
+        worst_rel = max(worst_rel, rel_y)
+    log(f"[fp8] large sampled: {len(picks)} assignments of experts {uniq.tolist()}; weight "
+        f"codes bit-exact; act within bound ({float(np.mean(act_gpu == act_ref)):.4f} "
+        f"bit-identical); down GEMM on the oracle's codes within its bound; end-to-end y "
+        f"worst rel {worst_rel:.2e}")
