@@ -14,6 +14,9 @@ namespace moe {
 
 namespace {
 
+// All k loads of a thread are issued before its fma chain (KMAX >= k slots,
+// unrolled), so each thread keeps k 16-byte loads in flight.
+template <int KMAX>
 __global__ __launch_bounds__(256) void combine_kernel(int T, int H4, int k,
                                                       const float4* __restrict__ y,
                                                       const float* __restrict__ w,
@@ -24,14 +27,27 @@ __global__ __launch_bounds__(256) void combine_kernel(int T, int H4, int k,
     const int h4 = (int)(idx - (long)t * H4);
     const float4* yt = y + (size_t)t * k * H4 + h4;
     const float* wt = w + (size_t)t * k;
+    float4 v[KMAX];
+    float wj[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+        if (j < k) {
+            typedef float f4v __attribute__((ext_vector_type(4)));
+            const f4v r = __builtin_nontemporal_load(
+                reinterpret_cast<const f4v*>(yt + (size_t)j * H4));
+            v[j] = make_float4(r.x, r.y, r.z, r.w);
+            wj[j] = wt[j];
+        }
+    }
     float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
-    for (int j = 0; j < k; ++j) {
-        const float wj = wt[j];
-        const float4 v = yt[(size_t)j * H4];
-        a0 = __builtin_fmaf(wj, v.x, a0);
-        a1 = __builtin_fmaf(wj, v.y, a1);
-        a2 = __builtin_fmaf(wj, v.z, a2);
-        a3 = __builtin_fmaf(wj, v.w, a3);
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+        if (j < k) {
+            a0 = __builtin_fmaf(wj[j], v[j].x, a0);
+            a1 = __builtin_fmaf(wj[j], v[j].y, a1);
+            a2 = __builtin_fmaf(wj[j], v[j].z, a2);
+            a3 = __builtin_fmaf(wj[j], v[j].w, a3);
+        }
     }
     uint2 o;
     o.x = f32_to_bf16_rne(a0) | (f32_to_bf16_rne(a1) << 16);
@@ -62,8 +78,12 @@ hipError_t launch_combine(int T, int H, int k, const float* y, const float* w, u
     const int H4 = H / 4;
     const long n = (long)T * H4;
     const int blocks = (int)((n + 255) / 256);
-    combine_kernel<<<blocks, 256, 0, s>>>(T, H4, k, reinterpret_cast<const float4*>(y), w,
-                                          reinterpret_cast<uint2*>(out));
+    const float4* y4 = reinterpret_cast<const float4*>(y);
+    uint2* o2 = reinterpret_cast<uint2*>(out);
+    if (k <= 8)
+        combine_kernel<8><<<blocks, 256, 0, s>>>(T, H4, k, y4, w, o2);
+    else
+        combine_kernel<16><<<blocks, 256, 0, s>>>(T, H4, k, y4, w, o2);
     return hipGetLastError();
 }
 

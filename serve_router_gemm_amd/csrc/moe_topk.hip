@@ -10,7 +10,8 @@
 // index).  It is a total order on (score, index), so the result is one
 // well-defined list whatever the thread schedule.
 //
-// One 1024-thread block per row.  With n > k valid scores:
+// One 1024-thread block per row; each thread loads 16 scores of a batch
+// before using them.  With n > k valid scores:
 //   1. radix select on the 32-bit order-preserving code, 8 bits per pass from
 //      the top (LDS histograms, integer counts): the code c* of the k-th
 //      element and kk, how many elements equal to c* are taken;
@@ -29,14 +30,16 @@ namespace {
 
 constexpr int kTkThreads = 1024;
 constexpr int kTkWaves = kTkThreads / kWave;
+constexpr int kTkU = 16;   // scores per thread per batch: element base + u * 1024 + tid
+constexpr int kTkBatch = kTkThreads * kTkU;
 
 __global__ __launch_bounds__(kTkThreads) void topk_large_kernel(
     int N, int k, const float* __restrict__ scores, const int32_t* __restrict__ lengths,
     int32_t* __restrict__ idx, float* __restrict__ vals) {
     __shared__ uint64_t rk[kMaxTopkLarge];
     __shared__ int hist[256];
-    __shared__ int wsum[kTkWaves];
-    __shared__ int s_bin, s_above, s_fill, s_run, s_done;
+    __shared__ int ucnt[kTkU * kTkWaves];   // equal-to-c* counts per (u, wave), then their prefix
+    __shared__ int s_bin, s_above, s_fill, s_run, s_done, s_tot;
 
     const int q = blockIdx.x;
     const int tid = threadIdx.x;
@@ -60,15 +63,26 @@ __global__ __launch_bounds__(kTkThreads) void topk_large_kernel(
         }
     } else {
         // 1. radix select: prefix/mask describe the code bits fixed so far,
-        //    need = how many of the elements matching them are still wanted
+        //    need = how many of the elements matching them are still wanted.
+        //    Each thread loads its kTkU scores of a batch before using them.
         uint32_t prefix = 0, mask = 0;
         int need = k;
         for (int shift = 24; shift >= 0; shift -= 8) {
             for (int b = tid; b < 256; b += kTkThreads) hist[b] = 0;
             __syncthreads();
-            for (int i = tid; i < n; i += kTkThreads) {
-                const uint32_t c = key_code(row[i]);
-                if ((c & mask) == prefix) atomicAdd(&hist[(c >> shift) & 255u], 1);
+            for (int base = 0; base < n; base += kTkBatch) {
+                float v[kTkU];
+#pragma unroll
+                for (int u = 0; u < kTkU; ++u) {
+                    const int i = base + u * kTkThreads + tid;
+                    v[u] = i < n ? row[i] : 0.0f;
+                }
+#pragma unroll
+                for (int u = 0; u < kTkU; ++u) {
+                    const int i = base + u * kTkThreads + tid;
+                    const uint32_t c = key_code(v[u]);
+                    if (i < n && (c & mask) == prefix) atomicAdd(&hist[(c >> shift) & 255u], 1);
+                }
             }
             __syncthreads();
             if (tid == 0) {
@@ -88,37 +102,80 @@ __global__ __launch_bounds__(kTkThreads) void topk_large_kernel(
         }
         const uint32_t cstar = prefix;   // the k-th element's code; take `need` of them
         // 2. elements above c* (any slot order), then the `need` lowest
-        //    indices equal to c*, in index order, after them
+        //    indices equal to c*, in index order, after them.  Index order in
+        //    a batch is (u, wave, lane): an element's rank among the equal ones
+        //    is the prefix of the per-(u, wave) counts plus its lane prefix.
         if (tid == 0) s_run = 0;
         __syncthreads();
         const int base_eq = k - need;
-        for (int i0 = 0; i0 < n; i0 += kTkThreads) {
-            const int i = i0 + tid;
-            uint32_t c = 0;
-            if (i < n) c = key_code(row[i]);
-            if (i < n && c > cstar) {
-                const int pos = atomicAdd(&s_fill, 1);
-                rk[pos] = ((uint64_t)c << 32) | (uint32_t)(~(uint32_t)i);
+        for (int base = 0; base < n; base += kTkBatch) {
+            float v[kTkU];
+#pragma unroll
+            for (int u = 0; u < kTkU; ++u) {
+                const int i = base + u * kTkThreads + tid;
+                v[u] = i < n ? row[i] : 0.0f;
             }
-            const bool eq = (i < n) && (c == cstar);
-            const uint64_t bal = __ballot(eq);
-            const int before_lane = __popcll(bal & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
-            if (lane == 0) wsum[wave] = __popcll(bal);
+            uint32_t eqbits = 0;
+            int lpre[kTkU];
+#pragma unroll
+            for (int u = 0; u < kTkU; ++u) {
+                const int i = base + u * kTkThreads + tid;
+                const uint32_t c = key_code(v[u]);
+                const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+                // elements above c*: one slot claim per wave
+                const bool up = (i < n) && (c > cstar);
+                const uint64_t ubal = __ballot(up);
+                if (ubal) {
+                    int slot0 = 0;
+                    if (lane == 0) slot0 = atomicAdd(&s_fill, __popcll(ubal));
+                    slot0 = __shfl(slot0, 0, kWave);
+                    if (up) rk[slot0 + __popcll(ubal & below)] =
+                        ((uint64_t)c << 32) | (uint32_t)(~(uint32_t)i);
+                }
+                const bool eq = (i < n) && (c == cstar);
+                const uint64_t bal = __ballot(eq);
+                lpre[u] = __popcll(bal & below);
+                if (lane == 0) ucnt[u * kTkWaves + wave] = __popcll(bal);
+                eqbits |= (eq ? 1u : 0u) << u;
+            }
             __syncthreads();
-            int before_wave = 0;
-            for (int w = 0; w < wave; ++w) before_wave += wsum[w];
+            if (wave == 0) {
+                // exclusive prefix of the 256 counts in (u, wave) order: lane
+                // l holds entries 4l .. 4l + 3
+                const int c0 = ucnt[4 * lane], c1 = ucnt[4 * lane + 1];
+                const int c2 = ucnt[4 * lane + 2], c3 = ucnt[4 * lane + 3];
+                const int sum = c0 + c1 + c2 + c3;
+                int incl = sum;
+#pragma unroll
+                for (int d = 1; d < kWave; d <<= 1) {
+                    const int t = __shfl_up(incl, d, kWave);
+                    if (lane >= d) incl += t;
+                }
+                const int ex = incl - sum;
+                ucnt[4 * lane] = ex;
+                ucnt[4 * lane + 1] = ex + c0;
+                ucnt[4 * lane + 2] = ex + c0 + c1;
+                ucnt[4 * lane + 3] = ex + c0 + c1 + c2;
+                if (lane == kWave - 1) s_tot = incl;
+            }
+            __syncthreads();
             const int run = s_run;
-            const int r = run + before_wave + before_lane;
-            if (eq && r < need) rk[base_eq + r] = ((uint64_t)c << 32) | (uint32_t)(~(uint32_t)i);
+#pragma unroll
+            for (int u = 0; u < kTkU; ++u) {
+                if (eqbits & (1u << u)) {
+                    const int r = run + ucnt[u * kTkWaves + wave] + lpre[u];
+                    const int i = base + u * kTkThreads + tid;
+                    if (r < need)
+                        rk[base_eq + r] = ((uint64_t)cstar << 32) | (uint32_t)(~(uint32_t)i);
+                }
+            }
             __syncthreads();
-            // One thread decides whether both parts are complete; s_fill is
-            // final for this pass of the loop here (its atomics came before
-            // the barrier above), and the decision is read by all after the
+            // One thread decides whether both parts are complete: s_fill and
+            // s_tot are final for this batch here (their writes came before
+            // the barriers above), and the decision is read by all after the
             // next barrier, before anyone can change it again.
             if (tid == 0) {
-                int tot = 0;
-                for (int w = 0; w < kTkWaves; ++w) tot += wsum[w];
-                s_run = run + tot;
+                s_run = run + s_tot;
                 s_done = (s_run >= need && s_fill >= base_eq) ? 1 : 0;
             }
             __syncthreads();
