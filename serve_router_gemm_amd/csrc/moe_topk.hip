@@ -11,7 +11,11 @@
 // well-defined list whatever the thread schedule.
 //
 // One 1024-thread block per row; each thread loads 16 scores of a batch
-// before using them.  With n > k valid scores:
+// before using them.  With n > k valid scores, a histogram of the top 11
+// code bits first finds the bin that holds the k-th element; when that bin
+// and the ones above it hold at most 4096 elements (no heavy ties), a second
+// read collects them and one sort of their ranks gives the list (two reads
+// of the row).  Otherwise:
 //   1. radix select on the 32-bit order-preserving code, 8 bits per pass from
 //      the top (LDS histograms, integer counts): the code c* of the k-th
 //      element and kk, how many elements equal to c* are taken;
@@ -33,13 +37,34 @@ constexpr int kTkWaves = kTkThreads / kWave;
 constexpr int kTkU = 16;   // scores per thread per batch: element base + u * 1024 + tid
 constexpr int kTkBatch = kTkThreads * kTkU;
 
+constexpr int kTkTopBits = 11;                 // first pass: histogram of the top 11 code bits
+constexpr int kTkTopBins = 1 << kTkTopBits;
+constexpr int kTkTopShift = 32 - kTkTopBits;
+
+// bitonic sort of rk[0..kp) descending (kp a power of two; zeros sink)
+__device__ __forceinline__ void sort_ranks_desc(uint64_t* rk, int kp, int tid) {
+    for (int size = 2; size <= kp; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int t = tid; t < kp / 2; t += kTkThreads) {
+                const int i = 2 * stride * (t / stride) + (t % stride);
+                const int j = i + stride;
+                const uint64_t a = rk[i], b = rk[j];
+                const bool desc = (i & size) == 0;
+                if (desc ? (a < b) : (a > b)) { rk[i] = b; rk[j] = a; }
+            }
+            __syncthreads();
+        }
+    }
+}
+
 __global__ __launch_bounds__(kTkThreads) void topk_large_kernel(
     int N, int k, const float* __restrict__ scores, const int32_t* __restrict__ lengths,
     int32_t* __restrict__ idx, float* __restrict__ vals) {
     __shared__ uint64_t rk[kMaxTopkLarge];
     __shared__ int hist[256];
     __shared__ int ucnt[kTkU * kTkWaves];   // equal-to-c* counts per (u, wave), then their prefix
-    __shared__ int s_bin, s_above, s_fill, s_run, s_done, s_tot;
+    __shared__ int s_bin, s_above, s_fill, s_run, s_done, s_tot, s_cand;
+    __shared__ int thist[kTkTopBins];
 
     const int q = blockIdx.x;
     const int tid = threadIdx.x;
@@ -50,13 +75,90 @@ __global__ __launch_bounds__(kTkThreads) void topk_large_kernel(
     n = n < 0 ? 0 : (n > N ? N : n);
     const int take = min(k, n);
     int kp = 1;
-    while (kp < take) kp <<= 1;
 
+    // Two reads of the row when they suffice: a histogram of the top 11 code
+    // bits finds the bin b1 where the count from the top reaches k; every
+    // element in b1 or above is a candidate (at least k of them, the top k
+    // among them), and when they fit in rk one sort of their 64-bit ranks
+    // gives the list.  Otherwise (heavy ties) the radix select below runs.
+    bool fast = false;
+    if (n > k) {
+        for (int b = tid; b < kTkTopBins; b += kTkThreads) thist[b] = 0;
+        __syncthreads();
+        for (int base = 0; base < n; base += kTkBatch) {
+            float v[kTkU];
+#pragma unroll
+            for (int u = 0; u < kTkU; ++u) {
+                const int i = base + u * kTkThreads + tid;
+                v[u] = i < n ? row[i] : 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < kTkU; ++u) {
+                const int i = base + u * kTkThreads + tid;
+                if (i < n) atomicAdd(&thist[key_code(v[u]) >> kTkTopShift], 1);
+            }
+        }
+        __syncthreads();
+        if (wave == 0) {
+            // lane l: bins [32l, 32l + 32); suffix sums over lanes find the
+            // group holding the k-th element, one lane scans inside it
+            int g = 0;
+            for (int j = 0; j < kTkTopBins / kWave; ++j) g += thist[lane * (kTkTopBins / kWave) + j];
+            int suf = g;
+#pragma unroll
+            for (int d = 1; d < kWave; d <<= 1) {
+                const int t = __shfl_down(suf, d, kWave);
+                if (lane + d < kWave) suf += t;
+            }
+            const uint64_t reach = __ballot(suf >= k);          // non-increasing in lane
+            const int L = 63 - __clzll((long long)reach);
+            const int above_groups = __shfl(suf - g, L, kWave);  // elements in groups > L
+            if (lane == L) {
+                int above = above_groups, b = L * (kTkTopBins / kWave) + (kTkTopBins / kWave) - 1;
+                for (; b > L * (kTkTopBins / kWave); --b) {
+                    if (above + thist[b] >= k) break;
+                    above += thist[b];
+                }
+                s_bin = b;
+                s_cand = above + thist[b];
+            }
+        }
+        __syncthreads();
+        fast = s_cand <= kMaxTopkLarge;
+    }
+    const int nrank = fast ? s_cand : take;     // entries sorted
+    kp = 1;
+    while (kp < nrank) kp <<= 1;
     for (int i = tid; i < kp; i += kTkThreads) rk[i] = 0;
     if (tid == 0) s_fill = 0;
     __syncthreads();
 
-    if (n <= k) {
+    if (fast) {
+        const uint32_t b1 = (uint32_t)s_bin;
+        for (int base = 0; base < n; base += kTkBatch) {
+            float v[kTkU];
+#pragma unroll
+            for (int u = 0; u < kTkU; ++u) {
+                const int i = base + u * kTkThreads + tid;
+                v[u] = i < n ? row[i] : 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < kTkU; ++u) {
+                const int i = base + u * kTkThreads + tid;
+                const uint32_t c = key_code(v[u]);
+                const bool cand = i < n && (c >> kTkTopShift) >= b1;
+                const uint64_t bal = __ballot(cand);
+                if (bal) {
+                    int slot0 = 0;
+                    if (lane == 0) slot0 = atomicAdd(&s_fill, __popcll(bal));
+                    slot0 = __shfl(slot0, 0, kWave);
+                    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+                    if (cand) rk[slot0 + __popcll(bal & below)] =
+                        ((uint64_t)c << 32) | (uint32_t)(~(uint32_t)i);
+                }
+            }
+        }
+    } else if (n <= k) {
         for (int i = tid; i < n; i += kTkThreads) {
             const int pos = atomicAdd(&s_fill, 1);
             rk[pos] = sel_rank(row[i], i);
@@ -184,19 +286,8 @@ __global__ __launch_bounds__(kTkThreads) void topk_large_kernel(
     }
     __syncthreads();
 
-    // 3. bitonic sort of rk[0..kp) descending (zeros, the padding, sink)
-    for (int size = 2; size <= kp; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int t = tid; t < kp / 2; t += kTkThreads) {
-                const int i = 2 * stride * (t / stride) + (t % stride);
-                const int j = i + stride;
-                const uint64_t a = rk[i], b = rk[j];
-                const bool desc = (i & size) == 0;
-                if (desc ? (a < b) : (a > b)) { rk[i] = b; rk[j] = a; }
-            }
-            __syncthreads();
-        }
-    }
+    // 3. sort rk[0..kp) descending (zeros, the padding, sink)
+    sort_ranks_desc(rk, kp, tid);
 
     for (int j = tid; j < k; j += kTkThreads) {
         int v = -1;

@@ -49,6 +49,37 @@ def test_topk_large_equals_oracle(Q, N, k, levels):
     _check(_rows(Q, N, levels, N + k), k)
 
 
+def _randn_rows(Q, N, seed):
+    return np.random.default_rng(seed).standard_normal((Q, N)).astype(np.float32)
+
+
+@pytest.mark.parametrize("Q,N,k", [(4, 131072, 2048), (3, 20000, 4096), (5, 3000, 100),
+                                   (2, 70000, 1), (3, 4097, 4096)])
+def test_topk_large_continuous_scores(Q, N, k):
+    """Continuous scores: the two-read path (the bin of the k-th element and
+    those above it hold few elements)."""
+    _check(_randn_rows(Q, N, N + k), k)
+
+
+def test_topk_large_candidates_at_capacity():
+    """The two-read path at its capacity: 4096 equal top scores (all of them
+    candidates, the top 2048 taken by index) and 4097 (the radix path)."""
+    N, k = 50000, 2048
+    rng = np.random.default_rng(4)
+    s = rng.uniform(-1, 1, (2, N)).astype(np.float32)
+    for q, m in ((0, 4096), (1, 4097)):
+        s[q, rng.choice(N, m, replace=False)] = 3.0
+    gi = _check(s, k)
+    assert np.all(np.diff(gi[0]) > 0)              # equal scores: ascending indices
+
+
+def test_topk_large_continuous_causal():
+    Q, N, k = 8, 9000, 2048
+    s = _randn_rows(Q, N, 77)
+    lengths = np.array([0, 5, 2048, 2049, 4000, 8999, 9000, 6000], dtype=np.int32)
+    _check(s, k, lengths)
+
+
 def test_topk_large_causal_lengths():
     Q, N, k = 16, 9000, 2048
     s = _rows(Q, N, 300, 5)
