@@ -86,12 +86,20 @@ def test_quantize_blocks_are_scaled_e4m3():
     assert ea[5, 0] == O.fp8_block_exp(3.0)
 
 
+def _block_scales(rows, cols, seed):
+    """A different power of two per 128 x 128 block, so that every block has
+    its own exponent and a mis-indexed exponent shows."""
+    rng = np.random.default_rng(seed)
+    f = 2.0 ** rng.integers(-4, 5, size=(rows // 128, cols // 128))
+    return torch.from_numpy(np.repeat(np.repeat(f, 128, axis=0), 128, axis=1)).float()
+
+
 def _fp8_layer(T=6, H=256, F=384, E=3, seed=2):
     g = torch.Generator().manual_seed(seed)
-    x = torch.randn((T, H), generator=g).to(torch.bfloat16)
-    wg = (torch.randn((E, F, H), generator=g) * 0.05).to(torch.bfloat16)
-    wu = (torch.randn((E, F, H), generator=g) * 0.05).to(torch.bfloat16)
-    wd = (torch.randn((E, H, F), generator=g) * 0.05).to(torch.bfloat16)
+    x = (torch.randn((T, H), generator=g) * _block_scales(128, H, seed)[0]).to(torch.bfloat16)
+    wg = (torch.randn((E, F, H), generator=g) * 0.05 * _block_scales(F, H, seed + 1)).to(torch.bfloat16)
+    wu = (torch.randn((E, F, H), generator=g) * 0.05 * _block_scales(F, H, seed + 2)).to(torch.bfloat16)
+    wd = (torch.randn((E, H, F), generator=g) * 0.05 * _block_scales(H, F, seed + 3)).to(torch.bfloat16)
     xq, xe = O.quantize_fp8(bits(x), 1)
     wq = {}
     wq["wgq"], wq["wge"] = O.quantize_fp8(bits(wg), 128)
@@ -218,10 +226,13 @@ def test_fp8_gemm_alone_against_library_matmul():
     order: equal bit for bit."""
     rng = np.random.default_rng(11)
     n, K, N, E = 7, 384, 256, 3
-    a = (rng.standard_normal((n, K)) * rng.choice([1e-3, 1.0, 30.0], (n, 1))).astype(np.float32)
-    w = (rng.standard_normal((E, N, K)) * 0.02).astype(np.float32)
+    a = (rng.standard_normal((n, K)) * rng.choice([1e-3, 1.0, 30.0], (n, 1)) *
+         np.repeat(2.0 ** rng.integers(-4, 5, size=(n, K // 128)), 128, axis=1)).astype(np.float32)
+    w = (rng.standard_normal((E, N, K)) * 0.02 *
+         np.stack([_block_scales(N, K, 20 + e).numpy() for e in range(E)])).astype(np.float32)
     aq, ae = O.quantize_fp8(O.f32_to_bf16(a), 1)
     wq, we = O.quantize_fp8(O.f32_to_bf16(w), 128)
+    assert len(np.unique(we)) > 4 and len(np.unique(ae)) > 4       # blocks differ
     experts = rng.integers(0, E, n)
     y = O.fp8_gemm(aq, ae, experts, wq, we)
     a_deq = _deq(aq, ae, 1)
@@ -246,3 +257,20 @@ def test_fp8_gemm_alone_exact_on_small_integers():
     y2 = O.fp8_gemm(O.f32_to_e4m3(ai), np.full((n, 2), 3, np.int8), np.zeros(n),
                     O.f32_to_e4m3(wi), np.full((1, 1, 2), -5, np.int8))
     assert np.array_equal(y2, y * np.float32(2.0 ** -2))
+
+
+def test_fp8_ffn_gate_up_equals_the_gemm():
+    """The FFN's act is bf16(silu(g) * u) of the block-scaled GEMM (pinned on
+    its own above) applied to the gate and up weights, every weight block with
+    its own exponent: a mis-indexed gate or up exponent shows here."""
+    x, wg, wu, wd, xq, xe, wq = _fp8_layer()
+    T, E = x.shape[0], wg.shape[0]
+    assert len(np.unique(wq["wge"])) > 4 and len(np.unique(wq["wue"])) > 4
+    toks = np.repeat(np.arange(T), E)
+    exps = np.tile(np.arange(E), T)
+    _, act = O.expert_ffn_fp8(toks, exps, xq, xe, wq["wgq"], wq["wge"], wq["wuq"], wq["wue"],
+                              wq["wdq"], wq["wde"], want_act=True)
+    g = O.fp8_gemm(xq[toks], xe[toks], exps, wq["wgq"], wq["wge"]).astype(np.float64)
+    u = O.fp8_gemm(xq[toks], xe[toks], exps, wq["wuq"], wq["wue"]).astype(np.float64)
+    ref = O.f32_to_bf16((g / (1.0 + np.exp(-g)) * u).astype(np.float32))
+    assert np.array_equal(act, ref)
