@@ -119,6 +119,21 @@ def test_log_softmax_sum_order_is_chunked():
     assert abs(got_S - float(s_chunk)) < abs(got_S - float(s_single))
 
 
+def test_log_softmax_chunks_are_added_in_ascending_order():
+    """Chunk sums 1, t, t with t about 0.7 ulp of 1: added in ascending chunk
+    order S = (1 + t) + t = 1 + 2 ulp, in descending order (t + t) + 1 =
+    1 + 1 ulp."""
+    V = 768
+    ulp = 2.0 ** -23
+    z = np.full((1, V), -np.inf, dtype=np.float32)
+    z[0, 0] = 0.0
+    z[0, 256] = z[0, 512] = np.float32(math.log(0.7 * ulp))
+    logp = O.log_softmax(z)
+    asc = -math.log(1.0 + 2 * ulp)
+    desc = -math.log(1.0 + ulp)
+    assert abs(float(logp[0, 0]) - asc) < abs(float(logp[0, 0]) - desc)
+
+
 def _rows(seed, V, scale):
     rng = np.random.default_rng(seed)
     return (rng.standard_normal((3, V)) * scale).astype(np.float32)
@@ -164,3 +179,20 @@ def test_k3_greedy_tie_takes_lowest_index():
     ref = np.log(np.array([[0.25, 0.25, 0.25, 0.25]], dtype=np.float32))
     _, _, g = O.k3(ref, test)
     assert g[0] == 1
+
+
+def test_k3_near_identical_rows_against_the_series():
+    """Rows a few ulps apart: each term expm1(d) - d equals the series
+    d^2/2 + d^3/6 + d^4/24 to fp64 precision (|d| < 1e-5), which an
+    evaluation as exp(d) - 1 - d would miss by cancellation."""
+    test = O.log_softmax(_rows(3, 4096, 1.0))
+    rng = np.random.default_rng(6)
+    ref = (test.astype(np.float64) * (1.0 + rng.uniform(-3e-7, 3e-7, test.shape))).astype(np.float32)
+    mean, gk3, g = O.k3(ref, test)
+    d = ref.astype(np.float64) - test.astype(np.float64)
+    assert np.abs(d).max() < 1e-5 and np.any(d != 0)
+    series = d * d / 2 + d ** 3 / 6 + d ** 4 / 24
+    lib = (np.exp(test.astype(np.float64)) * series).sum(axis=-1)
+    assert np.allclose(mean, lib, rtol=1e-9, atol=0)
+    for t in range(3):
+        assert math.isclose(gk3[t], series[t, g[t]], rel_tol=1e-9, abs_tol=1e-300)

@@ -64,6 +64,9 @@ def test_replay_weights_match_fp64_library_for_routed_and_random_ids():
     for renorm in (True, False):
         w_r = O.replay_weights(xb, wrb, rid, O.SIGMOID, renorm)
         assert np.all(_ulps(w_r, _np_weights(logits, rid, O.SIGMOID, renorm)) <= 1)
+        # softmax without renormalisation: the probability over all E experts
+        w_s = O.replay_weights(xb, wrb, rid, O.SOFTMAX, renorm)
+        assert np.all(_ulps(w_s, _np_weights(logits, rid, O.SOFTMAX, renorm)) <= 1)
 
 
 def test_replay_invalid_ids_get_no_weight_and_no_output():
@@ -77,11 +80,26 @@ def test_replay_invalid_ids_get_no_weight_and_no_output():
     ids[::3, 1] = -1
     ids[1::3, 0] = cfg.E + 5
     ids[2, :] = -7                                 # a token with no valid expert
+    invalid = (ids < 0) | (ids >= cfg.E)
+    for score, renorm in ((O.SIGMOID, True), (O.SIGMOID, False), (O.SOFTMAX, False)):
+        w_s = O.replay_weights(xb, hb["w_router"], ids, score, renorm)
+        assert np.all(_ulps(w_s, _np_weights(logits, ids, score, renorm)) <= 1)
+        assert np.all(w_s[invalid] == 0.0)
     out, w = O.forward_replay(xb, hb["w_router"], ids, hb["w_gate"], hb["w_up"], hb["w_down"],
                               O.SOFTMAX, True)
     assert np.all(_ulps(w, _np_weights(logits, ids, O.SOFTMAX, True)) <= 1)
-    assert np.all(w[(ids < 0) | (ids >= cfg.E)] == 0.0)
+    assert np.all(w[invalid] == 0.0)
     assert np.all(out[2] == 0)                     # bf16 +0
+    # recorded weights: an invalid id's expert output is 0 whatever its weight,
+    # so the out equals that of the same weights with those slots zeroed
+    wrec = np.random.default_rng(4).uniform(0.1, 1.0, size=ids.shape).astype(np.float32)
+    out_rec, _ = O.forward_replay(xb, hb["w_router"], ids, hb["w_gate"], hb["w_up"],
+                                  hb["w_down"], O.SOFTMAX, True, w=wrec)
+    wz = np.where(invalid, np.float32(0), wrec)
+    out_z, _ = O.forward_replay(xb, hb["w_router"], ids, hb["w_gate"], hb["w_up"], hb["w_down"],
+                                O.SOFTMAX, True, w=wz)
+    assert np.array_equal(out_rec, out_z)
+    assert np.all(out_rec[2] == 0)
     # a token with one valid slot of weight 1 equals that expert alone (k = 1)
     t = 0
     j = int(np.nonzero((ids[t] >= 0) & (ids[t] < cfg.E))[0][0])

@@ -15,7 +15,7 @@ def np_topk(scores, k, lengths=None):
     Q, N = scores.shape
     idx = np.full((Q, k), -1, dtype=np.int32)
     for q in range(Q):
-        n = N if lengths is None else int(lengths[q])
+        n = N if lengths is None else min(max(int(lengths[q]), 0), N)   # clamped to [0, N]
         row = scores[q, :n].astype(np.float64) + 0.0          # -0 -> +0
         nan = np.isnan(row)
         val = np.where(nan, 0.0, row)
@@ -50,10 +50,10 @@ def test_topk_large_row_lengths_and_padding():
     rng = np.random.default_rng(2)
     Q, N, k = 8, 3000, 2048
     s = rng.standard_normal((Q, N)).astype(np.float32)
-    lengths = np.array([0, 1, 5, 2047, 2048, 2049, 3000, 1500], dtype=np.int32)
+    lengths = np.array([0, 1, -1, 2047, 2048, 2049, 3000, -100], dtype=np.int32)
     idx, vals = O.topk_large(s, k, lengths)
     assert np.array_equal(idx, np_topk(s, k, lengths))
-    for q, n in enumerate(lengths):
+    for q, n in enumerate(np.maximum(lengths, 0)):
         assert np.all(idx[q, min(k, n):] == -1)
         assert np.all(np.isnan(vals[q, min(k, n):]))
         assert np.all(idx[q, :min(k, n)] < n)
