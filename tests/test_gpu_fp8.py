@@ -102,8 +102,13 @@ def _routing(cfg, L, x):
     return ids, w, offsets, perm
 
 
-@pytest.mark.parametrize("shape", [dict(), dict(T=37, H=256, F=384, E=5, k=3)],
-                         ids=["T300_H384_F640", "T37_H256_F384"])
+EDGE = [dict(T=1, H=128, F=128, E=1, k=1), dict(T=5, H=8192, F=256, E=2, k=1),
+        dict(T=5, H=256, F=8192, E=2, k=2), dict(T=40, H=256, F=256, E=512, k=16)]
+EDGE_IDS = ["T1_H128_F128_E1_k1", "Hmax8192", "Fmax8192", "E512_k16"]
+
+
+@pytest.mark.parametrize("shape", [dict(), dict(T=37, H=256, F=384, E=5, k=3)] + EDGE,
+                         ids=["T300_H384_F640", "T37_H256_F384"] + EDGE_IDS)
 def test_down_fp8_within_bound(shape):
     cfg = fp8_cfg(**shape)
     L = layer(cfg)
@@ -153,8 +158,8 @@ def _act_bound(g, u, tg, tu, act_ref):
     return 1.1 * (np.abs(u) + tu) * tg + (np.abs(silu) + 1.1 * tg) * tu, 2.0 ** -8
 
 
-@pytest.mark.parametrize("shape", [dict(), dict(T=37, H=256, F=384, E=5, k=3)],
-                         ids=["T300_H384_F640", "T37_H256_F384"])
+@pytest.mark.parametrize("shape", [dict(), dict(T=37, H=256, F=384, E=5, k=3)] + EDGE,
+                         ids=["T300_H384_F640", "T37_H256_F384"] + EDGE_IDS)
 def test_gate_up_fp8_within_bound(shape):
     cfg = fp8_cfg(**shape)
     L, x, ids, w, offsets, perm, xq, xe, wqd, aq, ae, ab = _gate_up_case(cfg)
@@ -358,3 +363,12 @@ def test_large_fp8_sampled():
         f"codes bit-exact; act within bound ({float(np.mean(act_gpu == act_ref)):.4f} "
         f"bit-identical); down GEMM on the oracle's codes within its bound; end-to-end y "
         f"worst rel {worst_rel:.2e}")
+
+
+def test_forward_fp8_empty_batch():
+    cfg = fp8_cfg()
+    L = layer(cfg)
+    wqd = M.quantize_weights_fp8(L["w_gate"], L["w_up"], L["w_down"])
+    x = torch.empty((0, cfg.H), dtype=torch.bfloat16, device=DEV)
+    out = M.forward_fp8(x, L["w_router"], wqd, cfg.k, cfg.score, cfg.renorm)
+    assert out.shape == (0, cfg.H)
