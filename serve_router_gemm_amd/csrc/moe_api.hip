@@ -123,6 +123,12 @@ size_t swiglu_ws(int T, int E, int F, int top_k) {
 
 hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+int check_vocab(int T, int V) {
+    if (T < 0 || V < 1 || V > moe::kMaxVocab) return MOE_ERR_SHAPE;
+    return ((long)T * (long)V > kMaxElems) ? MOE_ERR_SHAPE : 0;
+}
+
+
 template <typename P>
 unsigned char* at(P* base, size_t off) {
     return reinterpret_cast<unsigned char*>(base) + off;
@@ -323,8 +329,6 @@ int moe_forward(int T, int H, int E, int F, int top_k, int score, int renormaliz
     return hip_rc(launch_combine(T, H, top_k, y, w, out, s));
 }
 
-}  // extern "C"
-
 int moe_forward_replay(int T, int H, int E, int F, int top_k, int score, int renormalize,
                        const uint16_t* x, const uint16_t* w_router, const int32_t* topk_ids,
                        const float* topk_w, const uint16_t* w_gate, const uint16_t* w_up,
@@ -387,13 +391,6 @@ int moe_topk_large(int Q, int N, int k, const float* scores, const int32_t* leng
 // ---------------------------------------------------------------------------
 // decode-step measurement
 // ---------------------------------------------------------------------------
-
-namespace {
-int check_vocab(int T, int V) {
-    if (T < 0 || V < 1 || V > moe::kMaxVocab) return MOE_ERR_SHAPE;
-    return ((long)T * (long)V > kMaxElems) ? MOE_ERR_SHAPE : 0;
-}
-}  // namespace
 
 int moe_lm_head_logits(int T, int H, int V, const uint16_t* h, const uint16_t* proj, float* z,
                        void* stream) {
@@ -524,3 +521,5 @@ int moe_forward_fp8(int T, int H, int E, int F, int top_k, int score, int renorm
                                         sched, s)));
     return hip_rc(launch_combine(T, H, top_k, y, w, out, s));
 }
+
+}  // extern "C"
