@@ -117,6 +117,17 @@ def test_k3_random_rows_and_edge_cases():
     _, _, g = M.k3(torch.from_numpy(r).to(DEV), torch.from_numpy(t).to(DEV))
     _, _, og = O.k3(r, t)
     assert g.cpu().tolist()[0] == 0 and og.tolist()[0] == 0
+    # ties far apart (other waves of the block) and in one thread's elements
+    V = 70000
+    t = O.log_softmax((rng.standard_normal((3, V))).astype(np.float32))
+    r = O.log_softmax((rng.standard_normal((3, V))).astype(np.float32))
+    t[0, [61000, 3000, 45000]] = 0.0           # across waves: 3000 wins
+    t[1, [2048, 1024, 3072]] = 0.0             # one thread's elements: 1024 wins
+    t[2, [7, 69999]] = 0.0
+    t[2, 5] = -0.0                              # -0 == +0: 5 wins
+    _, _, g = M.k3(torch.from_numpy(r).to(DEV), torch.from_numpy(t).to(DEV))
+    _, _, og = O.k3(r, t)
+    assert g.cpu().tolist() == [3000, 1024, 5] and og.tolist() == [3000, 1024, 5]
 
 
 def test_log_softmax_in_place_and_edge_rows():
