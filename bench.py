@@ -36,6 +36,7 @@ METRIC = "MoE-layer tokens/s + MFMA util; bitwise-identical output across batch 
 TRAFFIC = {"kernel_sha256_prefix": "e3f9d88aa238abc4", "workload": "large", "bytes": 23.10e9}
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
+PEAK_FP32_VALU_TFLOPS = 78.6  # 256 CU x 64 lanes x 2 flop x 2.4 GHz, fp32 fma without packed math
 PEAK_HBM_GBS = 8000.0
 
 
@@ -119,6 +120,10 @@ def main():
     n_probe = min(16, T)
     if T >= 16:
         x, probe_pos = I.embed_probes(probes, T, rep=0)
+    else:
+        # a batch smaller than the 16 probes: the batch is the first T probes
+        x = probes[:T].contiguous()
+        probe_pos = list(range(T))
     torch.cuda.synchronize()
     log(f"[bench] inputs ready in {time.time() - t0:.1f}s")
 
@@ -334,7 +339,7 @@ def main():
             p1 = M.forward_fp8(probes[i:i + 1].contiguous(), L["w_router"], wq8, k, cfg.score,
                                cfg.renorm, bias=bias)
             a1 = p1.view(torch.int16).cpu().numpy()[0]
-            b1 = b8[probe_pos[i]] if T >= 16 else b8[0]
+            b1 = b8[probe_pos[i]]
             nd8 += int(np.unpackbits(np.bitwise_xor(a1, b1).view(np.uint8)).sum())
         fp8_res = {"ms_per_step": round(ms8, 4), "tokens_per_s": round(T / (ms8 * 1e-3), 1),
                    "stages_ms": {n: round(v, 4) for n, v in st8.items()},
@@ -402,11 +407,15 @@ def main():
     comb_bytes = 4.0 * A * H + 4.0 * A + 2.0 * T * H
     comb_gbs = comb_bytes / (stage_ms["combine"] * 1e-3) / 1e9
 
-    # The gate/up kernel's bound: MFMA at prefill sizes; at decode sizes
-    # (T <= 64) it streams the active experts' gate and up weights from HBM.
-    if cfg.name == "dec":
-        active = int((counts.cpu().numpy() > 0).sum())
-        gu_bytes = active * 2.0 * F * H * 2 + 2.0 * T * H + 2.0 * A * F
+    # The gate/up kernel's bound is the larger of its two floors: the MFMA time
+    # of its flops and the HBM time of its algorithmic bytes (the active
+    # experts' gate and up weights + x + h_act).  MFMA at prefill sizes; at
+    # decode sizes it streams the weights.
+    active = int((counts_np > 0).sum())
+    gu_bytes = active * 2.0 * F * H * 2 + 2.0 * T * H + 2.0 * A * F
+    t_mfma = gu_flops / (PEAK_BF16_TFLOPS * 1e12)
+    t_hbm = gu_bytes / (PEAK_HBM_GBS * 1e9)
+    if t_hbm > t_mfma:
         gu_gbs = gu_bytes / (stage_ms["gate_up"] * 1e-3) / 1e9
         roofline = {"kernel": "expert_gemm_pipe_kernel<0> (moe_expert_gate_up)",
                     "bound": "hbm", "achieved": round(gu_gbs, 1), "peak": PEAK_HBM_GBS,
@@ -428,9 +437,20 @@ def main():
             o1 = M.forward(probes[i:i + 1].contiguous(), L["w_router"], L["w_gate"], L["w_up"],
                            L["w_down"], k, cfg.score, cfg.renorm, bias=bias)
             a = o1.view(torch.int16).cpu().numpy()[0]
-            b = batch_bits[probe_pos[i]] if T >= 16 else batch_bits[0]
+            b = batch_bits[probe_pos[i]]
             nd += int(np.unpackbits(np.bitwise_xor(a, b).view(np.uint8)).sum())
         inv_bits = nd
+
+    # router logits: fp32 fma chains in the pinned order (VALU; packed fp32
+    # is not used), and the bytes of x and w_router
+    r_flops = 2.0 * T * H * E
+    r_bytes = 2.0 * T * H + 2.0 * E * H
+    r_s = stage_ms["route"] * 1e-3
+    route_res = {"valu_tflops": round(r_flops / r_s / 1e12, 2),
+                 "valu_frac": round(r_flops / r_s / 1e12 / PEAK_FP32_VALU_TFLOPS, 4),
+                 "hbm_frac": round(r_bytes / r_s / 1e9 / PEAK_HBM_GBS, 4),
+                 "binds": "valu" if r_flops / (PEAK_FP32_VALU_TFLOPS * 1e12) >
+                          r_bytes / (PEAK_HBM_GBS * 1e9) else "hbm"}
 
     res = {
         "metric": METRIC,
@@ -453,6 +473,7 @@ def main():
                    "max_expert_tokens": int(counts_np.max())},
         "roofline": roofline,
         "stages_ms": {n: round(v, 4) for n, v in stage_ms.items()},
+        "route": route_res,
         "grouped_gemm_tflops": round(grouped_tflops, 2),
         "grouped_gemm_mfma_frac": round(grouped_tflops / PEAK_BF16_TFLOPS, 4),
         "combine_hbm_frac": round(comb_gbs / PEAK_HBM_GBS, 4),
