@@ -73,6 +73,62 @@ def test_topk_large_candidates_at_capacity():
     assert np.all(np.diff(gi[0]) > 0)              # equal scores: ascending indices
 
 
+def _sampled_positions(n):
+    """Positions the kernel samples for its threshold guess: 64-score chunks
+    c * stride, c < min(nch, 64), stride = nch // min(nch, 64)."""
+    nch = (n + 63) // 64
+    nsc = min(nch, 64)
+    stride = nch // nsc
+    pos = (np.arange(nsc)[:, None] * stride * 64 + np.arange(64)[None, :]).ravel()
+    return pos[pos < n]
+
+
+def test_topk_large_unrepresentative_sample():
+    """Rows whose sampled chunks mislead the threshold guess; the list must
+    still be the oracle's.  Row 0: the sampled scores are the highest of the
+    row, so the guess leaves fewer than k scores.  Row 1: 5000 large,
+    spread-out scores sit outside the sample, so the guess leaves more than
+    4096 (the exact histogram's two reads follow).  Row 2: the same with 5000
+    equal large scores (the radix path follows).  Row 3: a short row whose
+    sample is the whole row."""
+    Q, N, k = 4, 131072, 2048
+    rng = np.random.default_rng(11)
+    s = rng.standard_normal((Q, N)).astype(np.float32)
+    pos = _sampled_positions(N)
+    assert pos.size == 4096
+    s[0, pos] = (10.0 + rng.random(pos.size)).astype(np.float32)
+    rest = np.setdiff1d(np.arange(N), pos)
+    hi = rng.choice(rest, 5000, replace=False)
+    s[1, hi] = (2.0 ** rng.uniform(4, 20, hi.size)).astype(np.float32)
+    s[2, hi] = 50.0
+    lengths = np.array([N, N, N, 3000], dtype=np.int32)
+    gi = _check(s, k, lengths)
+    assert set(gi[2][:k].tolist()) <= set(hi.tolist())
+
+
+def test_topk_large_threshold_sign_subnormal_and_infinity():
+    """Rows whose k-th score, and so the collection threshold, is negative,
+    subnormal, at +-0, or at -inf with NaN below it: the threshold test on
+    floats must select what the order code selects."""
+    Q, N, k = 5, 40000, 2048
+    rng = np.random.default_rng(12)
+    s = np.empty((Q, N), dtype=np.float32)
+    s[0] = -np.abs(rng.standard_normal(N)).astype(np.float32) - 1.0      # all negative
+    s[1] = (rng.standard_normal(N) * 1e-40).astype(np.float32)           # subnormal
+    assert np.count_nonzero(np.abs(s[1]) < np.finfo(np.float32).tiny) > N // 2
+    s[2] = (-np.abs(rng.standard_normal(N)) * 1e-3).astype(np.float32)  # +-0 at the k-th
+    z = rng.choice(N, 7000, replace=False)
+    s[2, z[:4000]] = 0.0
+    s[2, z[4000:]] = -0.0
+    s[2, rng.choice(np.setdiff1d(np.arange(N), z), 1000, replace=False)] = 1.0
+    s[3] = -np.inf                                                         # -inf at the k-th
+    s[3, rng.choice(N, 1000, replace=False)] = rng.standard_normal(1000).astype(np.float32)
+    s[3, rng.choice(N, 5000, replace=False)] = np.nan
+    s[4] = np.nan                                                          # NaN at the k-th
+    s[4, rng.choice(N, 100, replace=False)] = -np.inf
+    _check(s, k)
+
+
 def test_topk_large_continuous_causal():
     Q, N, k = 8, 9000, 2048
     s = _randn_rows(Q, N, 77)
