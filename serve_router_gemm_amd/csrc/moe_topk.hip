@@ -54,31 +54,37 @@ constexpr int kTkSampleChunks = kTkWaves * kTkSampleU;   // 64 chunks of 64 scor
 
 // wave 0 only: the highest bin b of h[0..NB) whose count from the top,
 // sum over j >= b of h[j], reaches need (the total must reach it); writes
-// *bin = b and *above = the sum over j > b.  Lane l sums bins [P l, P l + P),
-// a suffix scan over the lanes finds the group, one lane scans inside it.
+// *bin = b and *above = the sum over j > b.  Lane l sums bins [P l, P l + P)
+// and a suffix scan over the lanes finds the group L; then lane j < P takes
+// bin P L + j and a second suffix scan finds the bin inside the group.
+__device__ __forceinline__ int suffix_sum_lanes(int x, int lane) {
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int t = __shfl_down(x, d, kWave);
+        if (lane + d < kWave) x += t;
+    }
+    return x;
+}
+
 template <int NB>
 __device__ __forceinline__ void find_bin_from_top(const int* h, int need, int lane, int* bin,
                                                   int* above_out) {
     constexpr int P = NB / kWave;
+    static_assert(P >= 1 && P <= kWave, "bins per lane");
     int g = 0;
 #pragma unroll
     for (int j = 0; j < P; ++j) g += h[lane * P + j];
-    int suf = g;
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const int t = __shfl_down(suf, d, kWave);
-        if (lane + d < kWave) suf += t;
-    }
+    const int suf = suffix_sum_lanes(g, lane);
     const uint64_t reach = __ballot(suf >= need);            // non-increasing in lane
     const int L = 63 - __clzll((long long)reach);
     const int above_groups = __shfl(suf - g, L, kWave);      // elements in groups > L
-    if (lane == L) {
-        int above = above_groups, b = L * P + P - 1;
-        for (; b > L * P; --b) {
-            if (above + h[b] >= need) break;
-            above += h[b];
-        }
-        *bin = b;
+    const int x = lane < P ? h[L * P + lane] : 0;
+    const int suf2 = suffix_sum_lanes(x, lane);
+    const uint64_t reach2 = __ballot(lane < P && above_groups + suf2 >= need);
+    const int j = 63 - __clzll((long long)reach2);           // lane 0 always qualifies
+    const int above = above_groups + __shfl(suf2 - x, j, kWave);
+    if (lane == 0) {
+        *bin = L * P + j;
         *above_out = above;
     }
 }
@@ -119,13 +125,11 @@ __device__ __forceinline__ float code_to_float(uint32_t c) {
 // never passes); at or below it the code itself is compared.
 constexpr uint32_t kCodeNegInf = 0x007FFFFFu;
 
-// One batch of collect_at_least: KFULL, the batch lies inside the row and
-// the row is 16-byte aligned (no per-score bounds test).
-template <bool KFLOAT, bool KFULL>
-__device__ __forceinline__ void collect_batch(const float* __restrict__ row, int n, int base,
-                                              uint32_t thr, float t, uint64_t* rk, int cap,
-                                              int* fill, int tid, int lane, bool aligned) {
-    float v[kTkU];
+// Loads of one collect batch: KFULL, the batch lies inside the row and the
+// row is 16-byte aligned (no per-score bounds test).
+template <bool KFULL>
+__device__ __forceinline__ void collect_load(const float* __restrict__ row, int n, int base, int tid,
+                                             bool aligned, float (&v)[kTkU]) {
     if (KFULL) {
 #pragma unroll
         for (int u = 0; u < kTkU / 4; ++u) {
@@ -138,6 +142,21 @@ __device__ __forceinline__ void collect_batch(const float* __restrict__ row, int
     } else {
         load_batch_vec(row, n, base, tid, aligned, v);
     }
+}
+
+// The first batch of a collect, loaded ahead of it.
+__device__ __forceinline__ void collect_preload(const float* __restrict__ row, int n, int tid,
+                                                float (&v)[kTkU]) {
+    const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
+    if (aligned && kTkBatch <= n) collect_load<true>(row, n, 0, tid, aligned, v);
+    else collect_load<false>(row, n, 0, tid, aligned, v);
+}
+
+// One batch of collect_at_least, its scores already in v.
+template <bool KFLOAT, bool KFULL>
+__device__ __forceinline__ void collect_batch(const float (&v)[kTkU], int n, int base, uint32_t thr,
+                                              float t, uint64_t* rk, int cap, int* fill, int tid,
+                                              int lane) {
     bool c[kTkU];
     uint64_t m[kTkU];
     int tot = 0;
@@ -172,18 +191,28 @@ __device__ __forceinline__ void collect_batch(const float* __restrict__ row, int
 // as (float bits << 32 | ~index) (the sort turns the bits into the code):
 // one slot claim per wave per batch, slots at or past cap counted in *fill
 // but not written.  The slot order depends on the schedule; the sort that
-// follows removes it.
+// follows removes it.  v0 holds the first batch (collect_preload).
 __device__ __forceinline__ void collect_at_least(const float* __restrict__ row, int n, uint32_t thr,
-                                                 uint64_t* rk, int cap, int* fill, int tid, int lane) {
+                                                 uint64_t* rk, int cap, int* fill, int tid, int lane,
+                                                 const float (&v0)[kTkU]) {
     const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
     const float t = code_to_float(thr);
     for (int base = 0; base < n; base += kTkBatch) {
         const bool full = aligned && base + kTkBatch <= n;
-        if (thr > kCodeNegInf) {
-            if (full) collect_batch<true, true>(row, n, base, thr, t, rk, cap, fill, tid, lane, aligned);
-            else collect_batch<true, false>(row, n, base, thr, t, rk, cap, fill, tid, lane, aligned);
+        float v[kTkU];
+        if (base == 0) {
+#pragma unroll
+            for (int u = 0; u < kTkU; ++u) v[u] = v0[u];
+        } else if (full) {
+            collect_load<true>(row, n, base, tid, aligned, v);
         } else {
-            collect_batch<false, false>(row, n, base, thr, t, rk, cap, fill, tid, lane, aligned);
+            collect_load<false>(row, n, base, tid, aligned, v);
+        }
+        if (thr > kCodeNegInf) {
+            if (full) collect_batch<true, true>(v, n, base, thr, t, rk, cap, fill, tid, lane);
+            else collect_batch<true, false>(v, n, base, thr, t, rk, cap, fill, tid, lane);
+        } else {
+            collect_batch<false, false>(v, n, base, thr, t, rk, cap, fill, tid, lane);
         }
     }
 }
@@ -304,7 +333,7 @@ void topk_large_kernel(
     __shared__ uint64_t rk[kMaxTopkLarge];
     __shared__ int hist[256];
     __shared__ int ucnt[kTkU * kTkWaves];   // equal-to-c* counts per (u, wave), then their prefix
-    __shared__ int s_bin, s_above, s_fill, s_run, s_done, s_tot;
+    __shared__ int s_bin, s_above, s_fill, s_run, s_done, s_tot, s_nsamp;
     __shared__ int thist[kTkTopBins];
 
     const int q = blockIdx.x;
@@ -320,37 +349,50 @@ void topk_large_kernel(
     bool fast = false;
     int ncand = 0;
     if (n > k && 2 * k <= kMaxTopkLarge) {
-        // Sampled threshold.  Chunk c of the sample is scores
-        // [64 c stride, 64 c stride + 64) with stride = nch / nsc, so the
-        // nsc chunks spread over the row (all of it when nch <= 64).
+        float v0[kTkU];
+        // Sampled threshold.  Sample chunk c (c < nsc) is the 64 scores of
+        // row chunk c * stride + rot, stride = nch / nsc and rot a hash of
+        // the row index mod stride: the chunks spread evenly over the row
+        // (all of it when nch <= 64), and rows whose starts are a power of
+        // two apart do not all read the same offsets at once.
         for (int b = tid; b < kTkTopBins; b += kTkThreads) thist[b] = 0;
         for (int b = tid; b < 256; b += kTkThreads) hist[b] = 0;
-        if (tid == 0) s_fill = 0;
+        if (tid == 0) {
+            s_fill = 0;
+            s_nsamp = 0;
+        }
         const int nch = (n + kWave - 1) / kWave;
         const int nsc = min(nch, kTkSampleChunks);
         const int stride = nch / nsc;
-        const int S = (nsc - 1) * kWave + min(kWave, n - (nsc - 1) * stride * kWave);
-        // The sample rank r whose code should leave about T scores of the
-        // row at or above it: T = 2k, but at least 64 samples' worth (the
-        // relative spread of the count is about 1 / sqrt(r)) and at most
-        // (k + 4096) / 2.  S, T <= 4096 and n <= 2^24: no overflow.
-        const int T = min(k + (kMaxTopkLarge - k) / 2, max(2 * k, (64 * n + S - 1) / S));
-        const int r = max(1, min(S, (T * S + n - 1) / n));
+        const int rot = (int)((((uint32_t)q * 0x9E3779B1u) >> 16) % (uint32_t)stride);
         uint32_t sc[kTkSampleU];
         uint32_t sval = 0;
 #pragma unroll
         for (int u = 0; u < kTkSampleU; ++u) {
             const int c = wave + kTkWaves * u;
-            const int i = c * stride * kWave + lane;
+            const int i = (c * stride + rot) * kWave + lane;
             const bool ok = c < nsc && i < n;
             sc[u] = ok ? key_code(row[i]) : 0u;
             sval |= (ok ? 1u : 0u) << u;
         }
+        // the first batch of the collect is loaded while the sample is used
+        collect_preload(row, n, tid, v0);
         __syncthreads();
+        int ns = 0;
 #pragma unroll
-        for (int u = 0; u < kTkSampleU; ++u)
+        for (int u = 0; u < kTkSampleU; ++u) {
             if (sval & (1u << u)) atomicAdd(&thist[sc[u] >> kTkTopShift], 1);
+            ns += __popcll(__ballot((sval >> u) & 1u));
+        }
+        if (lane == 0) atomicAdd(&s_nsamp, ns);
         __syncthreads();
+        // The sample rank r whose code should leave about T scores of the
+        // row at or above it: T = 2k, but at least 64 samples' worth (the
+        // relative spread of the count is about 1 / sqrt(r)) and at most
+        // (k + 4096) / 2.  S, T <= 4096 and n <= 2^24: no overflow.
+        const int S = s_nsamp;
+        const int T = min(k + (kMaxTopkLarge - k) / 2, max(2 * k, (64 * n + S - 1) / S));
+        const int r = max(1, min(S, (T * S + n - 1) / n));
         if (wave == 0) find_bin_from_top<kTkTopBins>(thist, r, lane, &s_bin, &s_above);
         __syncthreads();
         const uint32_t b1 = (uint32_t)s_bin;
@@ -363,7 +405,7 @@ void topk_large_kernel(
         if (wave == 0) find_bin_from_top<256>(hist, need2, lane, &s_bin, &s_above);
         __syncthreads();
         const uint32_t thr = (b1 << kTkTopShift) | ((uint32_t)s_bin << kTkSubShift);
-        collect_at_least(row, n, thr, rk, kMaxTopkLarge, &s_fill, tid, lane);
+        collect_at_least(row, n, thr, rk, kMaxTopkLarge, &s_fill, tid, lane, v0);
         __syncthreads();
         ncand = s_fill;
         fast = ncand >= k && ncand <= kMaxTopkLarge;
@@ -392,7 +434,9 @@ void topk_large_kernel(
             __syncthreads();   // every thread has read s_bin
             if (tid == 0) s_fill = 0;
             __syncthreads();
-            collect_at_least(row, n, thr, rk, kMaxTopkLarge, &s_fill, tid, lane);
+            float v0[kTkU];
+            collect_preload(row, n, tid, v0);
+            collect_at_least(row, n, thr, rk, kMaxTopkLarge, &s_fill, tid, lane, v0);
             __syncthreads();
             ncand = s_fill;    // = the histogram's count
             fast = ncand >= k && ncand <= kMaxTopkLarge;

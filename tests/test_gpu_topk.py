@@ -73,13 +73,17 @@ def test_topk_large_candidates_at_capacity():
     assert np.all(np.diff(gi[0]) > 0)              # equal scores: ascending indices
 
 
-def _sampled_positions(n):
-    """Positions the kernel samples for its threshold guess: 64-score chunks
-    c * stride, c < min(nch, 64), stride = nch // min(nch, 64)."""
+def _sampled_positions(n, q):
+    """Positions the kernel samples in row q for its threshold guess: the
+    64-score chunks c * stride + rot, c < min(nch, 64),
+    stride = nch // min(nch, 64), rot = ((q * 0x9E3779B1 mod 2^32) >> 16)
+    mod stride."""
     nch = (n + 63) // 64
     nsc = min(nch, 64)
     stride = nch // nsc
-    pos = (np.arange(nsc)[:, None] * stride * 64 + np.arange(64)[None, :]).ravel()
+    rot = (((q * 0x9E3779B1) & 0xFFFFFFFF) >> 16) % stride
+    ch = np.arange(nsc) * stride + rot
+    pos = (ch[:, None] * 64 + np.arange(64)[None, :]).ravel()
     return pos[pos < n]
 
 
@@ -94,10 +98,11 @@ def test_topk_large_unrepresentative_sample():
     Q, N, k = 4, 131072, 2048
     rng = np.random.default_rng(11)
     s = rng.standard_normal((Q, N)).astype(np.float32)
-    pos = _sampled_positions(N)
+    pos = _sampled_positions(N, 0)
     assert pos.size == 4096
     s[0, pos] = (10.0 + rng.random(pos.size)).astype(np.float32)
-    rest = np.setdiff1d(np.arange(N), pos)
+    sampled_1_2 = np.union1d(_sampled_positions(N, 1), _sampled_positions(N, 2))
+    rest = np.setdiff1d(np.arange(N), sampled_1_2)
     hi = rng.choice(rest, 5000, replace=False)
     s[1, hi] = (2.0 ** rng.uniform(4, 20, hi.size)).astype(np.float32)
     s[2, hi] = 50.0
