@@ -93,7 +93,7 @@ def main():
         calibrate_copy(args.calibrate_copy)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only (the MoE layer forward on one "
+        print("bench.py: the MoE layer runs on one GPU only (the layer forward on one "
               "MI355X); --gpus must be 1", file=sys.stderr)
         sys.exit(2)
 

@@ -507,7 +507,7 @@ int orc_forward_tokens(int n, const int32_t* tokens, int H, int E, int F, int k,
 /*
  * Bit-identical layer outputs are a means; what training and serving compare
  * is the log-probability a model assigns to the next token, and a KL
- * estimate ("k3") between two runs judged against a small threshold (the
+ * estimate ("k3") between two runs, compared with a small threshold (the
  * best2ai.com page on numerical alignment and MoE routing, sections
  * "数值差异如何扰乱学习" and "混合专家模型更难对齐").  The pages fix neither
  * the projection's order nor the sums.  Reading taken here: the same pinned
