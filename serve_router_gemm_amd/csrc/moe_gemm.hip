@@ -110,10 +110,15 @@ constexpr int kP_Issuers = MOE_ISSUERS;         // waves that issue the stage lo
 constexpr int kP_Dma = kP_Blocks / kP_Issuers;  // loads per issuing thread per stage
 constexpr int kP_WDma = kP_WBlocks / kP_Issuers;   // the first of them: weight blocks
 constexpr int kP_GateUpF = kP_W / 2;            // 128
+// A tile with at most 64 valid token rows needs 32 KB of weight rows and
+// 8 KB of token rows per step: three such stages fit where two full stages
+// do, and keep the loads of two steps in flight.
+constexpr int kP_DeepTok = 64;
+constexpr int kP_DeepStageBytes = kP_WBlocks * 1024 + (kP_DeepTok / 8) * 1024;   // 40960
+static_assert(3 * kP_DeepStageBytes <= 2 * kP_StageBytes, "three deep stages fit");
 
-template <int MODE>
-__global__ __launch_bounds__(kP_Threads) void expert_gemm_pipe_kernel(GemmParams P) {
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kP_StageBytes];
+template <int MODE, bool DEEP>
+__device__ __forceinline__ void expert_gemm_body(const GemmParams& P, unsigned char* smem) {
     const uint32_t lds0 =
         (uint32_t)(uintptr_t)((__attribute__((address_space(3))) unsigned char*)smem);
 
@@ -217,8 +222,19 @@ __global__ __launch_bounds__(kP_Threads) void expert_gemm_pipe_kernel(GemmParams
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         block_barrier();
 
+        // Stage of K step kt.  In a launch that only streams weights (DEEP),
+        // a tile with at most 64 valid rows ("deep") cycles through three
+        // 40 KB stages with the loads of two steps in flight.  Every other
+        // tile alternates two 64 KB stages, one step ahead.  Either way a
+        // stage is refilled only after the barrier that follows every wave's
+        // reads of it, and the MFMA sequence of an output element is the
+        // same.
+        const bool deep = DEEP && valid <= kP_DeepTok;
+        auto stage_off = [&](int kt) {
+            return deep ? ((kt - kt0) % 3) * kP_DeepStageBytes : ((kt - kt0) & 1) * kP_StageBytes;
+        };
         auto issue = [&](int kt) {
-            const uint32_t sbase = lds0 + (uint32_t)(((kt - kt0) & 1) * kP_StageBytes);
+            const uint32_t sbase = lds0 + (uint32_t)stage_off(kt);
             if (wave >= kP_Issuers) return;
 #pragma unroll
             for (int i = 0; i < kP_Dma; ++i) {
@@ -226,15 +242,30 @@ __global__ __launch_bounds__(kP_Threads) void expert_gemm_pipe_kernel(GemmParams
                 dma16(src[i] + (size_t)kt * kP_BK, sbase + (uint32_t)((i * kP_Issuers + iw) * 1024));
             }
         };
-        if (kt0 < kt1) issue(kt0);
+        const int ahead = deep ? 2 : 1;
+        // loads per step of this thread in a deep tile: 8 weight blocks and
+        // its token blocks below ntb (at most 8 in all)
+        const int nload =
+            wave < kP_Issuers ? kP_WDma + (ntb > iw ? 1 : 0) + (ntb > iw + 4 ? 1 : 0) : 0;
+        for (int j = 0; j < ahead; ++j)
+            if (kt0 + j < kt1) issue(kt0 + j);
 
         bf16x8 fbP[kNB], faP[4];
         for (int kt = kt0; kt < kt1; ++kt) {
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            // this step's loads landed; a deep tile leaves the next step's
+            // nload loads of this thread in flight (loads complete in order)
+            if (deep && kt + 1 < kt1 && nload == 8)
+                asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+            else if (deep && kt + 1 < kt1 && nload == 9)
+                asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+            else if (deep && kt + 1 < kt1 && nload == 10)
+                asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+            else
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             block_barrier();
-            if (kt + 1 < kt1) issue(kt + 1);
+            if (kt + ahead < kt1) issue(kt + ahead);
             if (!active) continue;
-            const unsigned char* sb = smem + ((kt - kt0) & 1) * kP_StageBytes;
+            const unsigned char* sb = smem + stage_off(kt);
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 const unsigned char* sk = sb + frag_off[kk];
@@ -317,6 +348,23 @@ __global__ __launch_bounds__(kP_Threads) void expert_gemm_pipe_kernel(GemmParams
     }
     // leave no load in flight
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// One kernel per GEMM.  A gate/up launch whose tile list holds no long tile
+// (every expert has at most 128 tokens: decode-sized batches) only streams
+// expert weights, and runs the body that keeps two steps of loads in flight
+// for its tiles of at most 64 rows.  Which body runs is decided from the tile
+// list once per launch and changes the load pipeline only, never the MFMA
+// sequence of an output element.  (Three stages for the short tails of a
+// large batch, or for the down projection's short tiles, which run between
+// long tiles, measured slower; so did deciding per tile inside one loop.)
+template <int MODE>
+__global__ __launch_bounds__(kP_Threads) void expert_gemm_pipe_kernel(GemmParams P) {
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kP_StageBytes];
+    if (MODE == MODE_GATE_UP && P.tile_start[P.E] == 0)
+        expert_gemm_body<MODE, MODE == MODE_GATE_UP>(P, smem);
+    else
+        expert_gemm_body<MODE, false>(P, smem);
 }
 
 // K parts for the split-K variant: more parts the fewer tokens an expert has.
