@@ -192,12 +192,17 @@ __device__ __forceinline__ void dma16_sbase(const void* base, uint32_t voff, uin
                  :: "v"(voff), "s"(base), "s"(lds) : "memory");
 }
 
-template <int MODE>
-__global__ __launch_bounds__(kQ_Threads) void expert_gemm_fp8_kernel(Fp8Params P) {
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kQ_StageBytes];
-    __shared__ uint8_t s_tsc[kFp8MaxKB * kQ_Tok];   // [kb][token row] 127 + e
-    __shared__ uint8_t s_wsc[kFp8MaxKB * 2];        // [kb][gate|up, or weight half] 127 + e
-    __shared__ float s_amax[2 * kQ_Tok];            // gate/up: |act| max per column half
+// A tile with at most 64 valid token rows needs 32 KB of weight rows and
+// 8 KB of token rows per step: three such stages fit where two full stages
+// do, and keep the loads of two steps in flight.
+constexpr int kQ_DeepTok = 64;
+constexpr int kQ_DeepStageBytes = kQ_WBlocks * 1024 + (kQ_DeepTok / 8) * 1024;   // 40960
+static_assert(3 * kQ_DeepStageBytes <= 2 * kQ_StageBytes, "three deep stages fit");
+
+template <int MODE, bool DEEP>
+__device__ __forceinline__ void expert_gemm_fp8_body(const Fp8Params& P, unsigned char* smem,
+                                                     uint8_t* s_tsc, uint8_t* s_wsc,
+                                                     float* s_amax) {
     const uint32_t lds0 =
         (uint32_t)(uintptr_t)((__attribute__((address_space(3))) unsigned char*)smem);
 
@@ -297,8 +302,18 @@ __global__ __launch_bounds__(kQ_Threads) void expert_gemm_fp8_kernel(Fp8Params P
             }
         }
 
+        // In a launch that only streams weights (DEEP), a tile with at most
+        // 64 valid rows ("deep") cycles through three 40 KB stages with the
+        // loads of two steps in flight; every other tile alternates two 64 KB
+        // stages, one step ahead.  Either way a stage is refilled only after
+        // the barrier that follows every wave's reads of it, and the MFMA
+        // sequence of an output element is the same.
+        const bool deep = DEEP && valid <= kQ_DeepTok;
+        auto stage_off = [&](int kt) {
+            return deep ? (kt % 3) * kQ_DeepStageBytes : (kt & 1) * kQ_StageBytes;
+        };
         auto issue = [&](int kt) {
-            const uint32_t sbase = lds0 + (uint32_t)((kt & 1) * kQ_StageBytes);
+            const uint32_t sbase = lds0 + (uint32_t)stage_off(kt);
             if (wave >= kQ_Issuers) return;
             const size_t ko = (size_t)kt * kQ_BK;
 #pragma unroll
@@ -308,14 +323,29 @@ __global__ __launch_bounds__(kQ_Threads) void expert_gemm_fp8_kernel(Fp8Params P
                 dma16_sbase(bse + ko, voff[i], sbase + (uint32_t)((i * kQ_Issuers + iw) * 1024));
             }
         };
-        issue(0);
+        const int ahead = deep ? 2 : 1;
+        // loads per step of this thread in a deep tile: 8 weight blocks and
+        // its token blocks below ntb (at most 8 in all)
+        const int nload =
+            wave < kQ_Issuers ? kQ_WDma + (ntb > iw ? 1 : 0) + (ntb > iw + 4 ? 1 : 0) : 0;
+        for (int j = 0; j < ahead; ++j)
+            if (j < nkb) issue(j);
 
         for (int kt = 0; kt < nkb; ++kt) {
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            // this step's loads landed; a deep tile leaves the next step's
+            // nload loads of this thread in flight (loads complete in order)
+            if (deep && kt + 1 < nkb && nload == 8)
+                asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+            else if (deep && kt + 1 < nkb && nload == 9)
+                asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+            else if (deep && kt + 1 < nkb && nload == 10)
+                asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+            else
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             block_barrier();
-            if (kt + 1 < nkb) issue(kt + 1);
+            if (kt + ahead < nkb) issue(kt + ahead);
             if (!active) continue;
-            const unsigned char* sb = smem + (kt & 1) * kQ_StageBytes;
+            const unsigned char* sb = smem + stage_off(kt);
             const int sa0 = s_wsc[kt * 2 + (MODE == MODE_GATE_UP ? 0 : wm)];
             const int sa1 = (MODE == MODE_GATE_UP) ? (int)s_wsc[kt * 2 + 1] : sa0;
             int sbv[kNB];
@@ -411,6 +441,22 @@ __global__ __launch_bounds__(kQ_Threads) void expert_gemm_fp8_kernel(Fp8Params P
         }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// A gate/up launch whose tile list holds no long tile (every expert has at
+// most 128 tokens: decode-sized batches) only streams expert weights and runs
+// the body that keeps two steps of loads in flight; the choice is made once
+// per launch from the tile list and never changes the MFMA sequence.
+template <int MODE>
+__global__ __launch_bounds__(kQ_Threads) void expert_gemm_fp8_kernel(Fp8Params P) {
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kQ_StageBytes];
+    __shared__ uint8_t s_tsc[kFp8MaxKB * kQ_Tok];   // [kb][token row] 127 + e
+    __shared__ uint8_t s_wsc[kFp8MaxKB * 2];        // [kb][gate|up, or weight half] 127 + e
+    __shared__ float s_amax[2 * kQ_Tok];            // gate/up: |act| max per column half
+    if (MODE == MODE_GATE_UP && P.tile_start[P.E] == 0)
+        expert_gemm_fp8_body<MODE, MODE == MODE_GATE_UP>(P, smem, s_tsc, s_wsc, s_amax);
+    else
+        expert_gemm_fp8_body<MODE, false>(P, smem, s_tsc, s_wsc, s_amax);
 }
 
 template <int MODE>
