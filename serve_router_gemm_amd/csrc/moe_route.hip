@@ -27,9 +27,14 @@ constexpr int kRouteThreads = 256;
 constexpr int kStageK = 32;   // hidden indices staged in LDS per step
 
 // part[c][t][e] = fp32 logit (SPLIT=false: all chunks folded, c = 0) or the
-// chunk-c partial sum (SPLIT=true: blockIdx.z = c).
+// chunk-c partial sum (SPLIT=true: blockIdx.z = c).  With PF the next step's
+// x and w pieces are loaded into registers while the current step's chains
+// run from LDS: the vocabulary projection streams its rows from HBM and gains
+// (T = 64: 0.89 -> 0.85 ms, T = 1: 0.47 -> 0.38 ms); the router, whose
+// operands sit in L2, loses 4% with it and runs without.  The chains, and so
+// the bits, are the same either way.
 // Thread (ty, tx): tokens t0 + ty*TT + i, experts e0 + tx + 32*j.
-template <int TT, int TE, bool SPLIT>
+template <int TT, int TE, bool SPLIT, bool PF>
 __global__ __launch_bounds__(kRouteThreads) void router_logits_kernel(
     int T, int H, int E, const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
     float* __restrict__ part) {
@@ -56,56 +61,137 @@ __global__ __launch_bounds__(kRouteThreads) void router_logits_kernel(
 #pragma unroll
         for (int j = 0; j < TE; ++j) { total[i][j] = 0.0f; acc[i][j] = 0.0f; }
 
-    for (int k0 = k_begin; k0 < k_end; k0 += kStageK) {
-        __syncthreads();
-        // stage x[t0:t0+BT, k0:k0+32] and wr[e0:e0+BE, k0:k0+32] as fp32, k-major
-        for (int c = tid; c < BT * 4; c += kRouteThreads) {
-            const int row = c >> 2, q = c & 3;
-            const int t = t0 + row;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (t < T) v = *reinterpret_cast<const uint4*>(x + (size_t)t * H + k0 + q * 8);
-            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+    if constexpr (PF) {
+        // piece c of a step: row c / 4, hidden indices k0 + 8 * (c % 4) .. + 7.
+        // The next step's pieces are loaded into registers while the current
+        // step's chains run from LDS; the chains are unchanged by this.
+        constexpr int NX = (BT * 4 + kRouteThreads - 1) / kRouteThreads;
+        constexpr int NW = (BE * 4 + kRouteThreads - 1) / kRouteThreads;
+        uint4 xr[NX], wg[NW];
+        auto fetch = [&](int k0) {
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                xs[q * 8 + 2 * u][row] = bf16_to_f32(w4[u] & 0xFFFFu);
-                xs[q * 8 + 2 * u + 1][row] = bf16_to_f32(w4[u] >> 16);
+            for (int i = 0; i < NX; ++i) {
+                const int c = tid + i * kRouteThreads;
+                const int t = t0 + (c >> 2);
+                xr[i] = make_uint4(0, 0, 0, 0);
+                if (c < BT * 4 && t < T)
+                    xr[i] = *reinterpret_cast<const uint4*>(x + (size_t)t * H + k0 + (c & 3) * 8);
             }
-        }
-        for (int c = tid; c < BE * 4; c += kRouteThreads) {
-            const int row = c >> 2, q = c & 3;
-            const int e = e0 + row;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (e < E) v = *reinterpret_cast<const uint4*>(wr + (size_t)e * H + k0 + q * 8);
-            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                ws[q * 8 + 2 * u][row] = bf16_to_f32(w4[u] & 0xFFFFu);
-                ws[q * 8 + 2 * u + 1][row] = bf16_to_f32(w4[u] >> 16);
+            for (int i = 0; i < NW; ++i) {
+                const int c = tid + i * kRouteThreads;
+                const int e = e0 + (c >> 2);
+                wg[i] = make_uint4(0, 0, 0, 0);
+                if (c < BE * 4 && e < E)
+                    wg[i] = *reinterpret_cast<const uint4*>(wr + (size_t)e * H + k0 + (c & 3) * 8);
             }
-        }
-        __syncthreads();
-#pragma unroll 4
-        for (int kk = 0; kk < kStageK; ++kk) {
-            float xv[TT], wv[TE];
+        };
+        if (k_begin < k_end) fetch(k_begin);
+        for (int k0 = k_begin; k0 < k_end; k0 += kStageK) {
+            __syncthreads();
+            // stage x[t0:t0+BT, k0:k0+32] and wr[e0:e0+BE, k0:k0+32] as fp32, k-major
 #pragma unroll
-            for (int i = 0; i < TT; ++i) xv[i] = xs[kk][ty * TT + i];
+            for (int i = 0; i < NX; ++i) {
+                const int c = tid + i * kRouteThreads;
+                if (c >= BT * 4) continue;
+                const int row = c >> 2, q = c & 3;
+                const uint32_t w4[4] = {xr[i].x, xr[i].y, xr[i].z, xr[i].w};
 #pragma unroll
-            for (int j = 0; j < TE; ++j) wv[j] = ws[kk][tx + 32 * j];
-#pragma unroll
-            for (int i = 0; i < TT; ++i)
-#pragma unroll
-                for (int j = 0; j < TE; ++j) acc[i][j] = __builtin_fmaf(xv[i], wv[j], acc[i][j]);
-        }
-        // end of a 256-wide chunk (or of H): fold the chunk sum in order
-        const int kn = k0 + kStageK;
-        if (!SPLIT && ((kn % kLogitChunk) == 0 || kn == k_end)) {
-#pragma unroll
-            for (int i = 0; i < TT; ++i)
-#pragma unroll
-                for (int j = 0; j < TE; ++j) {
-                    total[i][j] = total[i][j] + acc[i][j];
-                    acc[i][j] = 0.0f;
+                for (int u = 0; u < 4; ++u) {
+                    xs[q * 8 + 2 * u][row] = bf16_to_f32(w4[u] & 0xFFFFu);
+                    xs[q * 8 + 2 * u + 1][row] = bf16_to_f32(w4[u] >> 16);
                 }
+            }
+#pragma unroll
+            for (int i = 0; i < NW; ++i) {
+                const int c = tid + i * kRouteThreads;
+                if (c >= BE * 4) continue;
+                const int row = c >> 2, q = c & 3;
+                const uint32_t w4[4] = {wg[i].x, wg[i].y, wg[i].z, wg[i].w};
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    ws[q * 8 + 2 * u][row] = bf16_to_f32(w4[u] & 0xFFFFu);
+                    ws[q * 8 + 2 * u + 1][row] = bf16_to_f32(w4[u] >> 16);
+                }
+            }
+            __syncthreads();
+            if (k0 + kStageK < k_end) fetch(k0 + kStageK);
+#pragma unroll 4
+            for (int kk = 0; kk < kStageK; ++kk) {
+                float xv[TT], wv[TE];
+#pragma unroll
+                for (int i = 0; i < TT; ++i) xv[i] = xs[kk][ty * TT + i];
+#pragma unroll
+                for (int j = 0; j < TE; ++j) wv[j] = ws[kk][tx + 32 * j];
+#pragma unroll
+                for (int i = 0; i < TT; ++i)
+#pragma unroll
+                    for (int j = 0; j < TE; ++j) acc[i][j] = __builtin_fmaf(xv[i], wv[j], acc[i][j]);
+            }
+            // end of a 256-wide chunk (or of H): fold the chunk sum in order
+            const int kn = k0 + kStageK;
+            if (!SPLIT && ((kn % kLogitChunk) == 0 || kn == k_end)) {
+#pragma unroll
+                for (int i = 0; i < TT; ++i)
+#pragma unroll
+                    for (int j = 0; j < TE; ++j) {
+                        total[i][j] = total[i][j] + acc[i][j];
+                        acc[i][j] = 0.0f;
+                    }
+            }
+        }
+    } else {
+        for (int k0 = k_begin; k0 < k_end; k0 += kStageK) {
+            __syncthreads();
+            // stage x[t0:t0+BT, k0:k0+32] and wr[e0:e0+BE, k0:k0+32] as fp32, k-major
+            for (int c = tid; c < BT * 4; c += kRouteThreads) {
+                const int row = c >> 2, q = c & 3;
+                const int t = t0 + row;
+                uint4 v = make_uint4(0, 0, 0, 0);
+                if (t < T) v = *reinterpret_cast<const uint4*>(x + (size_t)t * H + k0 + q * 8);
+                const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    xs[q * 8 + 2 * u][row] = bf16_to_f32(w4[u] & 0xFFFFu);
+                    xs[q * 8 + 2 * u + 1][row] = bf16_to_f32(w4[u] >> 16);
+                }
+            }
+            for (int c = tid; c < BE * 4; c += kRouteThreads) {
+                const int row = c >> 2, q = c & 3;
+                const int e = e0 + row;
+                uint4 v = make_uint4(0, 0, 0, 0);
+                if (e < E) v = *reinterpret_cast<const uint4*>(wr + (size_t)e * H + k0 + q * 8);
+                const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    ws[q * 8 + 2 * u][row] = bf16_to_f32(w4[u] & 0xFFFFu);
+                    ws[q * 8 + 2 * u + 1][row] = bf16_to_f32(w4[u] >> 16);
+                }
+            }
+            __syncthreads();
+#pragma unroll 4
+            for (int kk = 0; kk < kStageK; ++kk) {
+                float xv[TT], wv[TE];
+#pragma unroll
+                for (int i = 0; i < TT; ++i) xv[i] = xs[kk][ty * TT + i];
+#pragma unroll
+                for (int j = 0; j < TE; ++j) wv[j] = ws[kk][tx + 32 * j];
+#pragma unroll
+                for (int i = 0; i < TT; ++i)
+#pragma unroll
+                    for (int j = 0; j < TE; ++j) acc[i][j] = __builtin_fmaf(xv[i], wv[j], acc[i][j]);
+            }
+            // end of a 256-wide chunk (or of H): fold the chunk sum in order
+            const int kn = k0 + kStageK;
+            if (!SPLIT && ((kn % kLogitChunk) == 0 || kn == k_end)) {
+#pragma unroll
+                for (int i = 0; i < TT; ++i)
+#pragma unroll
+                    for (int j = 0; j < TE; ++j) {
+                        total[i][j] = total[i][j] + acc[i][j];
+                        acc[i][j] = 0.0f;
+                    }
+            }
         }
     }
 
@@ -230,13 +316,13 @@ __global__ __launch_bounds__(256) void router_select_kernel(
         }
 }
 
-template <int TT, int TE, bool SPLIT>
+template <int TT, int TE, bool SPLIT, bool PF = false>
 hipError_t launch_logits(int T, int H, int E, const uint16_t* x, const uint16_t* wr,
                          float* part, hipStream_t s) {
     constexpr int BT = 8 * TT, BE = 32 * TE;
     const int nchunks = (H + kLogitChunk - 1) / kLogitChunk;
     dim3 grid((T + BT - 1) / BT, (E + BE - 1) / BE, SPLIT ? nchunks : 1);
-    router_logits_kernel<TT, TE, SPLIT><<<grid, kRouteThreads, 0, s>>>(T, H, E, x, wr, part);
+    router_logits_kernel<TT, TE, SPLIT, PF><<<grid, kRouteThreads, 0, s>>>(T, H, E, x, wr, part);
     return hipGetLastError();
 }
 
@@ -271,8 +357,8 @@ size_t route_ws_bytes(int T, int H, int E) {
 // only on its own row pair, so the tile never changes its bits.
 hipError_t launch_lm_logits(int T, int H, int V, const uint16_t* h, const uint16_t* proj,
                             float* z, hipStream_t s) {
-    if (T <= 8) return launch_logits<1, 4, false>(T, H, V, h, proj, z, s);
-    return launch_logits<8, 4, false>(T, H, V, h, proj, z, s);
+    if (T <= 8) return launch_logits<1, 4, false, true>(T, H, V, h, proj, z, s);
+    return launch_logits<8, 4, false, true>(T, H, V, h, proj, z, s);
 }
 
 hipError_t launch_route(int T, int H, int E, int k, int score, int renorm, const uint16_t* x,
