@@ -489,7 +489,10 @@ def main():
     # oracle on the host cores, bounded sample of the same workload
     nsample = args.cpu_sample
     if nsample is None:
-        nsample = {"large": 96, "dec": 32, "tie": 96, "mid": 256, "tiny": 64}[cfg.name]
+        # about 10-15 s of oracle work on 16 host threads (the large layer's
+        # whole-layer oracle runs ~27 tokens/s there; the tie and mid layers
+        # cost 0.66x and 0.23x as much per token); at most the batch
+        nsample = {"large": 320, "dec": 64, "tie": 480, "mid": 1400, "tiny": 64}[cfg.name]
     nsample = min(nsample, T)
     if nsample > 0:
         from oracle import oracle as O
