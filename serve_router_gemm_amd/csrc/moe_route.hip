@@ -208,6 +208,79 @@ __global__ __launch_bounds__(kRouteThreads) void router_logits_kernel(
     }
 }
 
+// Vocabulary projection for a few tokens (T <= TT <= 8): one thread per
+// vocabulary row streams the row in 16-byte loads (two groups of 8 in flight
+// per lane) and runs the same chains as the folded router kernel: within
+// each 256-wide chunk an ascending fp32 fma chain from +0 for every token,
+// chunk sums added in ascending order.  The tokens' hidden states sit in LDS
+// as fp32, 2048 indices at a time.  Rows past V read row V-1 and drop it.
+constexpr int kStreamThreads = 256;
+constexpr int kStreamCh = 2048;   // hidden indices of the tokens staged in LDS
+
+template <int TT>
+__global__ __launch_bounds__(kStreamThreads) void lm_logits_stream_kernel(
+    int T, int H, int V, const uint16_t* __restrict__ h, const uint16_t* __restrict__ proj,
+    float* __restrict__ z) {
+    static_assert(kStreamCh % kLogitChunk == 0, "staged span is whole chunks");
+    __shared__ __attribute__((aligned(16))) float xs[TT][kStreamCh];
+    const int v = blockIdx.x * kStreamThreads + threadIdx.x;
+    const uint16_t* row = proj + (size_t)min(v, V - 1) * H;
+
+    float total[TT], acc[TT];
+#pragma unroll
+    for (int t = 0; t < TT; ++t) { total[t] = 0.0f; acc[t] = 0.0f; }
+
+    for (int c0 = 0; c0 < H; c0 += kStreamCh) {
+        const int n = min(kStreamCh, H - c0);   // a multiple of 64
+        __syncthreads();   // every thread done with the previous span
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+            for (int i = threadIdx.x; i < n; i += kStreamThreads)
+                xs[t][i] = t < T ? bf16_to_f32(h[(size_t)t * H + c0 + i]) : 0.0f;
+        __syncthreads();
+#pragma unroll 2
+        for (int i0 = 0; i0 < n; i0 += 64) {
+            uint4 w[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                w[u] = *reinterpret_cast<const uint4*>(row + c0 + i0 + 8 * u);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const uint32_t q[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float wv = bf16_to_f32((e & 1) ? (q[e >> 1] >> 16) : (q[e >> 1] & 0xFFFFu));
+#pragma unroll
+                    for (int t = 0; t < TT; ++t)
+                        acc[t] = __builtin_fmaf(xs[t][i0 + 8 * u + e], wv, acc[t]);
+                }
+            }
+            // end of a 256-wide chunk (or of H): fold the chunk sum in order
+            const int kn = c0 + i0 + 64;
+            if ((kn % kLogitChunk) == 0 || kn == H) {
+#pragma unroll
+                for (int t = 0; t < TT; ++t) {
+                    total[t] = total[t] + acc[t];
+                    acc[t] = 0.0f;
+                }
+            }
+        }
+    }
+    if (v < V) {
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+            if (t < T) z[(size_t)t * V + v] = total[t];
+    }
+}
+
+template <int TT>
+hipError_t launch_lm_stream(int T, int H, int V, const uint16_t* h, const uint16_t* proj,
+                            float* z, hipStream_t s) {
+    const int blocks = (V + kStreamThreads - 1) / kStreamThreads;
+    lm_logits_stream_kernel<TT><<<blocks, kStreamThreads, 0, s>>>(T, H, V, h, proj, z);
+    return hipGetLastError();
+}
+
 constexpr int kSelMaxQ = 8;   // experts per lane: E <= 512
 
 // One wave per token: fold partial logits, keys, top-k, weights.  With
@@ -352,12 +425,16 @@ size_t route_ws_bytes(int T, int H, int E) {
 }
 
 // Vocabulary projection of a decode step (z = h . proj^T) in the router's
-// pinned order: the same kernel, folded, one register tile per thread (one
-// token per thread for the few-token batches of decoding).  Each z depends
-// only on its own row pair, so the tile never changes its bits.
+// pinned order: up to 8 tokens by the streaming kernel (one vocabulary row per
+// thread), more by the folded router kernel with its register tile.  Each z
+// depends only on its own row pair and is the same chain in both, so the
+// choice never changes its bits.
 hipError_t launch_lm_logits(int T, int H, int V, const uint16_t* h, const uint16_t* proj,
                             float* z, hipStream_t s) {
-    if (T <= 8) return launch_logits<1, 4, false, true>(T, H, V, h, proj, z, s);
+    if (T <= 1) return launch_lm_stream<1>(T, H, V, h, proj, z, s);
+    if (T <= 2) return launch_lm_stream<2>(T, H, V, h, proj, z, s);
+    if (T <= 4) return launch_lm_stream<4>(T, H, V, h, proj, z, s);
+    if (T <= 8) return launch_lm_stream<8>(T, H, V, h, proj, z, s);
     return launch_logits<8, 4, false, true>(T, H, V, h, proj, z, s);
 }
 
