@@ -25,6 +25,7 @@ namespace {
 constexpr int kHistThreads = 256;
 constexpr int kMaxExperts = 512;
 constexpr int kExpertBits = 9;   // ids < 512
+constexpr int kScanBatch = 16;   // chunk counts loaded together in the scan
 
 __global__ __launch_bounds__(kHistThreads) void permute_hist_kernel(
     int A, int E, int chunk, const int32_t* __restrict__ ids, int32_t* __restrict__ bh) {
@@ -48,12 +49,21 @@ __global__ __launch_bounds__(kMaxExperts) void permute_scan_kernel(
     int32_t* __restrict__ offsets) {
     __shared__ int sc[kMaxExperts];
     const int e = threadIdx.x;
+    // The chunk counts of an expert are read kScanBatch at a time, so that
+    // their loads are in flight together rather than one after another.
     int run = 0;
     if (e < E)
-        for (int b = 0; b < nchunks; ++b) {
-            const int v = bh[(size_t)b * E + e];
-            bh[(size_t)b * E + e] = run;
-            run += v;
+        for (int b0 = 0; b0 < nchunks; b0 += kScanBatch) {
+            int v[kScanBatch];
+#pragma unroll
+            for (int u = 0; u < kScanBatch; ++u)
+                v[u] = (b0 + u < nchunks) ? bh[(size_t)(b0 + u) * E + e] : 0;
+#pragma unroll
+            for (int u = 0; u < kScanBatch; ++u)
+                if (b0 + u < nchunks) {
+                    bh[(size_t)(b0 + u) * E + e] = run;
+                    run += v[u];
+                }
         }
     sc[e] = (e < E) ? run : 0;
     __syncthreads();
@@ -68,7 +78,15 @@ __global__ __launch_bounds__(kMaxExperts) void permute_scan_kernel(
     if (e < E) {
         counts[e] = run;
         offsets[e] = excl;
-        for (int b = 0; b < nchunks; ++b) bh[(size_t)b * E + e] += excl;
+        for (int b0 = 0; b0 < nchunks; b0 += kScanBatch) {
+            int v[kScanBatch];
+#pragma unroll
+            for (int u = 0; u < kScanBatch; ++u)
+                v[u] = (b0 + u < nchunks) ? bh[(size_t)(b0 + u) * E + e] : 0;
+#pragma unroll
+            for (int u = 0; u < kScanBatch; ++u)
+                if (b0 + u < nchunks) bh[(size_t)(b0 + u) * E + e] = v[u] + excl;
+        }
     }
     if (e == E - 1) offsets[E] = sc[e];
 }
