@@ -279,6 +279,29 @@ def test_fp8_batch_invariance():
         log(f"[fp8] invariance mid T={T}: 0 differing bits over 2 batches")
 
 
+def test_fp8_weight_streaming_launch_matches_full_launch():
+    """The FP8 gate/up keeps two steps of loads in flight in a launch where no
+    expert has more than 128 tokens; the MFMA sequence is the same.  500
+    tokens alone (tiles on both sides of 64 rows) and inside a 4000-token batch
+    (experts above 128 tokens) must give bit-identical outputs."""
+    cfg = I.scaled(I.CONFIGS["mid"], T=500)
+    L = layer(cfg)
+    wqd = M.quantize_weights_fp8(L["w_gate"], L["w_up"], L["w_down"])
+    x = I.make_tokens(4000, cfg.H, 4343, "cpu").to(DEV)
+    o1 = bits(_fwd8(cfg, L, wqd, x[:500].contiguous()))
+    o2 = bits(_fwd8(cfg, L, wqd, x))
+    ids1, _ = M.route(x[:500].contiguous(), L["w_router"], cfg.k, cfg.score, cfg.renorm,
+                      bias=L["bias"])
+    ids2, _ = M.route(x, L["w_router"], cfg.k, cfg.score, cfg.renorm, bias=L["bias"])
+    c1 = np.bincount(ids1.cpu().numpy().reshape(-1), minlength=cfg.E)
+    c2 = np.bincount(ids2.cpu().numpy().reshape(-1), minlength=cfg.E)
+    assert c1.max() <= 128 and np.any((c1 > 64) & (c1 <= 128)) and np.any(c1 <= 64), c1
+    assert c2.max() > 128
+    assert np.array_equal(o1, o2[:500])
+    log(f"[fp8] 500 tokens: weight-streaming launch (max {c1.max()} tokens per expert) == "
+        f"the same rows of a 4000-token launch (max {c2.max()})")
+
+
 def test_large_fp8_sampled():
     """The large layer at T = 16384 in the launch configuration the benchmark
     times: the GPU's weight codes of sampled experts bit-exact, and act and y of
