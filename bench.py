@@ -471,6 +471,14 @@ def main():
                    "variant": "invariant" if args.variant == 0 else "splitk",
                    "active_experts": int((counts_np > 0).sum()),
                    "max_expert_tokens": int(counts_np.max())},
+        # the realised routing load: experts per token-count bucket, and the largest loads
+        "expert_load": {
+            "experts_by_tokens": {
+                label: int(((counts_np >= lo) & (counts_np < hi)).sum())
+                for label, lo, hi in (("0", 0, 1), ("1-63", 1, 64), ("64-255", 64, 256),
+                                      ("256-1023", 256, 1024), ("1024-4095", 1024, 4096),
+                                      (">=4096", 4096, 1 << 31))},
+            "largest": [int(v) for v in np.sort(counts_np)[::-1][:8]]},
         "roofline": roofline,
         "stages_ms": {n: round(v, 4) for n, v in stage_ms.items()},
         "route": route_res,
