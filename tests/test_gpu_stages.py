@@ -160,6 +160,9 @@ GEMM_CASES = [
     ("mid_T300", _cfg("mid", T=300)),
     ("mid_T7", _cfg("mid", T=7)),
     ("Fedge_Hedge", _cfg("mid", T=257, H=320, F=192, E=16, k=4)),
+    # every expert far below 64 tokens: the gate/up launch keeps two steps of
+    # loads in flight, here over 5 K steps (not a multiple of its 3 stages)
+    ("Hedge_streaming", _cfg("mid", T=40, H=320, F=192, E=16, k=4)),
     ("E1_k1", _cfg("tiny", T=300, E=1, k=1)),
 ]
 
