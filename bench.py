@@ -33,7 +33,7 @@ METRIC = "MoE-layer tokens/s + MFMA util; bitwise-identical output across batch 
 # HBM bytes per launch of the gate/up kernel from rocprofv3 FETCH_SIZE (x2.0) and
 # WRITE_SIZE (x1.0) on the large workload (profiles/expert_gemm_large_T16384.md),
 # valid only for the kernel source they were taken on.
-TRAFFIC = {"kernel_sha256_prefix": "8814eb5422376843", "workload": "large", "bytes": 22.68e9}
+TRAFFIC = {"kernel_sha256_prefix": "8814eb5422376843", "workload": "large", "bytes": 23.38e9}
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 PEAK_FP32_VALU_TFLOPS = 78.6  # 256 CU x 64 lanes x 2 flop x 2.4 GHz, fp32 fma without packed math
