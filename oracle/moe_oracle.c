@@ -515,8 +515,16 @@ int orc_forward_tokens(int n, const int32_t* tokens, int H, int E, int F, int k,
  *   z[t,v]    = the D1 chain of out[t,:] against proj[v,:] (bf16 x bf16, fp32);
  *   m         = max_v z[t,v];
  *   S         = +0; for each chunk of 256 consecutive v (ascending): s = +0,
- *               s = s + expf(z_v - m) for v ascending; S = S + s   (fp32);
- *   logp[t,v] = z[t,v] - (m + logf(S))                               (fp32);
+ *               s = s + exp32(z_v - m) for v ascending; S = S + s   (fp32);
+ *   logp[t,v] = z[t,v] - (m + log32(S))                              (fp32);
+ *   exp32(a), log32(a): the fp32 exponential and logarithm, correctly rounded
+ *               (the exact value rounded to nearest fp32, ties to even).  They
+ *               are evaluated as the fp64 library function rounded once to
+ *               fp32, which is the correctly rounded value unless the exact
+ *               value lies within an fp64 ulp of an fp32 rounding boundary.
+ *               Fixing the transcendental's rounding (rather than taking
+ *               whatever a platform's single-precision expf returns) is what
+ *               lets two implementations of S agree bit for bit.
  *   k3        (Schulman's estimator, r = p_ref / p_test):
  *               d_v = logp_ref[v] - logp_test[v] (fp64), r - 1 = expm1(d_v),
  *               ln r = d_v; mean = sum_v exp(logp_test[v]) * (expm1(d_v) - d_v)
@@ -534,6 +542,10 @@ void orc_lm_head_logits(int T, int H, int V, const uint16_t* h, const uint16_t* 
     orc_router_logits(T, H, V, h, proj, z, nthreads);
 }
 
+/* exp32 / log32 of the definition above */
+float orc_exp32(float a) { return (float)exp((double)a); }
+float orc_log32(float a) { return (float)log((double)a); }
+
 static void log_softmax_row(const float* z, int V, float* logp)
 {
     float m = -INFINITY;
@@ -542,10 +554,10 @@ static void log_softmax_row(const float* z, int V, float* logp)
     for (int c0 = 0; c0 < V; c0 += ORC_SUM_CHUNK) {
         int c1 = c0 + ORC_SUM_CHUNK < V ? c0 + ORC_SUM_CHUNK : V;
         float s = 0.0f;
-        for (int v = c0; v < c1; ++v) s = s + expf(z[v] - m);
+        for (int v = c0; v < c1; ++v) s = s + orc_exp32(z[v] - m);
         S = S + s;
     }
-    float lse = m + logf(S);
+    float lse = m + orc_log32(S);
     for (int v = 0; v < V; ++v) logp[v] = z[v] - lse;
 }
 

@@ -81,6 +81,10 @@ def _declare(L):
     L.orc_forward_tokens_fp8.argtypes = [i32, P, i32, i32, i32, i32, i32, i32, P, P, P, P, P,
                                          P, P, P, P, P, P, P, P, P, i32]
     L.orc_log_softmax.argtypes = [i32, i32, P, P, i32]
+    L.orc_exp32.restype = ctypes.c_float
+    L.orc_exp32.argtypes = [ctypes.c_float]
+    L.orc_log32.restype = ctypes.c_float
+    L.orc_log32.argtypes = [ctypes.c_float]
     L.orc_k3.argtypes = [i32, i32, P, P, P, P, P]
 
 
@@ -264,6 +268,16 @@ def log_softmax(z, nthreads=0) -> np.ndarray:
     out = np.empty_like(z)
     lib().orc_log_softmax(T, V, _p(z), _p(out), nthreads)
     return out
+
+
+def exp32(a: float) -> np.float32:
+    """The correctly rounded fp32 exponential of the log-softmax definition."""
+    return np.float32(lib().orc_exp32(float(np.float32(a))))
+
+
+def log32(a: float) -> np.float32:
+    """The correctly rounded fp32 logarithm of the log-softmax definition."""
+    return np.float32(lib().orc_log32(float(np.float32(a))))
 
 
 def k3(logp_ref, logp_test):

@@ -196,3 +196,138 @@ def test_k3_near_identical_rows_against_the_series():
     assert np.allclose(mean, lib, rtol=1e-9, atol=0)
     for t in range(3):
         assert math.isclose(gk3[t], series[t, g[t]], rel_tol=1e-9, abs_tol=1e-300)
+
+
+# ---------------------------------------------------------------------------
+# The log-softmax's transcendentals and sums, pinned to the last bit.
+# ---------------------------------------------------------------------------
+
+def _cr_f32(d):
+    """Round a high-precision Decimal to the nearest fp32, ties to even (written
+    out here from the IEEE definition: the nearest of the fp32 neighbours of
+    the double nearest d, compared in Decimal arithmetic)."""
+    from decimal import Decimal
+    f = np.float32(float(d))
+    cands = [np.nextafter(f, np.float32(-np.inf)), f, np.nextafter(f, np.float32(np.inf))]
+    return min(cands, key=lambda c: (abs(Decimal(float(c)) - d), int(c.view(np.uint32)) & 1))
+
+
+def test_exp32_and_log32_are_correctly_rounded():
+    """exp32 / log32 equal the exact exponential and logarithm (Python's
+    decimal module at 60 digits, which rounds them correctly at its precision)
+    rounded to the nearest fp32, on arguments the log-softmax meets: z - m in
+    [-110, 0] (down to subnormal and zero results) and sums in [1, 2^17]."""
+    from decimal import Decimal, getcontext
+    getcontext().prec = 60
+    rng = np.random.default_rng(12)
+    a = np.concatenate([-rng.exponential(4.0, 3000), -rng.uniform(80, 110, 300),
+                        [0.0, -1e-30, -2.0 ** -24, -87.3, -103.9, -150.0]]).astype(np.float32)
+    for v in a:
+        want = _cr_f32(Decimal(float(v)).exp())
+        got = O.exp32(v)
+        assert got.view(np.uint32) == want.view(np.uint32), (float(v), float(got), float(want))
+    s = np.concatenate([rng.uniform(1.0, 2.0 ** 17, 3000), [1.0, 1.0 + 2 ** -23, 65536.0]])
+    for v in s.astype(np.float32):
+        want = _cr_f32(Decimal(float(v)).ln())
+        got = O.log32(v)
+        assert got.view(np.uint32) == want.view(np.uint32), (float(v), float(got), float(want))
+    assert O.exp32(-np.inf) == 0.0 and O.exp32(0.0) == 1.0 and O.log32(1.0) == 0.0
+
+
+def test_log_softmax_sums_in_fp32_from_the_first_term():
+    """A chunk of one term 1 (z = m) followed by 255 terms t < 2^-24 (half an
+    fp32 ulp of 1): in the fp32 chain each t is lost, S = 1 exactly, log 1 = 0
+    and logp = z exactly.  An fp64 (or compensated, or pairwise) sum keeps the
+    255 t and moves logp_0 by about -2.5e-6."""
+    V = 256
+    z = np.full((1, V), np.float32(-18.5), dtype=np.float32)   # exp(-18.5) ~ 9.2e-9
+    z[0, 0] = 0.0
+    logp = O.log_softmax(z)
+    assert logp[0, 0] == 0.0
+    assert np.array_equal(logp[0, 1:], z[0, 1:])
+
+
+def test_log_softmax_chain_runs_in_ascending_v():
+    """The same terms with the 1 last: the ascending chain first adds the 255
+    terms t (about 255 t = 2.4e-6 in all), which then survive the add of 1, so
+    logp at the maximum is -log(1 + ~255 t) instead of 0 (descending order would
+    lose them)."""
+    V = 256
+    z = np.full((1, V), np.float32(-18.5), dtype=np.float32)
+    z[0, V - 1] = 0.0
+    logp = O.log_softmax(z)
+    t = math.exp(-18.5)
+    assert logp[0, V - 1] < -2e-6
+    assert abs(float(logp[0, V - 1]) + 255 * t) < 2 * 2.0 ** -23
+
+
+def test_log_softmax_chunks_sum_on_their_own():
+    """Two chunks: [1, t x 255] and [t x 256], t < 2^-24.  Chunk 0 sums to 1,
+    chunk 1 to ~256 t, and S = 1 + 256 t: logp_0 ~ -256 t.  A single running
+    fp32 sum gives 0 and an fp64 sum about -511 t; both are told apart."""
+    V = 512
+    z = np.full((1, V), np.float32(-18.5), dtype=np.float32)
+    z[0, 0] = 0.0
+    logp = O.log_softmax(z)
+    t = math.exp(-18.5)
+    got = -float(logp[0, 0])
+    assert abs(got - 256 * t) < 2 * 2.0 ** -23          # ~2.4e-6, within 2 ulp of 1
+    assert abs(got - 511 * t) > 1e-6 and got > 1e-6
+
+
+def test_k3_sums_fp64_terms_in_chunks():
+    """k3 terms: v = 0 gives T0 = expm1(1) - 1 (~0.718); every other v gives
+    exp(-38) * T0 (~2.3e-17, below half an fp64 ulp of T0).  In one running sum
+    they are all lost and the mean is T0; in the chunked order chunk 0 is T0 and
+    chunk 1 sums 256 of them (~5.8e-15, ~52 ulps of T0) before it is added."""
+    V = 512
+    test = np.full((1, V), np.float32(-38.0), dtype=np.float32)
+    test[0, 0] = 0.0
+    ref = test + np.float32(1.0)                          # d = 1 exactly everywhere
+    mean, _, g = O.k3(ref, test)
+    T0 = math.expm1(1.0) - 1.0
+    small = math.exp(-38.0) * T0
+    ulp = 2.0 ** -53
+    assert abs((mean[0] - T0) - 256 * small) <= 3 * ulp
+    assert g[0] == 0
+
+
+@pytest.mark.parametrize("m", [9.25, 1000.0, -3.5])
+def test_log_softmax_final_steps_round_in_fp32(m):
+    """A row of two equal logits m: both terms are exp(0) = 1, S = 2 exactly,
+    so lse = fp32(m + log32(2)) and logp = fp32(m - lse), with log32(2) the
+    correctly rounded fp32 log 2 (decimal module).  At m = 9.25 an fp64 add of
+    m and log 2 rounds to another fp32 than the fp32 add does, and at every m
+    (z - m) - log32(2) (two subtractions) differs from z - lse."""
+    from decimal import Decimal, getcontext
+    getcontext().prec = 60
+    l2 = _cr_f32(Decimal(2).ln())
+    z = np.full((1, 2), np.float32(m), dtype=np.float32)
+    logp = O.log_softmax(z)
+    lse = np.float32(np.float32(m) + l2)
+    want = np.float32(np.float32(m) - lse)
+    assert logp[0, 0].view(np.uint32) == want.view(np.uint32), (float(logp[0, 0]), float(want))
+    assert logp[0, 1] == logp[0, 0]
+
+
+def test_k3_chunk_sums_are_added_in_ascending_order():
+    """Chunk sums T0, c, c with c about 0.7 fp64 ulp of T0 (one term per later
+    chunk; every other term is exp(q) * 0 = 0 since ref = test there): in
+    ascending chunk order the mean is (T0 + c) + c = T0 + 2 ulp, in descending
+    order T0 + (c + c) = T0 + 1 ulp."""
+    V = 768
+    test = np.full((1, V), np.float32(-200.0), dtype=np.float32)
+    ref = test.copy()
+    T0 = math.expm1(1.0) - 1.0
+    ulp = 2.0 ** -53                                      # T0 in [0.5, 1)
+    a = np.float32(math.log(0.7 * ulp / T0))
+    test[0, 0], ref[0, 0] = 0.0, 1.0
+    for v in (256, 512):
+        test[0, v], ref[0, v] = a, a + np.float32(1.0)
+    assert float(ref[0, 256]) - float(test[0, 256]) == 1.0
+    mean, _, _ = O.k3(ref, test)
+    c = math.exp(float(a)) * T0
+    asc = (T0 + c) + c
+    desc = T0 + (c + c)
+    assert asc != desc
+    assert abs(mean[0] - asc) < abs(mean[0] - desc)
