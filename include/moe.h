@@ -128,7 +128,12 @@ const char* moe_status_string(int status);
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
 int moe_version(void);
 
-/* Router: logits, selection and weights (the "route" step).
+/* Router: logits, selection and weights (the "route" step).  The router is
+ * one of the reductions whose order must not depend on the batch, and near
+ * ties between experts must break deterministically (Fireworks page
+ * "位级一致：前沿训练的差异化关键", sections "曾经只有前沿实验室才有的功能" and
+ * "为什么比特级一致是一个复杂的问题"); hence the fixed logit order and the
+ * lowest-index tie-break described at the top of this file.
  *   x [device] [T,H] bf16; w_router [device] [E,H] bf16;
  *   bias [device] [E] fp32 or NULL (sigmoid only: NULL means all zero; a
  *   non-NULL bias with softmax is rejected with MOE_ERR_UNSUPPORTED);
@@ -139,6 +144,9 @@ int moe_route(int T, int H, int E, int top_k, int score, int renormalize,
               int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes, void* stream);
 
 /* Expert histogram, offsets and the stable permutation (the "permute" step).
+ * How many tokens each expert receives depends on the whole batch (same
+ * page, section "为什么比特级一致是一个复杂的问题"); this step is integer-only
+ * and stable, so the counts change launch work but never a token's values.
  *   topk_ids [device] [T,k] int32 with values in [0,E) (other values are
  *   skipped: not counted and not placed, and the tail of perm is then left
  *   unwritten);
@@ -151,7 +159,10 @@ int moe_permute(int T, int E, int top_k, const int32_t* topk_ids,
                 int32_t* inv_perm, void* ws, size_t ws_bytes, void* stream);
 
 /* Gate/up projections with the SwiGLU epilogue, grouped by expert (the
- * first expert GEMM).  For every permuted row p of expert e:
+ * first expert GEMM).  One kernel choice, tile and K order for every expert
+ * whatever its token count, and no split-K (same page, sections
+ * "为什么比特级一致是一个复杂的问题" and "曾经只有前沿实验室才有的功能").
+ * For every permuted row p of expert e:
  *   h_act[p, f] = bf16(silu(g) * u), g = x[perm[p]/k] . w_gate[e,f,:],
  *   u = x[perm[p]/k] . w_up[e,f,:], fp32 accumulation.
  *   x [device] [T,H]; perm, expert_offsets [device] from moe_permute;
@@ -162,7 +173,8 @@ int moe_expert_gate_up(int T, int H, int E, int F, int top_k, const uint16_t* x,
                        const uint16_t* w_gate, const uint16_t* w_up, uint16_t* h_act,
                        void* ws, size_t ws_bytes, void* stream);
 
-/* Down projection grouped by expert (the second expert GEMM): for every
+/* Down projection grouped by expert (the second expert GEMM), under the same
+ * fixed-kernel rule as the gate/up GEMM (same page and sections): for every
  * permuted row p of expert e, y[perm[p], h] = h_act[p,:] . w_down[e,h,:] in
  * fp32, written to assignment order.
  *   h_act [device] [T*k,F] bf16; w_down [device] [E,H,F]; y [device] out
@@ -172,22 +184,28 @@ int moe_expert_down(int T, int H, int E, int F, int top_k, const uint16_t* h_act
                     const uint16_t* w_down, float* y, int variant,
                     void* ws, size_t ws_bytes, void* stream);
 
-/* Both expert GEMMs: moe_expert_gate_up then moe_expert_down, with h_act
- * kept in the workspace. */
+/* Both expert GEMMs (the grouped SwiGLU expert FFN; same page and sections
+ * as moe_expert_gate_up): moe_expert_gate_up then moe_expert_down, with
+ * h_act kept in the workspace. */
 int moe_grouped_swiglu(int T, int H, int E, int F, int top_k, const uint16_t* x,
                        const int32_t* perm, const int32_t* expert_offsets,
                        const uint16_t* w_gate, const uint16_t* w_up,
                        const uint16_t* w_down, float* y, int variant,
                        void* ws, size_t ws_bytes, void* stream);
 
-/* Fixed-order fp32 weighted combine (the "combine" step):
+/* Fixed-order fp32 weighted combine (the "combine" step).  Both the
+ * precision and the order of the weighted sum of the expert outputs must be
+ * fixed (Fireworks page on numerical alignment and MoE routing, section
+ * "混合专家模型更难对齐"):
  *   out[t,h] = bf16(fma chain over j = 0..k-1 of topk_w[t,j] * y[t*k+j,h]).
  *   y [device] [T*k,H] fp32; topk_w [device] [T,k]; out [device] out [T,H]. */
 int moe_combine(int T, int H, int top_k, const float* y, const float* topk_w,
                 uint16_t* out, void* stream);
 
 /* The whole layer: route, permute, both expert GEMMs, combine, enqueued in
- * that order on `stream`.  topk_ids / topk_w may be NULL (then they live in
+ * that order on `stream`.  Each token's out is bit-identical whatever else
+ * shares the call (Fireworks page "位级一致：前沿训练的差异化关键", sections
+ * "曾经只有前沿实验室才有的功能" and "端到端零 KLD").  topk_ids / topk_w may be NULL (then they live in
  * the workspace); when given they receive the routing. */
 int moe_forward(int T, int H, int E, int F, int top_k, int score, int renormalize,
                 const uint16_t* x, const uint16_t* w_router, const float* bias,
@@ -263,8 +281,10 @@ int moe_lm_head_logits(int T, int H, int V, const uint16_t* h, const uint16_t* p
 
 /* fp32 log-softmax over v with fixed sums:
  *   m = max_v z; S = +0, for each chunk of 256 consecutive v (ascending):
- *   s = +0, s = s + expf(z_v - m) for v ascending, S = S + s;
- *   logp[t,v] = z[t,v] - (m + logf(S)).
+ *   s = +0, s = s + exp32(z_v - m) for v ascending, S = S + s;
+ *   logp[t,v] = z[t,v] - (m + log32(S)), every operation in fp32, where
+ *   exp32 and log32 are the exponential and logarithm correctly rounded to
+ *   fp32 (evaluated as the fp64 function rounded once).
  *   z [device] [T,V] fp32; logp [device] out [T,V] fp32; logp == z allowed
  *   (in place).  NaN inputs give NaN rows. */
 int moe_log_softmax(int T, int V, const float* z, float* logp, void* stream);

@@ -31,6 +31,8 @@
 // The split-K variant (down projection only) exists to show what invariance
 // costs and what breaking it does: experts with few tokens have their K range
 // cut into 2..8 parts, each summed on its own and added with fp32 atomics.
+#include <atomic>
+
 #include "moe_device.h"
 #include "moe_gemm_tiles.h"
 #include "moe_internal.h"
@@ -458,12 +460,22 @@ hipError_t launch_gemm(const GemmParams& P, hipStream_t s) {
 
 }  // namespace
 
+// CU count of the current device, queried once per device and kept (a launch
+// only reads the cache; the attribute query is not repeated per launch).
 int device_cu_count() {
-    int dev = 0, cu = 0;
+    constexpr int kMaxDev = 64;
+    static std::atomic<int> cache[kMaxDev];
+    int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (dev >= 0 && dev < kMaxDev) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int cu = 0;
     if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cu <= 0)
         return 256;
+    if (dev >= 0 && dev < kMaxDev) cache[dev].store(cu, std::memory_order_relaxed);
     return cu;
 }
 

@@ -9,8 +9,13 @@
 // neither the projection's order nor the sums; both are pinned here:
 //   z      the router's chunked fp32 chain (moe_route.hip);
 //   S      chunks of 256 consecutive v, each an ascending fp32 sum of
-//          expf(z_v - m) from +0, chunk sums added in ascending order;
-//   logp_v = z_v - (m + logf(S)), m = max_v z_v;
+//          exp32(z_v - m) from +0, chunk sums added in ascending order;
+//   logp_v = z_v - (m + log32(S)), m = max_v z_v;
+//   exp32, log32: the fp32 exponential and logarithm correctly rounded,
+//          taken as the fp64 function rounded once to fp32 (correct unless
+//          the exact value is within an fp64 ulp of an fp32 rounding
+//          boundary), so that any two implementations of S agree bit for
+//          bit instead of depending on a single-precision expf's last bit;
 //   k3     d_v = logp_ref - logp_test (fp64), term_v = exp(logp_test) *
 //          (expm1(d_v) - d_v), summed in fp64 in the same chunked order;
 //          greedy = the lowest v of largest logp_test, with its (unweighted)
@@ -33,6 +38,9 @@ constexpr int kPad = kSumChunk + 1;   // LDS stride of a chunk: chains of neighb
                                       // chunks fall on different banks
 constexpr int kSegF = 128;            // chunks per segment, fp32 terms (128.5 KB)
 constexpr int kSegD = 64;             // chunks per segment, fp64 terms (128.5 KB)
+
+__device__ __forceinline__ float exp32(float a) { return (float)exp((double)a); }
+__device__ __forceinline__ float log32(float a) { return (float)log((double)a); }
 
 __device__ __forceinline__ float block_max(float v, float* red) {
     for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
@@ -82,7 +90,7 @@ __global__ __launch_bounds__(kRowThreads) void log_softmax_kernel(int V, const f
 #pragma unroll
             for (int u = 0; u < kRowU; ++u) {
                 const int v = b + u * kRowThreads + threadIdx.x;
-                if (v < v1) seg[(v / kSumChunk - c0) * kPad + (v % kSumChunk)] = expf(t[u] - m);
+                if (v < v1) seg[(v / kSumChunk - c0) * kPad + (v % kSumChunk)] = exp32(t[u] - m);
             }
         }
         __syncthreads();
@@ -117,7 +125,7 @@ __global__ __launch_bounds__(kRowThreads) void log_softmax_kernel(int V, const f
         }
         __syncthreads();
     }
-    const float lse = m + logf(s_S);
+    const float lse = m + log32(s_S);
     for (int b = 0; b < V; b += kRowThreads * kRowU) {
         float t[kRowU];
 #pragma unroll

@@ -16,10 +16,13 @@ quantisation section).  Bars:
   * gate/up's bf16 act within that bound carried through silu(g)*u plus a
     bf16 rounding on each side, and its codes exactly the quantiser's codes
     of that act;
-  * the whole layer: routing bit-exact; out, whose act codes can differ from
-    the oracle's where the two act values straddle an e4m3 rounding point,
-    within 2^-7 of the oracle's norm-wise (the FP8-vs-BF16 gap is several
-    percent);
+  * the whole layer: routing bit-exact; out element by element within the
+    layer tolerance (2e-2 + 1e-2 |ref|) of the oracle's FP8 layer, and within
+    the propagated down-GEMM bound (plus one bf16 ulp) of the oracle's down
+    GEMM and combine run on the GPU's own act codes (those can differ from the
+    oracle's where the two act values straddle an e4m3 rounding point); the
+    norm-wise gap to the oracle per row (<= 2^-6) and over the sample is
+    reported next to the FP8-vs-BF16 gap;
   * batch invariance: probe rows bit-identical at every batch size.
 """
 from __future__ import annotations
@@ -140,6 +143,48 @@ def test_down_fp8_within_bound(shape):
         f"{same:.3f} of outputs bit-identical to the oracle")
 
 
+def test_scaled_mfma_arithmetic_probes():
+    """The arithmetic the FP8 GEMM bound rests on, probed through the down GEMM
+    (one token, one expert, one 128 x 128 block, unit scales).  A lane holds
+    the codes of K positions 16c..16c+15 and 64+16c..64+16c+15 (c = lane/16) in
+    its 32 slots; the instruction adds products in groups of 8 slots, and in a
+    group a product more than 13 binades below the group's largest is cut
+    toward zero to that grid; group sums are added at fp32 precision.  So with
+    products {1, 2^-18}: lost in one group (K 0 and 1), kept in different groups
+    (K 0 and 8: other slot group; 0 and 64: other chunk; 0 and 16: other lane);
+    {1, 2^-12} is kept in one group; 2^-18 alone is exact.  Each case is the
+    closed form of that model (the bound in this file allows 7 * 2^-13 of the
+    group's largest product per group)."""
+    one, sub, mn = 0x38, 0x01, 0x08          # e4m3 codes of 1, 2^-9, 2^-6
+    H = F = 128
+    aq = np.zeros((1, F), np.uint8)
+    aq[0, [0, 1, 8, 16, 64]] = [one, sub, sub, sub, sub]
+    aq[0, 2] = mn
+    wq = np.zeros((1, H, F), np.uint8)
+    cases = {0: [(0, one), (1, sub)], 1: [(0, one), (8, sub)], 2: [(0, one), (2, mn)],
+             3: [(0, one), (64, sub)], 4: [(0, one), (16, sub)], 5: [(1, sub)]}
+    for h, entries in cases.items():
+        for k, c in entries:
+            wq[0, h, k] = c
+    want = np.zeros(H, np.float64)
+    want[[0, 1, 2, 3, 4, 5]] = [1.0, 1 + 2.0 ** -18, 1 + 2.0 ** -12, 1 + 2.0 ** -18,
+                                1 + 2.0 ** -18, 2.0 ** -18]
+    t = lambda a: torch.from_numpy(a).to(DEV)
+    perm = t(np.zeros(1, np.int32))
+    offsets = t(np.array([0, 1], np.int32))
+    y = _np(M.expert_down_fp8(t(aq), t(np.zeros((1, 1), np.int8)), perm, offsets, t(wq),
+                              t(np.zeros((1, 1, 1), np.int8)), 1))[0].astype(np.float64)
+    assert np.array_equal(y, want), (y[:6].tolist(), want[:6].tolist())
+    # the oracle's exact block sum is within the bound of this arithmetic
+    ref = O.fp8_gemm(aq, np.zeros((1, 1), np.int8), np.zeros(1, np.int32), wq,
+                     np.zeros((1, 1, 1), np.int8))[0].astype(np.float64)
+    tol = gemm_tol(deq(aq, np.zeros((1, 1), np.int8), 1)[0],
+                   deq(wq[0], np.zeros((1, 1), np.int8), B))
+    assert np.all(np.abs(y - ref) <= tol)
+    log("[fp8] scaled-MFMA probes: groups of 8 slots, 13-binade cut inside a group, "
+        "fp32 sums across groups and lanes")
+
+
 def _gate_up_case(cfg):
     L = layer(cfg)
     x = I.make_x(cfg, DEV)
@@ -242,13 +287,58 @@ def test_forward_fp8_parity(case):
     o = O.bf16_to_f32(bits(out)[rows]).astype(np.float64)
     r8 = O.bf16_to_f32(ref8).astype(np.float64)
     r16 = O.bf16_to_f32(ref16).astype(np.float64)
+    # element-wise against the oracle's own FP8 layer: the layer tolerance
+    err8 = np.abs(o - r8)
+    assert np.all(err8 <= 2e-2 + 1e-2 * np.abs(r8)), float(err8.max())
+    # element-wise, down GEMM and combine: the oracle's FP8 down GEMM on the
+    # GPU's own act codes (its act can differ from the oracle's where the two
+    # straddle an e4m3 rounding point) and the oracle's combine on the GPU's
+    # weights; out within the propagated GEMM bound plus one bf16 ulp
+    _, w_s, offsets, perm = _routing(cfg, L, x)
+    xq, xe = M.quantize_fp8(x, 1)
+    aq, ae, _ = M.expert_gate_up_fp8(xq, xe, perm, offsets, wqd["wg_q"], wqd["wg_e"],
+                                     wqd["wu_q"], wqd["wu_e"], cfg.k)
+    y_s = M.expert_down_fp8(aq, ae, perm, offsets, wqd["wd_q"], wqd["wd_e"], cfg.k)
+    out_s = M.combine(y_s, w_s)
+    assert torch.equal(out_s.view(torch.int16), out.view(torch.int16)), "staged != fused"
+    perm_np = _np(perm)
+    inv = np.empty_like(perm_np)
+    inv[perm_np] = np.arange(perm_np.size)
+    asg = (rows[:, None] * cfg.k + np.arange(cfg.k)[None, :]).reshape(-1)
+    aq_g, ae_g = _np(aq)[inv[asg]], _np(ae)[inv[asg]]
+    experts = _np(ids).reshape(-1)[asg]
+    y_ref = O.fp8_gemm(aq_g, ae_g, experts, wq["wdq"], wq["wde"])
+    w_rows = _np(w)[rows]
+    out_ref = O.combine(y_ref, w_rows, len(rows), cfg.H, cfg.k)
+    a_deq = deq(aq_g, ae_g, 1)
+    # |out_gpu - out_ref| <= sum_j |w_j| (GEMM bound of y_j) + the two fma
+    # chains' roundings (k u sum_j |w_j y_j| each) + one bf16 ulp (two
+    # round-to-nearest results of values delta apart differ by <= delta + 1 ulp,
+    # and a bf16 ulp is at most 2^-7 of the value)
+    lim = np.zeros((len(rows), cfg.H))
+    wy = np.zeros((len(rows), cfg.H))
+    for i in range(len(rows)):
+        for j in range(cfg.k):
+            a = i * cfg.k + j
+            e = experts[a]
+            wj = abs(float(w_rows[i, j]))
+            lim[i] += wj * gemm_tol(a_deq[a], deq(wq["wdq"][e], wq["wde"][e], B))
+            wy[i] += wj * np.abs(y_ref[a].astype(np.float64))
+    orf = O.bf16_to_f32(out_ref).astype(np.float64)
+    lim = (lim * (1 + 2 * cfg.k * U) + 2 * cfg.k * U * wy
+           + 2.0 ** -7 * np.maximum(np.abs(o), np.abs(orf)) + 1e-30)
+    err = np.abs(o - orf)
+    assert np.all(err <= lim), float((err / lim).max())
+    # per row, and over the sample: norm-wise gaps (reported; per row bounded)
+    row_rel = np.linalg.norm(o - r8, axis=1) / np.maximum(np.linalg.norm(r8, axis=1), 1e-30)
+    assert np.all(row_rel <= 2.0 ** -6), float(row_rel.max())
     rel = np.linalg.norm(o - r8) / np.linalg.norm(r8)
     gap = np.linalg.norm(r8 - r16) / np.linalg.norm(r16)
     same = float(np.mean(bits(out)[rows] == ref8))
-    log(f"[fp8] forward {name}: |gpu - oracle| / |oracle| = {rel:.2e}; FP8-vs-BF16 gap "
-        f"{gap:.2e}; {same:.4f} of outputs bit-identical")
-    assert rel <= 2.0 ** -7, rel
-    assert rel < 0.25 * gap, (rel, gap)
+    log(f"[fp8] forward {name}: out element-wise within the down-GEMM bound on the GPU's act "
+        f"codes (worst err/bound {float((err / lim).max()):.3f}); |gpu - oracle| / |oracle| = "
+        f"{rel:.2e} (worst row {row_rel.max():.2e}); FP8-vs-BF16 gap {gap:.2e}; "
+        f"{same:.4f} of outputs bit-identical")
 
 
 def _fwd8(cfg, L, wqd, x):
