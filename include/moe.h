@@ -66,7 +66,8 @@
  *     is valid and enqueues nothing.  A launch failure returns MOE_ERR_HIP.
  *   - Limits: 1 <= E <= 512; 1 <= top_k <= min(E, 16); H and F multiples of
  *     64 in [64, 65536]; 0 <= T; T*top_k <= 2^24 and T*top_k*max(H,F) < 2^31.
- *   - Thread-safe and reentrant (no global mutable state).
+ *   - Thread-safe and reentrant (no global mutable state), except
+ *     moe_forward_static, whose calls share one scratch array per GPU.
  */
 #ifndef MOE_H_
 #define MOE_H_
@@ -85,7 +86,9 @@ typedef enum moe_status {
     MOE_ERR_ALIGN = -3,       /* a device pointer is not 16-byte aligned */
     MOE_ERR_UNSUPPORTED = -4, /* H or F not a multiple of 64, bad enum value */
     MOE_ERR_WORKSPACE = -5,   /* ws_bytes smaller than moe_workspace_bytes() */
-    MOE_ERR_HIP = -6          /* the HIP runtime reported a launch error */
+    MOE_ERR_HIP = -6,         /* the HIP runtime reported a launch error */
+    MOE_ERR_SCRATCH = -7      /* moe_forward_static: the sizes need more than
+                                 the library's static scratch */
 } moe_status;
 
 typedef enum moe_score_fn {
@@ -212,6 +215,26 @@ int moe_forward(int T, int H, int E, int F, int top_k, int score, int renormaliz
                 const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
                 uint16_t* out, int32_t* topk_ids, float* topk_w, int variant,
                 void* ws, size_t ws_bytes, void* stream);
+
+/* moe_forward without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops
+ * and harnesses that forbid hipMalloc.  Arguments and results are those of
+ * moe_forward (same kernels, bit-identical out, topk_ids and topk_w); the
+ * workspace is a static array inside the library, 32 MiB per GPU, which each
+ * GPU the library runs on holds until the process ends.  The call allocates
+ * and frees nothing.  Sizes whose moe_forward workspace
+ * (moe_workspace_bytes(MOE_OP_FORWARD, ...)) exceeds 32 MiB are rejected
+ * with MOE_ERR_SCRATCH before anything is enqueued (e.g. H = 6144, F = 2048,
+ * E = 256, top_k = 8 fits up to T = 132 tokens).  Every call on one GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (on
+ * different streams, or from different threads) race and must be ordered by
+ * the caller.  The array keeps the last call's contents; nothing in the
+ * layer reads scratch it has not written in the same call. */
+int moe_forward_static(int T, int H, int E, int F, int top_k, int score, int renormalize,
+                       const uint16_t* x, const uint16_t* w_router, const float* bias,
+                       const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
+                       uint16_t* out, int32_t* topk_ids, float* topk_w, int variant,
+                       void* stream);
 
 /* Router replay: the whole layer with each token's experts given instead of
  * selected.  The pages describe recording the routing decisions taken while

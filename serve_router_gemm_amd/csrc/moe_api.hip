@@ -1,8 +1,11 @@
 // moe_api.hip -- the C ABI of libmoe (declared in include/moe.h): argument
 // checks, workspace layout and the order of launches.  Every check runs on
-// the host before anything is enqueued; nothing here allocates, synchronizes
-// or keeps state.
+// the host before anything is enqueued; nothing here allocates or
+// synchronizes.  The only state is moe_forward_static's per-GPU scratch array
+// and the device address of it that is looked up once per GPU.
 #include <hip/hip_runtime.h>
+
+#include <mutex>
 
 #include "../../include/moe.h"
 #include "moe_internal.h"
@@ -134,6 +137,90 @@ unsigned char* at(P* base, size_t off) {
     return reinterpret_cast<unsigned char*>(base) + off;
 }
 
+// Checks of moe_forward's arguments other than the workspace (shared with
+// moe_forward_static).
+int check_forward(int T, int H, int E, int F, int top_k, int score, int renormalize,
+                  const uint16_t* x, const uint16_t* w_router, const float* bias,
+                  const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
+                  const uint16_t* out, const int32_t* topk_ids, const float* topk_w,
+                  int variant) {
+    MOE_TRY(check_layer(T, H, E, F, top_k));
+    if (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID) return MOE_ERR_UNSUPPORTED;
+    if (renormalize != 0 && renormalize != 1) return MOE_ERR_UNSUPPORTED;
+    if (score == MOE_SCORE_SOFTMAX && bias) return MOE_ERR_UNSUPPORTED;
+    if (variant != MOE_GEMM_INVARIANT && variant != MOE_GEMM_SPLITK_VARIANT)
+        return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!x || !w_router || !w_gate || !w_up || !w_down || !out) return MOE_ERR_NULL;
+    if (!aligned16(x) || !aligned16(w_router) || !aligned16(w_gate) || !aligned16(w_up) ||
+        !aligned16(w_down) || !aligned16(out) || (bias && !aligned16(bias)) ||
+        (topk_ids && !aligned16(topk_ids)) || (topk_w && !aligned16(topk_w)))
+        return MOE_ERR_ALIGN;
+    return MOE_OK;
+}
+
+// The five steps of the layer on stream s, with the workspace laid out by
+// fwd_layout (at least that many bytes at ws, 256-byte aligned).
+int enqueue_forward(int T, int H, int E, int F, int top_k, int score, int renormalize,
+                    const uint16_t* x, const uint16_t* w_router, const float* bias,
+                    const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
+                    uint16_t* out, int32_t* topk_ids, float* topk_w, int variant, void* ws,
+                    hipStream_t s) {
+    const FwdLayout L = fwd_layout(T, H, E, F, top_k);
+    const int A = T * top_k;
+    int32_t* ids = topk_ids ? topk_ids : reinterpret_cast<int32_t*>(at(ws, L.ids));
+    float* w = topk_w ? topk_w : reinterpret_cast<float*>(at(ws, L.w));
+    int32_t* counts = reinterpret_cast<int32_t*>(at(ws, L.counts));
+    int32_t* offsets = reinterpret_cast<int32_t*>(at(ws, L.offsets));
+    int32_t* perm = reinterpret_cast<int32_t*>(at(ws, L.perm));
+    int32_t* inv = reinterpret_cast<int32_t*>(at(ws, L.inv_perm));
+    float* part = reinterpret_cast<float*>(at(ws, L.route));
+    int32_t* pws = reinterpret_cast<int32_t*>(at(ws, L.permute));
+    int32_t* sched = reinterpret_cast<int32_t*>(at(ws, L.sched));
+    uint16_t* hact = reinterpret_cast<uint16_t*>(at(ws, L.hact));
+    float* y = reinterpret_cast<float*>(at(ws, L.y));
+    MOE_TRY(hip_rc(moe::launch_route(T, H, E, top_k, score, renormalize, x, w_router, bias, ids,
+                                     w, part, s)));
+    MOE_TRY(hip_rc(moe::launch_permute(A, E, ids, counts, offsets, perm, inv, pws, s)));
+    MOE_TRY(hip_rc(moe::launch_gate_up(T, H, E, F, top_k, x, perm, offsets, w_gate, w_up, hact,
+                                       sched, s)));
+    MOE_TRY(hip_rc(moe::launch_down(T, H, E, F, top_k, hact, perm, offsets, w_down, y, variant,
+                                    sched, s)));
+    return hip_rc(launch_combine(T, H, top_k, y, w, out, s));
+}
+
+// ---------------------------------------------------------------------------
+// Static scratch of moe_forward_static: the workspace of moe_forward for
+// callers that cannot allocate device memory.  Every GPU the library runs on
+// holds its own copy of this array until the process ends.  In host code
+// `scratch` names a host-side stand-in, not device memory: the device address
+// of the current GPU's copy is looked up once per device with
+// hipGetSymbolAddress and kept, and only that address is handed to kernels.
+// Nothing in the forward path needs the scratch zeroed on entry (every piece
+// is written before it is read), so the contents a previous call left are
+// harmless; calls that overlap in time on one GPU share the array and race.
+// ---------------------------------------------------------------------------
+constexpr size_t kStaticScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch`, per device
+
+int static_scratch(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -149,6 +236,8 @@ const char* moe_status_string(int status) {
         case MOE_ERR_UNSUPPORTED: return "unsupported argument (H/F not a multiple of 64, or bad enum)";
         case MOE_ERR_WORKSPACE: return "workspace smaller than moe_workspace_bytes()";
         case MOE_ERR_HIP: return "the HIP runtime reported a launch error";
+        case MOE_ERR_SCRATCH:
+            return "the call needs more than the library's static scratch (32 MiB per GPU)";
         default: return "unknown status";
     }
 }
@@ -292,41 +381,29 @@ int moe_forward(int T, int H, int E, int F, int top_k, int score, int renormaliz
                 const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
                 uint16_t* out, int32_t* topk_ids, float* topk_w, int variant, void* ws,
                 size_t ws_bytes, void* stream) {
-    MOE_TRY(check_layer(T, H, E, F, top_k));
-    if (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID) return MOE_ERR_UNSUPPORTED;
-    if (renormalize != 0 && renormalize != 1) return MOE_ERR_UNSUPPORTED;
-    if (score == MOE_SCORE_SOFTMAX && bias) return MOE_ERR_UNSUPPORTED;
-    if (variant != MOE_GEMM_INVARIANT && variant != MOE_GEMM_SPLITK_VARIANT)
-        return MOE_ERR_UNSUPPORTED;
+    MOE_TRY(check_forward(T, H, E, F, top_k, score, renormalize, x, w_router, bias, w_gate, w_up,
+                          w_down, out, topk_ids, topk_w, variant));
     if (T == 0) return MOE_OK;
-    if (!x || !w_router || !w_gate || !w_up || !w_down || !out || !ws) return MOE_ERR_NULL;
-    if (!aligned16(x) || !aligned16(w_router) || !aligned16(w_gate) || !aligned16(w_up) ||
-        !aligned16(w_down) || !aligned16(out) || !aligned16(ws) || (bias && !aligned16(bias)) ||
-        (topk_ids && !aligned16(topk_ids)) || (topk_w && !aligned16(topk_w)))
-        return MOE_ERR_ALIGN;
-    const FwdLayout L = fwd_layout(T, H, E, F, top_k);
-    if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
-    const int A = T * top_k;
-    int32_t* ids = topk_ids ? topk_ids : reinterpret_cast<int32_t*>(at(ws, L.ids));
-    float* w = topk_w ? topk_w : reinterpret_cast<float*>(at(ws, L.w));
-    int32_t* counts = reinterpret_cast<int32_t*>(at(ws, L.counts));
-    int32_t* offsets = reinterpret_cast<int32_t*>(at(ws, L.offsets));
-    int32_t* perm = reinterpret_cast<int32_t*>(at(ws, L.perm));
-    int32_t* inv = reinterpret_cast<int32_t*>(at(ws, L.inv_perm));
-    float* part = reinterpret_cast<float*>(at(ws, L.route));
-    int32_t* pws = reinterpret_cast<int32_t*>(at(ws, L.permute));
-    int32_t* sched = reinterpret_cast<int32_t*>(at(ws, L.sched));
-    uint16_t* hact = reinterpret_cast<uint16_t*>(at(ws, L.hact));
-    float* y = reinterpret_cast<float*>(at(ws, L.y));
-    hipStream_t s = S(stream);
-    MOE_TRY(hip_rc(moe::launch_route(T, H, E, top_k, score, renormalize, x, w_router, bias, ids,
-                                     w, part, s)));
-    MOE_TRY(hip_rc(moe::launch_permute(A, E, ids, counts, offsets, perm, inv, pws, s)));
-    MOE_TRY(hip_rc(moe::launch_gate_up(T, H, E, F, top_k, x, perm, offsets, w_gate, w_up, hact,
-                                       sched, s)));
-    MOE_TRY(hip_rc(moe::launch_down(T, H, E, F, top_k, hact, perm, offsets, w_down, y, variant,
-                                    sched, s)));
-    return hip_rc(launch_combine(T, H, top_k, y, w, out, s));
+    if (!ws) return MOE_ERR_NULL;
+    if (!aligned16(ws)) return MOE_ERR_ALIGN;
+    if (ws_bytes < fwd_layout(T, H, E, F, top_k).total) return MOE_ERR_WORKSPACE;
+    return enqueue_forward(T, H, E, F, top_k, score, renormalize, x, w_router, bias, w_gate, w_up,
+                           w_down, out, topk_ids, topk_w, variant, ws, S(stream));
+}
+
+int moe_forward_static(int T, int H, int E, int F, int top_k, int score, int renormalize,
+                       const uint16_t* x, const uint16_t* w_router, const float* bias,
+                       const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
+                       uint16_t* out, int32_t* topk_ids, float* topk_w, int variant,
+                       void* stream) {
+    MOE_TRY(check_forward(T, H, E, F, top_k, score, renormalize, x, w_router, bias, w_gate, w_up,
+                          w_down, out, topk_ids, topk_w, variant));
+    if (T == 0) return MOE_OK;
+    if (fwd_layout(T, H, E, F, top_k).total > kStaticScratchBytes) return MOE_ERR_SCRATCH;
+    void* ws = nullptr;
+    MOE_TRY(static_scratch(&ws));
+    return enqueue_forward(T, H, E, F, top_k, score, renormalize, x, w_router, bias, w_gate, w_up,
+                           w_down, out, topk_ids, topk_w, variant, ws, S(stream));
 }
 
 int moe_forward_replay(int T, int H, int E, int F, int top_k, int score, int renormalize,

@@ -26,7 +26,8 @@ SPLITK_VARIANT = 1
 FP8_BLOCK = 128
 
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_ALIGN",
-          -4: "MOE_ERR_UNSUPPORTED", -5: "MOE_ERR_WORKSPACE", -6: "MOE_ERR_HIP"}
+          -4: "MOE_ERR_UNSUPPORTED", -5: "MOE_ERR_WORKSPACE", -6: "MOE_ERR_HIP",
+          -7: "MOE_ERR_SCRATCH"}
 
 # name -> (restype, argtypes); must match include/moe.h
 _P = ctypes.c_void_p
@@ -45,6 +46,8 @@ SIGNATURES = {
     "moe_combine": (_I, [_I, _I, _I, _P, _P, _P, _P]),
     "moe_forward": (_I, [_I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I,
                          _P, _Z, _P]),
+    "moe_forward_static": (_I, [_I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                _I, _P]),
     "moe_forward_replay": (_I, [_I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P,
                                 _P, _I, _P, _Z, _P]),
     "moe_topk_large": (_I, [_I, _I, _I, _P, _P, _P, _P, _P]),
@@ -285,6 +288,36 @@ def forward(x, w_router, w_gate, w_up, w_down, top_k, score=SCORE_SOFTMAX, renor
     _check("moe_forward", rc)
     if return_routing:
         return out, topk_ids, topk_w
+    return out
+
+
+def forward_static(x, w_router, w_gate, w_up, w_down, top_k, score=SCORE_SOFTMAX,
+                   renormalize=True, bias=None, variant=INVARIANT, out=None, topk_ids=None,
+                   topk_w=None, stream=None):
+    """moe_forward_static: moe_forward with the library's static per-GPU scratch
+    instead of a workspace (nothing is allocated by the call itself; `out` and
+    the routing outputs must then be passed in)."""
+    T, H = x.shape
+    E, F = w_gate.shape[0], w_gate.shape[1]
+    _dev(x, "x", torch.bfloat16)
+    _dev(w_router, "w_router", torch.bfloat16, (E, H))
+    _dev(w_gate, "w_gate", torch.bfloat16, (E, F, H))
+    _dev(w_up, "w_up", torch.bfloat16, (E, F, H))
+    _dev(w_down, "w_down", torch.bfloat16, (E, H, F))
+    if bias is not None:
+        _dev(bias, "bias", torch.float32, (E,))
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    _dev(out, "out", torch.bfloat16, (T, H))
+    if topk_ids is not None:
+        _dev(topk_ids, "topk_ids", torch.int32, (T, top_k))
+    if topk_w is not None:
+        _dev(topk_w, "topk_w", torch.float32, (T, top_k))
+    rc = lib().moe_forward_static(T, H, E, F, top_k, int(score), int(bool(renormalize)),
+                                  _ptr(x), _ptr(w_router), _ptr(bias), _ptr(w_gate), _ptr(w_up),
+                                  _ptr(w_down), _ptr(out), _ptr(topk_ids), _ptr(topk_w),
+                                  int(variant), _stream(stream))
+    _check("moe_forward_static", rc)
     return out
 
 

@@ -13,7 +13,7 @@ from serve_router_gemm_amd import moe as M
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "moe.h")
 
-OK, NULL, SHAPE, ALIGN, UNSUP, WS = 0, -1, -2, -3, -4, -5
+OK, NULL, SHAPE, ALIGN, UNSUP, WS, SCRATCH = 0, -1, -2, -3, -4, -5, -7
 
 
 def declared_functions():
@@ -54,7 +54,7 @@ def test_binding_arity_matches_header(L):
 
 def test_version_and_status_strings(L):
     assert L.moe_version() >= 10000
-    for rc in (OK, NULL, SHAPE, ALIGN, UNSUP, WS, -6):
+    for rc in (OK, NULL, SHAPE, ALIGN, UNSUP, WS, -6, SCRATCH):
         s = L.moe_status_string(rc).decode()
         assert s and s != "unknown status"
     assert L.moe_status_string(-99).decode() == "unknown status"
@@ -135,6 +135,32 @@ def test_combine_and_forward_checks(L):
     b3[8] = MIS
     assert f(4, 64, 8, 64, 2, 0, 1, *b3, 0, FAKE, 0, None) == ALIGN
     assert f(0, 64, 8, 64, 2, 0, 1, *([None] * 9), 0, None, 0, None) == OK
+
+
+def test_forward_static_checks(L):
+    """moe_forward_static: moe_forward's checks, and sizes whose workspace
+    exceeds the 32 MiB static scratch rejected before any HIP call."""
+    f = L.moe_forward_static
+    base = [FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None, None]
+    b2 = list(base)
+    b2[2] = FAKE
+    assert f(4, 64, 8, 64, 2, 0, 1, *b2, 0, None) == UNSUP      # softmax + bias
+    assert f(4, 64, 8, 64, 2, 0, 1, *base, 3, None) == UNSUP    # variant
+    assert f(4, 64, 8, 96, 2, 0, 1, *base, 0, None) == UNSUP    # F % 64
+    assert f(4, 64, 8, 64, 9, 0, 1, *base, 0, None) == SHAPE    # k > E
+    b0 = list(base)
+    b0[0] = None
+    assert f(4, 64, 8, 64, 2, 0, 1, *b0, 0, None) == NULL
+    b3 = list(base)
+    b3[6] = MIS
+    assert f(4, 64, 8, 64, 2, 0, 1, *b3, 0, None) == ALIGN
+    assert f(0, 64, 8, 64, 2, 0, 1, *([None] * 9), 0, None) == OK
+    # the decode layer (H 6144, E 256, F 2048, top-8) fits up to 132 tokens
+    wb = L.moe_workspace_bytes
+    assert wb(M.OP_FORWARD, 132, 6144, 256, 2048, 8, 0) <= 32 << 20
+    assert wb(M.OP_FORWARD, 133, 6144, 256, 2048, 8, 0) > 32 << 20
+    assert f(133, 6144, 256, 2048, 8, 1, 1, *base, 0, None) == SCRATCH
+    assert f(16384, 6144, 256, 2048, 8, 1, 1, *base, 1, None) == SCRATCH
 
 
 def test_workspace_sizes(L):
