@@ -302,12 +302,13 @@ int moe_permute(int T, int E, int top_k, const int32_t* topk_ids, int32_t* exper
     MOE_TRY(check_tk(T, top_k));
     MOE_TRY(check_e(E, top_k));
     if (T == 0) return MOE_OK;
-    if (!topk_ids || !expert_counts || !expert_offsets || !perm || !inv_perm || !ws)
+    const size_t need = moe::permute_ws_bytes(T * top_k, E);   // 0 for small batches
+    if (!topk_ids || !expert_counts || !expert_offsets || !perm || !inv_perm || (need && !ws))
         return MOE_ERR_NULL;
     if (!aligned16(topk_ids) || !aligned16(expert_counts) || !aligned16(expert_offsets) ||
-        !aligned16(perm) || !aligned16(inv_perm) || !aligned16(ws))
+        !aligned16(perm) || !aligned16(inv_perm) || (ws && !aligned16(ws)))
         return MOE_ERR_ALIGN;
-    if (ws_bytes < moe::permute_ws_bytes(T * top_k, E)) return MOE_ERR_WORKSPACE;
+    if (ws_bytes < need) return MOE_ERR_WORKSPACE;
     return hip_rc(moe::launch_permute(T * top_k, E, topk_ids, expert_counts, expert_offsets, perm,
                                       inv_perm, static_cast<int32_t*>(ws), S(stream)));
 }

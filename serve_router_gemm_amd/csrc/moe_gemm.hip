@@ -31,6 +31,7 @@
 // The split-K variant (down projection only) exists to show what invariance
 // costs and what breaking it does: experts with few tokens have their K range
 // cut into 2..8 parts, each summed on its own and added with fp32 atomics.
+#include <algorithm>
 #include <atomic>
 
 #include "moe_device.h"
@@ -369,6 +370,186 @@ __global__ __launch_bounds__(kP_Threads) void expert_gemm_pipe_kernel(GemmParams
         expert_gemm_body<MODE, false>(P, smem);
 }
 
+// ---------------------------------------------------------------------------
+// Weight-streaming kernel for small batches (the host picks it when the call
+// holds at most 32 tokens, so an expert rarely has more; any count is still
+// handled, in chunks of NB*16 rows).  Such a launch only streams the active
+// experts' weights, and the 256-row tiles above would leave most CUs idle
+// (8 active experts x F/128 output tiles).  Here a work item is one expert x
+// 64 weight rows (gate/up: 32 gate + 32 up rows of the same features), so the
+// same launch spreads over every CU.  4 waves; wave w multiplies 16 weight
+// rows (gate/up: waves 0-1 gate, 2-3 up) by the expert's token rows, with
+// fragments loaded straight into registers, up to 8 K steps ahead.  The list of
+// active experts is built in LDS from the offsets at kernel start, so no
+// separate schedule launch is needed.
+//
+// The MFMA sequence of an output element is the one of the 256 x 256 kernel:
+// v_mfma_f32_16x16x32_bf16, lane l holding row l%16 and K positions
+// 32s + 8(l/16) .. +7 of step s on both operands, accumulators from 0, steps
+// ascending, no split.  So the bits equal those of the tiled kernel.
+// ---------------------------------------------------------------------------
+constexpr int kS_Threads = 256;
+constexpr int kS_MaxE = 512;
+constexpr int kS_GateUpF = 32;         // features per gate/up work item
+constexpr int kS_DownH = 64;           // output rows per down work item
+constexpr int kS_MaxTok = 32;          // the host's threshold (tokens per call)
+
+template <int MODE, int NB, int U>
+__global__ __launch_bounds__(kS_Threads) void expert_gemm_stream_kernel(GemmParams P) {
+    __shared__ int act_list[kS_MaxE];
+    __shared__ int wcnt[kS_Threads / kWave];
+    __shared__ floatx4 xch[2][NB][kWave];   // up waves' accumulators, for the gate waves
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int E = P.E;
+
+    // active experts in ascending order
+    int n_act = 0;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int e0 = 0; e0 < E; e0 += kS_Threads) {
+        const int e = e0 + tid;
+        const bool a = e < E && P.offsets[e + 1] > P.offsets[e];
+        const uint64_t bal = __ballot(a);
+        if (lane == 0) wcnt[wave] = __popcll(bal);
+        __syncthreads();
+        int off = n_act, tot = 0;
+#pragma unroll
+        for (int w = 0; w < kS_Threads / kWave; ++w) {
+            off += (w < wave) ? wcnt[w] : 0;
+            tot += wcnt[w];
+        }
+        if (a) act_list[off + __popcll(bal & below)] = e;
+        n_act += tot;
+        __syncthreads();
+    }
+
+    const int n_tiles = P.n_tiles;
+    const int total = n_act * n_tiles;
+    const int KS = P.K / 32;
+    const int koff = (lane >> 4) * 8;          // this lane's K offset inside a step
+    for (int item = blockIdx.x; item < total; item += gridDim.x) {
+        const int e = act_list[item / n_tiles];
+        const int nt = item - (item / n_tiles) * n_tiles;
+        const int seg0 = P.offsets[e], seg1 = P.offsets[e + 1];
+
+        // this wave's weight row
+        const uint16_t* pa;
+        if (MODE == MODE_GATE_UP) {
+            const int f = min(nt * kS_GateUpF + (wave & 1) * 16 + (lane & 15), P.N - 1);
+            pa = ((wave < 2) ? P.w0 : P.w1) + ((size_t)e * P.N + f) * P.K + koff;
+        } else {
+            const int h = min(nt * kS_DownH + wave * 16 + (lane & 15), P.N - 1);
+            pa = P.w0 + ((size_t)e * P.N + h) * P.K + koff;
+        }
+
+        for (int tb = seg0; tb < seg1; tb += NB * 16) {
+            const uint16_t* pb[NB];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const int p = min(tb + nb * 16 + (lane & 15), seg1 - 1);
+                const int ar = (MODE == MODE_GATE_UP) ? P.perm[p] / P.top_k : p;
+                pb[nb] = P.act + (size_t)ar * P.K + koff;
+            }
+            // a ring of U steps of fragments (U divides KS): slot u holds step
+            // s0 + u; after its MFMAs it is refilled with step s0 + u + U (the
+            // last step again past the end: a cache hit whose value is unused)
+            bf16x8 ra[U], rb[U][NB];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                ra[u] = *reinterpret_cast<const bf16x8*>(pa + (size_t)u * 32);
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    rb[u][nb] = *reinterpret_cast<const bf16x8*>(pb[nb] + (size_t)u * 32);
+                __builtin_amdgcn_sched_barrier(0);   // issue slot by slot, as in the loop
+            }
+            floatx4 acc[NB];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) acc[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+            for (int s0 = 0; s0 < KS; s0 += U) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+                        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra[u], rb[u][nb],
+                                                                           acc[nb], 0, 0, 0);
+                    const int sn = min(s0 + u + U, KS - 1);
+                    ra[u] = *reinterpret_cast<const bf16x8*>(pa + (size_t)sn * 32);
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+                        rb[u][nb] = *reinterpret_cast<const bf16x8*>(pb[nb] + (size_t)sn * 32);
+                    // keep each slot's refill right after its MFMAs, so that
+                    // U - 1 steps stay in flight (the scheduler would otherwise
+                    // group every refill after every MFMA of the ring)
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+
+            // epilogue: lane holds weight rows 4*(lane>>4)+q of token column lane&15
+            const int colq = 4 * (lane >> 4);
+            if (MODE == MODE_GATE_UP) {
+                if (wave >= 2) {
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) xch[wave - 2][nb][lane] = acc[nb];
+                }
+                __syncthreads();
+                if (wave < 2) {
+                    const int f = nt * kS_GateUpF + wave * 16 + colq;
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+                        const int p = tb + nb * 16 + (lane & 15);
+                        if (p >= seg1 || f >= P.N) continue;
+                        const floatx4 up = xch[wave][nb][lane];
+                        uint32_t h[4];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            h[q] = f32_to_bf16_rne(silu_f(acc[nb][q]) * up[q]);
+                        uint2 pk;
+                        pk.x = h[0] | (h[1] << 16);
+                        pk.y = h[2] | (h[3] << 16);
+                        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(P.out) +
+                                                  (size_t)p * P.N + f) = pk;
+                    }
+                }
+                __syncthreads();
+            } else {
+                const int h = nt * kS_DownH + wave * 16 + colq;
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    const int p = tb + nb * 16 + (lane & 15);
+                    if (p >= seg1 || h >= P.N) continue;
+                    *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(P.out) +
+                                                (size_t)P.perm[p] * P.N + h) = acc[nb];
+                }
+            }
+        }
+    }
+}
+
+template <int MODE>
+hipError_t launch_stream(const GemmParams& P0, int T, hipStream_t s) {
+    GemmParams P = P0;
+    P.n_tiles = (MODE == MODE_GATE_UP) ? P.N / kS_GateUpF : P.N / kS_DownH;
+    // at most min(E, T*k) experts are active: no more work items than that
+    const long items = (long)std::min(P.E, T * P.top_k) * P.n_tiles;
+    const int grid = (int)std::max(1L, std::min(items, (long)device_cu_count() * 8));
+    // ring depth: the largest of 8, 4, 2 dividing the K steps (K is a
+    // multiple of 64, so KS = K / 32 is even)
+    const int KS = P.K / 32;
+    const int U = (KS % 8 == 0) ? 8 : (KS % 4 == 0 ? 4 : 2);
+    if (T <= 16) {
+        if (U == 8) expert_gemm_stream_kernel<MODE, 1, 8><<<grid, kS_Threads, 0, s>>>(P);
+        else if (U == 4) expert_gemm_stream_kernel<MODE, 1, 4><<<grid, kS_Threads, 0, s>>>(P);
+        else expert_gemm_stream_kernel<MODE, 1, 2><<<grid, kS_Threads, 0, s>>>(P);
+    } else {
+        if (U == 8) expert_gemm_stream_kernel<MODE, 2, 8><<<grid, kS_Threads, 0, s>>>(P);
+        else if (U == 4) expert_gemm_stream_kernel<MODE, 2, 4><<<grid, kS_Threads, 0, s>>>(P);
+        else expert_gemm_stream_kernel<MODE, 2, 2><<<grid, kS_Threads, 0, s>>>(P);
+    }
+    return hipGetLastError();
+}
+
 // K parts for the split-K variant: more parts the fewer tokens an expert has.
 __device__ __forceinline__ int splitk_parts(int m) {
     return m <= 1 ? 8 : (m <= 4 ? 4 : (m <= 32 ? 2 : 1));
@@ -492,7 +673,12 @@ hipError_t launch_gate_up(int T, int H, int E, int F, int k, const uint16_t* x,
                           const int32_t* perm, const int32_t* offsets, const uint16_t* wg,
                           const uint16_t* wu, uint16_t* h_act, int32_t* sched_ws,
                           hipStream_t s) {
-    (void)T;
+    if (T <= kS_MaxTok && F % kS_GateUpF == 0) {
+        GemmParams P{};
+        P.K = H; P.N = F; P.top_k = k; P.E = E;
+        P.act = x; P.perm = perm; P.offsets = offsets; P.w0 = wg; P.w1 = wu; P.out = h_act;
+        return launch_stream<MODE_GATE_UP>(P, T, s);
+    }
     int32_t* tile_start = sched_ws;
     int32_t* split = sched_ws + E + 1;
     int32_t* tail = sched_ws + 2 * E + 1;
@@ -510,6 +696,12 @@ hipError_t launch_gate_up(int T, int H, int E, int F, int k, const uint16_t* x,
 hipError_t launch_down(int T, int H, int E, int F, int k, const uint16_t* h_act,
                        const int32_t* perm, const int32_t* offsets, const uint16_t* wd,
                        float* y, int variant, int32_t* sched_ws, hipStream_t s) {
+    if (variant == 0 && T <= kS_MaxTok && H % kS_DownH == 0) {
+        GemmParams P{};
+        P.K = F; P.N = H; P.top_k = k; P.E = E;
+        P.act = h_act; P.perm = perm; P.offsets = offsets; P.w0 = wd; P.w1 = nullptr; P.out = y;
+        return launch_stream<MODE_DOWN>(P, T, s);
+    }
     int32_t* tile_start = sched_ws;
     int32_t* split = sched_ws + E + 1;
     int32_t* tail = sched_ws + 2 * E + 1;

@@ -7,7 +7,8 @@
 // integer work and deterministic: assignments a = t*k + j are grouped by
 // expert and kept in ascending a inside each expert (a stable counting sort).
 //
-// Three launches, no atomics whose winner decides a position:
+// Three launches (one for small batches, below), no atomics whose winner
+// decides a position:
 //   hist    one block per chunk of assignments: per-chunk expert counts
 //           (LDS integer atomics: the count does not depend on their order)
 //   scan    one block: per expert, exclusive prefix over chunks; counts;
@@ -125,6 +126,86 @@ __global__ __launch_bounds__(kWave) void permute_scatter_kernel(
     }
 }
 
+// Small batches (A <= kSmallA assignments): the three steps above in one
+// block of 16 waves, so a decode-sized step pays one launch for them.  Wave w
+// takes the w-th chunk of kSmallChunk assignments: per-wave histograms in LDS,
+// then per expert the prefix over waves (the chunk bases) and the exclusive
+// prefix over experts (offsets), then each wave places its chunk in order
+// with the same ballot ranking.  Same permutation as the three launches.
+constexpr int kSmallThreads = 1024;
+constexpr int kSmallWaves = kSmallThreads / kWave;   // 16
+constexpr int kSmallChunk = 256;
+constexpr int kSmallA = kSmallWaves * kSmallChunk;   // 4096
+
+__global__ __launch_bounds__(kSmallThreads) void permute_small_kernel(
+    int A, int E, const int32_t* __restrict__ ids, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm) {
+    __shared__ int hw[kSmallWaves][kMaxExperts];   // per-wave counts, then per-wave bases
+    __shared__ int sc[kMaxExperts];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    for (int i = tid; i < kSmallWaves * kMaxExperts; i += kSmallThreads) (&hw[0][0])[i] = 0;
+    __syncthreads();
+    const int a0 = wave * kSmallChunk;
+    const int a1 = min(A, a0 + kSmallChunk);
+    for (int a = a0 + lane; a < a1; a += kWave) {
+        const int e = ids[a];
+        if (e >= 0 && e < E) atomicAdd(&hw[wave][e], 1);
+    }
+    __syncthreads();
+    // per expert: chunk bases relative to the expert's segment, and its count
+    int run = 0;
+    if (tid < kMaxExperts) {
+        for (int w = 0; w < kSmallWaves; ++w) {
+            const int v = hw[w][tid];
+            hw[w][tid] = run;
+            run += v;
+        }
+        sc[tid] = (tid < E) ? run : 0;
+    }
+    __syncthreads();
+    for (int d = 1; d < kMaxExperts; d <<= 1) {
+        int v = 0;
+        if (tid < kMaxExperts && tid >= d) v = sc[tid - d];
+        __syncthreads();
+        if (tid < kMaxExperts) sc[tid] += v;
+        __syncthreads();
+    }
+    if (tid < E) {
+        const int excl = sc[tid] - run;
+        counts[tid] = run;
+        offsets[tid] = excl;
+        for (int w = 0; w < kSmallWaves; ++w) hw[w][tid] += excl;
+        if (tid == E - 1) offsets[E] = sc[tid];
+    }
+    __syncthreads();
+    const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int s = a0; s < a1; s += kWave) {
+        const int a = s + lane;
+        const int e = (a < a1) ? ids[a] : -1;
+        const bool valid = (e >= 0) && (e < E);
+        uint64_t same = __ballot(valid);
+        if (!valid) same = 0;
+#pragma unroll
+        for (int b = 0; b < kExpertBits; ++b) {
+            const bool bit = valid && ((e >> b) & 1);
+            const uint64_t bal = __ballot(bit);
+            same &= bit ? bal : ~bal;
+        }
+        const int rank = __popcll(same & lower);
+        const int cnt = __popcll(same);
+        int pos = -1;
+        if (valid) pos = hw[wave][e] + rank;
+        // the wave's own row of bases: lanes of one wave, no block barrier
+        __builtin_amdgcn_wave_barrier();
+        if (valid && rank == cnt - 1) hw[wave][e] = pos + 1;
+        __builtin_amdgcn_wave_barrier();
+        if (valid) perm[pos] = a;
+        if (a < a1) inv_perm[a] = pos;
+    }
+}
+
 }  // namespace
 
 int permute_chunk(int A) {
@@ -135,6 +216,7 @@ int permute_chunk(int A) {
 }
 
 size_t permute_ws_bytes(int A, int E) {
+    if (A <= kSmallA) return 0;
     const int chunk = permute_chunk(A);
     const int nchunks = (A + chunk - 1) / chunk;
     return (size_t)nchunks * (size_t)E * sizeof(int32_t);
@@ -142,6 +224,11 @@ size_t permute_ws_bytes(int A, int E) {
 
 hipError_t launch_permute(int A, int E, const int32_t* ids, int32_t* counts, int32_t* offsets,
                           int32_t* perm, int32_t* inv_perm, int32_t* ws, hipStream_t s) {
+    if (A <= kSmallA) {
+        permute_small_kernel<<<1, kSmallThreads, 0, s>>>(A, E, ids, counts, offsets, perm,
+                                                         inv_perm);
+        return hipGetLastError();
+    }
     const int chunk = permute_chunk(A);
     const int nchunks = (A + chunk - 1) / chunk;
     permute_hist_kernel<<<nchunks, kHistThreads, 0, s>>>(A, E, chunk, ids, ws);

@@ -227,6 +227,26 @@ def test_weight_streaming_launch_matches_full_launch():
         f"expert) == the same rows of a 4000-token launch (max {c2.max()})")
 
 
+@pytest.mark.parametrize("name,big", [("mid", 4000), ("dec", 600)])
+def test_small_batch_streaming_launch_matches_tiled_launch(name, big):
+    """Batches of at most 32 tokens run the weight-streaming GEMMs (64 weight
+    rows per work item, fragments straight from memory into registers); larger
+    ones the 256 x 256 tiled kernels.  The MFMA sequence of an element is the
+    same, so the rows of T = 1, 5, 16, 17 and 32 tokens alone equal the same
+    rows inside a large batch bit for bit."""
+    cfg = _cfg(name, T=big)
+    L = layer(cfg)
+    x = I.make_tokens(big, cfg.H, 5151, "cpu").to(DEV)
+    o_big, ids_big, _ = fwd(cfg, L, x)
+    c_big = np.bincount(ids_big.cpu().numpy().reshape(-1), minlength=cfg.E)
+    ob = bits(o_big)
+    for T in (1, 5, 16, 17, 32):
+        o, _, _ = fwd(cfg, L, x[big - T:].contiguous())
+        assert np.array_equal(bits(o), ob[big - T:]), (name, T)
+    log(f"[invariance] {name}: T = 1, 5, 16, 17, 32 (streaming GEMMs) == the same rows of a "
+        f"{big}-token launch (tiled GEMMs, max {c_big.max()} tokens per expert)")
+
+
 def _logp(out_row_bits, P):
     """GPU log-probabilities of one layer output row (bf16 bits) over P."""
     h = I.bits_to_bf16(out_row_bits).reshape(1, -1).to(DEV)

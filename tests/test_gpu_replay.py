@@ -89,3 +89,26 @@ def test_replay_is_batch_invariant():
                                L["w_up"], L["w_down"], w_router=L["w_router"], score=cfg.score,
                                renormalize=cfg.renorm)
         assert torch.equal(one.view(torch.int16), full[t:t + 1].view(torch.int16)), t
+
+
+def test_replay_with_repeated_experts_small_batch():
+    """Recorded ids that repeat an expert inside a token (the router never
+    does): in a 12-token batch expert 3 gets 20 rows, more than one 16-row
+    chunk of the weight-streaming GEMM, and the result matches the oracle's
+    replay (each slot evaluated on its own)."""
+    cfg = _cfg("tiny", T=12)
+    L = layer(cfg)
+    hb = host(cfg)
+    x = I.make_x(cfg, DEV)
+    rng = np.random.default_rng(21)
+    ids_np = rng.integers(0, cfg.E, size=(cfg.T, cfg.k)).astype(np.int32)
+    ids_np[:10, :] = 3
+    ids = torch.from_numpy(ids_np).to(DEV)
+    out, w = M.forward_replay(x, ids, L["w_gate"], L["w_up"], L["w_down"],
+                              w_router=L["w_router"], score=cfg.score, renormalize=cfg.renorm,
+                              return_weights=True)
+    ref_out, ref_w = O.forward_replay(bits(x), hb["w_router"], ids_np, hb["w_gate"],
+                                      hb["w_up"], hb["w_down"], cfg.score, cfg.renorm)
+    weights_close(w.cpu().numpy(), ref_w)
+    stats = assert_out_close(bits(out), ref_out, what="replay repeated experts")
+    log(f"[replay] repeated experts, T=12: {stats}")

@@ -164,6 +164,13 @@ GEMM_CASES = [
     # loads in flight, here over 5 K steps (not a multiple of its 3 stages)
     ("Hedge_streaming", _cfg("mid", T=40, H=320, F=192, E=16, k=4)),
     ("E1_k1", _cfg("tiny", T=300, E=1, k=1)),
+    # batches of at most 32 tokens run the weight-streaming kernel: 16-row and
+    # 32-row token chunks, rings of 8, 4 (F = 1408) and 2 (H = 320, F = 192)
+    # K steps, one expert holding every token
+    ("mid_T20_stream", _cfg("mid", T=20)),
+    ("Hedge_stream_ring2", _cfg("mid", T=24, H=320, F=192, E=16, k=4)),
+    ("dec_T5_stream", _cfg("dec", T=5)),
+    ("E1_k1_T3_stream", _cfg("tiny", T=3, E=1, k=1)),
 ]
 
 
