@@ -99,11 +99,16 @@ typedef enum moe_score_fn {
 typedef enum moe_gemm_variant {
     /* fixed tile, one MFMA instruction, ascending K, no split-K */
     MOE_GEMM_INVARIANT = 0,
-    /* deliberately NOT batch-invariant: the down projection of an expert is
-     * split along K into a number of parts chosen from that expert's token
-     * count, and the parts are summed with fp32 atomics.  Exists to show the
-     * drift that load-dependent kernels cause and to measure what invariance
-     * costs. */
+    /* deliberately NOT batch-invariant, as load-dependent kernels are (the
+     * per-expert kernel and tiling that change with the expert's token
+     * count: Fireworks page "位级一致：前沿训练的差异化关键", section
+     * "为什么比特级一致是一个复杂的问题"): in both expert GEMMs, an expert
+     * with at most 32 tokens has its K range split into parts chosen from its
+     * token count (4 parts up to 4 tokens, else 2; fewer where K does not
+     * divide), each part summed on its own and the parts added in a second
+     * pass; larger experts take the invariant kernel.  Deterministic from run
+     * to run, but a token's bits depend on how many tokens its experts got.
+     * Exists to show that drift and to measure what invariance costs. */
     MOE_GEMM_SPLITK_VARIANT = 1
 } moe_gemm_variant;
 
@@ -170,7 +175,8 @@ int moe_permute(int T, int E, int top_k, const int32_t* topk_ids,
  *   u = x[perm[p]/k] . w_up[e,f,:], fp32 accumulation.
  *   x [device] [T,H]; perm, expert_offsets [device] from moe_permute;
  *   w_gate, w_up [device] [E,F,H]; h_act [device] out [T*k,F] bf16.
- * Always the invariant kernel. */
+ * Always the invariant kernels (the load-dependent variant of this GEMM is
+ * reached through moe_grouped_swiglu, moe_forward and moe_forward_replay). */
 int moe_expert_gate_up(int T, int H, int E, int F, int top_k, const uint16_t* x,
                        const int32_t* perm, const int32_t* expert_offsets,
                        const uint16_t* w_gate, const uint16_t* w_up, uint16_t* h_act,
@@ -181,7 +187,9 @@ int moe_expert_gate_up(int T, int H, int E, int F, int top_k, const uint16_t* x,
  * permuted row p of expert e, y[perm[p], h] = h_act[p,:] . w_down[e,h,:] in
  * fp32, written to assignment order.
  *   h_act [device] [T*k,F] bf16; w_down [device] [E,H,F]; y [device] out
- *   [T*k,H] fp32.  variant: moe_gemm_variant. */
+ *   [T*k,H] fp32.  variant: moe_gemm_variant (the variant's partial sums live
+ *   in the workspace, which is then larger: moe_workspace_bytes with the
+ *   same variant). */
 int moe_expert_down(int T, int H, int E, int F, int top_k, const uint16_t* h_act,
                     const int32_t* perm, const int32_t* expert_offsets,
                     const uint16_t* w_down, float* y, int variant,

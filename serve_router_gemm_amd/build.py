@@ -20,14 +20,18 @@ def sources():
     return sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
 
 
-def command(out: str, extra=()) -> list:
+def flags() -> list:
     # -ffp-contract=off: every fused multiply-add is written out (fmaf / MFMA);
     #   the compiler fuses nothing on its own, so each rounding step is explicit.
     # -packed-fp32-ops off: no v_pk_* fp32 instructions are generated.
-    return [HIPCC, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
             "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include"),
-            *extra, "-o", out, *sources()]
+            "-Wall", "-Wno-unused-function"]
+
+
+def command(out: str, extra=()) -> list:
+    return [HIPCC, *flags(), "-I", os.path.join(ROOT, "include"), *extra, "-o", out,
+            *sources()]
 
 
 def build(verbose: bool = True) -> str:

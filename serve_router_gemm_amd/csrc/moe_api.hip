@@ -61,10 +61,10 @@ int check_layer(int T, int H, int E, int F, int top_k) {
 
 // Workspace layout of moe_forward (every piece 256-byte aligned).
 struct FwdLayout {
-    size_t ids, w, counts, offsets, perm, inv_perm, route, permute, sched, hact, y, total;
+    size_t ids, w, counts, offsets, perm, inv_perm, route, permute, sched, hact, y, var, total;
 };
 
-FwdLayout fwd_layout(int T, int H, int E, int F, int top_k) {
+FwdLayout fwd_layout(int T, int H, int E, int F, int top_k, int variant = 0) {
     const size_t A = (size_t)T * top_k;
     FwdLayout L;
     size_t o = 0;
@@ -79,6 +79,7 @@ FwdLayout fwd_layout(int T, int H, int E, int F, int top_k) {
     L.sched = o; o += up(moe::gemm_sched_ws_bytes(E));
     L.hact = o; o += up(A * (size_t)F * 2);
     L.y = o; o += up(A * (size_t)H * 4);
+    L.var = o; o += variant ? up(moe::gemm_variant_ws_bytes(T, H, E, F, top_k)) : 0;
     L.total = o;
     return L;
 }
@@ -120,8 +121,14 @@ Fwd8Layout fwd8_layout(int T, int H, int E, int F, int top_k) {
     return L;
 }
 
-size_t swiglu_ws(int T, int E, int F, int top_k) {
-    return up(moe::gemm_sched_ws_bytes(E)) + up((size_t)T * top_k * (size_t)F * 2);
+size_t swiglu_ws(int T, int H, int E, int F, int top_k, int variant) {
+    return up(moe::gemm_sched_ws_bytes(E)) + up((size_t)T * top_k * (size_t)F * 2) +
+           (variant ? up(moe::gemm_variant_ws_bytes(T, H, E, F, top_k)) : 0);
+}
+
+size_t down_ws(int T, int H, int E, int F, int top_k, int variant) {
+    return up(moe::gemm_sched_ws_bytes(E)) +
+           (variant ? up(moe::gemm_variant_ws_bytes(T, H, E, F, top_k)) : 0);
 }
 
 hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
@@ -166,7 +173,7 @@ int enqueue_forward(int T, int H, int E, int F, int top_k, int score, int renorm
                     const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
                     uint16_t* out, int32_t* topk_ids, float* topk_w, int variant, void* ws,
                     hipStream_t s) {
-    const FwdLayout L = fwd_layout(T, H, E, F, top_k);
+    const FwdLayout L = fwd_layout(T, H, E, F, top_k, variant);
     const int A = T * top_k;
     int32_t* ids = topk_ids ? topk_ids : reinterpret_cast<int32_t*>(at(ws, L.ids));
     float* w = topk_w ? topk_w : reinterpret_cast<float*>(at(ws, L.w));
@@ -182,10 +189,11 @@ int enqueue_forward(int T, int H, int E, int F, int top_k, int score, int renorm
     MOE_TRY(hip_rc(moe::launch_route(T, H, E, top_k, score, renormalize, x, w_router, bias, ids,
                                      w, part, s)));
     MOE_TRY(hip_rc(moe::launch_permute(A, E, ids, counts, offsets, perm, inv, pws, s)));
+    void* vws = variant ? at(ws, L.var) : nullptr;
     MOE_TRY(hip_rc(moe::launch_gate_up(T, H, E, F, top_k, x, perm, offsets, w_gate, w_up, hact,
-                                       sched, s)));
+                                       sched, s, variant, vws)));
     MOE_TRY(hip_rc(moe::launch_down(T, H, E, F, top_k, hact, perm, offsets, w_down, y, variant,
-                                    sched, s)));
+                                    sched, s, vws)));
     return hip_rc(launch_combine(T, H, top_k, y, w, out, s));
 }
 
@@ -253,17 +261,19 @@ size_t moe_workspace_bytes(int op, int T, int H, int E, int F, int top_k, int va
             if (check_tk(T, top_k) || check_e(E, top_k)) return 0;
             return moe::permute_ws_bytes(T * top_k, E);
         case MOE_OP_GATE_UP:
-        case MOE_OP_DOWN:
             if (check_layer(T, H, E, F, top_k)) return 0;
             return moe::gemm_sched_ws_bytes(E);
+        case MOE_OP_DOWN:
+            if (check_layer(T, H, E, F, top_k)) return 0;
+            return down_ws(T, H, E, F, top_k, variant);
         case MOE_OP_GROUPED_SWIGLU:
             if (check_layer(T, H, E, F, top_k)) return 0;
-            return swiglu_ws(T, E, F, top_k);
+            return swiglu_ws(T, H, E, F, top_k, variant);
         case MOE_OP_COMBINE:
             return 0;
         case MOE_OP_FORWARD:
             if (check_layer(T, H, E, F, top_k)) return 0;
-            return fwd_layout(T, H, E, F, top_k).total;
+            return fwd_layout(T, H, E, F, top_k, variant).total;
         case MOE_OP_GATE_UP_FP8:
         case MOE_OP_DOWN_FP8:
             if (variant != MOE_GEMM_INVARIANT || check_layer_fp8(T, H, E, F, top_k)) return 0;
@@ -339,9 +349,10 @@ int moe_expert_down(int T, int H, int E, int F, int top_k, const uint16_t* h_act
     if (!aligned16(h_act) || !aligned16(perm) || !aligned16(expert_offsets) ||
         !aligned16(w_down) || !aligned16(y) || !aligned16(ws))
         return MOE_ERR_ALIGN;
-    if (ws_bytes < moe::gemm_sched_ws_bytes(E)) return MOE_ERR_WORKSPACE;
+    if (ws_bytes < down_ws(T, H, E, F, top_k, variant)) return MOE_ERR_WORKSPACE;
     return hip_rc(moe::launch_down(T, H, E, F, top_k, h_act, perm, expert_offsets, w_down, y,
-                                   variant, static_cast<int32_t*>(ws), S(stream)));
+                                   variant, static_cast<int32_t*>(ws), S(stream),
+                                   at(ws, up(moe::gemm_sched_ws_bytes(E)))));
 }
 
 int moe_grouped_swiglu(int T, int H, int E, int F, int top_k, const uint16_t* x,
@@ -357,13 +368,15 @@ int moe_grouped_swiglu(int T, int H, int E, int F, int top_k, const uint16_t* x,
     if (!aligned16(x) || !aligned16(perm) || !aligned16(expert_offsets) || !aligned16(w_gate) ||
         !aligned16(w_up) || !aligned16(w_down) || !aligned16(y) || !aligned16(ws))
         return MOE_ERR_ALIGN;
-    if (ws_bytes < swiglu_ws(T, E, F, top_k)) return MOE_ERR_WORKSPACE;
+    if (ws_bytes < swiglu_ws(T, H, E, F, top_k, variant)) return MOE_ERR_WORKSPACE;
     int32_t* sched = static_cast<int32_t*>(ws);
-    uint16_t* hact = reinterpret_cast<uint16_t*>(at(ws, up(moe::gemm_sched_ws_bytes(E))));
+    const size_t o_hact = up(moe::gemm_sched_ws_bytes(E));
+    uint16_t* hact = reinterpret_cast<uint16_t*>(at(ws, o_hact));
+    void* vws = variant ? at(ws, o_hact + up((size_t)T * top_k * (size_t)F * 2)) : nullptr;
     MOE_TRY(hip_rc(moe::launch_gate_up(T, H, E, F, top_k, x, perm, expert_offsets, w_gate, w_up,
-                                       hact, sched, S(stream))));
+                                       hact, sched, S(stream), variant, vws)));
     return hip_rc(moe::launch_down(T, H, E, F, top_k, hact, perm, expert_offsets, w_down, y,
-                                   variant, sched, S(stream)));
+                                   variant, sched, S(stream), vws));
 }
 
 int moe_combine(int T, int H, int top_k, const float* y, const float* topk_w, uint16_t* out,
@@ -387,7 +400,7 @@ int moe_forward(int T, int H, int E, int F, int top_k, int score, int renormaliz
     if (T == 0) return MOE_OK;
     if (!ws) return MOE_ERR_NULL;
     if (!aligned16(ws)) return MOE_ERR_ALIGN;
-    if (ws_bytes < fwd_layout(T, H, E, F, top_k).total) return MOE_ERR_WORKSPACE;
+    if (ws_bytes < fwd_layout(T, H, E, F, top_k, variant).total) return MOE_ERR_WORKSPACE;
     return enqueue_forward(T, H, E, F, top_k, score, renormalize, x, w_router, bias, w_gate, w_up,
                            w_down, out, topk_ids, topk_w, variant, ws, S(stream));
 }
@@ -400,7 +413,8 @@ int moe_forward_static(int T, int H, int E, int F, int top_k, int score, int ren
     MOE_TRY(check_forward(T, H, E, F, top_k, score, renormalize, x, w_router, bias, w_gate, w_up,
                           w_down, out, topk_ids, topk_w, variant));
     if (T == 0) return MOE_OK;
-    if (fwd_layout(T, H, E, F, top_k).total > kStaticScratchBytes) return MOE_ERR_SCRATCH;
+    if (fwd_layout(T, H, E, F, top_k, variant).total > kStaticScratchBytes)
+        return MOE_ERR_SCRATCH;
     void* ws = nullptr;
     MOE_TRY(static_scratch(&ws));
     return enqueue_forward(T, H, E, F, top_k, score, renormalize, x, w_router, bias, w_gate, w_up,
@@ -425,9 +439,10 @@ int moe_forward_replay(int T, int H, int E, int F, int top_k, int score, int ren
         (w_router && !aligned16(w_router)) || (topk_w && !aligned16(topk_w)) ||
         (w_out && !aligned16(w_out)))
         return MOE_ERR_ALIGN;
-    const FwdLayout L = fwd_layout(T, H, E, F, top_k);
+    const FwdLayout L = fwd_layout(T, H, E, F, top_k, variant);
     if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
     const int A = T * top_k;
+    void* vws = variant ? at(ws, L.var) : nullptr;
     int32_t* counts = reinterpret_cast<int32_t*>(at(ws, L.counts));
     int32_t* offsets = reinterpret_cast<int32_t*>(at(ws, L.offsets));
     int32_t* perm = reinterpret_cast<int32_t*>(at(ws, L.perm));
@@ -447,9 +462,9 @@ int moe_forward_replay(int T, int H, int E, int F, int top_k, int score, int ren
     }
     MOE_TRY(hip_rc(moe::launch_permute(A, E, topk_ids, counts, offsets, perm, inv, pws, s)));
     MOE_TRY(hip_rc(moe::launch_gate_up(T, H, E, F, top_k, x, perm, offsets, w_gate, w_up, hact,
-                                       sched, s)));
+                                       sched, s, variant, vws)));
     MOE_TRY(hip_rc(moe::launch_down(T, H, E, F, top_k, hact, perm, offsets, w_down, y, variant,
-                                    sched, s)));
+                                    sched, s, vws)));
     MOE_TRY(hip_rc(moe::launch_zero_unplaced(A, H, inv, y, s)));
     return hip_rc(launch_combine(T, H, top_k, y, w, out, s));
 }

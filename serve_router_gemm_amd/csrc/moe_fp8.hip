@@ -489,7 +489,7 @@ hipError_t launch_gate_up_fp8(int T, int H, int E, int F, int k, const uint8_t* 
     Fp8Params P;
     P.K = H; P.N = F; P.n_tiles = F / kQ_GateUpF; P.top_k = k; P.E = E;
     P.act = xq; P.act_e = xe; P.perm = perm; P.offsets = offsets;
-    P.tile_start = sched_ws; P.tail = sched_ws + 2 * E + 1;
+    P.tile_start = sched_ws; P.tail = sched_ws + E + 1;
     P.w0 = wgq; P.we0 = wge; P.w1 = wuq; P.we1 = wue;
     P.out = aq; P.out_e = ae; P.out_bf16 = act_bf16;
     return launch_fp8_gemm<MODE_GATE_UP>(P, s);
@@ -505,7 +505,7 @@ hipError_t launch_down_fp8(int T, int H, int E, int F, int k, const uint8_t* aq,
     Fp8Params P;
     P.K = F; P.N = H; P.n_tiles = (H + kQ_W - 1) / kQ_W; P.top_k = k; P.E = E;
     P.act = aq; P.act_e = ae; P.perm = perm; P.offsets = offsets;
-    P.tile_start = sched_ws; P.tail = sched_ws + 2 * E + 1;
+    P.tile_start = sched_ws; P.tail = sched_ws + E + 1;
     P.w0 = wdq; P.we0 = wde; P.w1 = nullptr; P.we1 = nullptr;
     P.out = y; P.out_e = nullptr; P.out_bf16 = nullptr;
     return launch_fp8_gemm<MODE_DOWN>(P, s);

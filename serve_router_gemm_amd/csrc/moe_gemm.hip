@@ -28,9 +28,12 @@
 // its L2.  Only the launch work depends on the per-expert counts, never the
 // arithmetic.
 //
-// The split-K variant (down projection only) exists to show what invariance
-// costs and what breaking it does: experts with few tokens have their K range
-// cut into 2..8 parts, each summed on its own and added with fp32 atomics.
+// The load-dependent variant exists to measure what invariance costs and to
+// show what breaking it does: experts with at most 32 tokens have the K range
+// of both GEMMs cut into parts chosen from their token count, each part
+// summed on its own into a workspace and the parts added by a separate pass
+// (deterministic run to run, but an expert's arithmetic then depends on how
+// many tokens the batch sent it); larger experts take the tiled kernel.
 #include <algorithm>
 #include <atomic>
 
@@ -50,7 +53,6 @@ constexpr int kNB = 4;                   // MFMA blocks of 16 token rows per wav
 
 constexpr int MODE_GATE_UP = 0;
 constexpr int MODE_DOWN = 1;
-constexpr int MODE_DOWN_SPLITK = 2;
 
 struct GemmParams {
     int K;            // reduction length: H (gate/up) or F (down)
@@ -61,12 +63,21 @@ struct GemmParams {
     const uint16_t* act;       // gate/up: x [T,H]; down: h_act [A,F]
     const int32_t* perm;
     const int32_t* offsets;    // [E+1]
-    const int32_t* tile_start; // [E+1] prefix of long token tiles (x split parts)
+    const int32_t* tile_start; // [E+1] prefix of long token tiles
     const int32_t* tail;       // [1+E] count, then experts whose last tile is short
-    const int32_t* split;      // [E] K parts per expert (split-K variant)
     const uint16_t* w0;        // w_gate or w_down [E, N, K]
     const uint16_t* w1;        // w_up (gate/up only)
     void* out;                 // h_act bf16 [A,F] or y fp32 [A,H]
+    // streaming kernel: experts with 0 < count <= max_count; in the split
+    // (variant) mode their partial sums go to part [parts_max][R][NW] fp32
+    // (NW = 2F: g then u, or H), rowmap [R][2] (permuted row, parts) and
+    // nrows [1] (rows used)
+    int max_count;
+    int parts_max;
+    int R;
+    float* part;
+    int32_t* rowmap;
+    int32_t* nrows;
 };
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g)); }
@@ -165,21 +176,9 @@ __device__ __forceinline__ void expert_gemm_body(const GemmParams& P, unsigned c
         const TileRef tr = tile_at(lt, total_m, total_long, P.n_tiles, E, P.tile_start, P.tail,
                                    P.offsets);
         const int e = tr.e, local = tr.local, nt = tr.nt;
-        int parts = 1, part = 0, mloc = local;
-        if (MODE == MODE_DOWN_SPLITK) {
-            parts = P.split[e];
-            mloc = local / parts;
-            part = local - mloc * parts;
-        }
         const int seg1 = P.offsets[e + 1];
-        const int p0 = P.offsets[e] + mloc * kP_Tok;
-
-        int kt0 = 0, kt1 = KT;
-        if (MODE == MODE_DOWN_SPLITK && parts > 1) {
-            const int per = (KT + parts - 1) / parts;
-            kt0 = min(KT, part * per);
-            kt1 = min(KT, kt0 + per);
-        }
+        const int p0 = P.offsets[e] + local * kP_Tok;
+        const int kt0 = 0, kt1 = KT;
 
         // Rows of the token tile that hold tokens of this expert (>= 1); the
         // rest is padding.  An 8-row token block with no valid row is not
@@ -339,12 +338,7 @@ __device__ __forceinline__ void expert_gemm_body(const GemmParams& P, unsigned c
                 for (int mb = 0; mb < kMB; ++mb) {
                     const int h = nt * kP_W + wm * 128 + mb * 16 + colq;
                     if (h >= P.N) continue;
-                    if (MODE == MODE_DOWN_SPLITK && parts > 1) {
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) unsafeAtomicAdd(yout + h + q, acc[mb][nb][q]);
-                    } else {
-                        *reinterpret_cast<floatx4*>(yout + h) = acc[mb][nb];
-                    }
+                    *reinterpret_cast<floatx4*>(yout + h) = acc[mb][nb];
                 }
             }
         }
@@ -371,68 +365,137 @@ __global__ __launch_bounds__(kP_Threads) void expert_gemm_pipe_kernel(GemmParams
 }
 
 // ---------------------------------------------------------------------------
-// Weight-streaming kernel for small batches (the host picks it when the call
-// holds at most 32 tokens, so an expert rarely has more; any count is still
-// handled, in chunks of NB*16 rows).  Such a launch only streams the active
-// experts' weights, and the 256-row tiles above would leave most CUs idle
-// (8 active experts x F/128 output tiles).  Here a work item is one expert x
-// 64 weight rows (gate/up: 32 gate + 32 up rows of the same features), so the
-// same launch spreads over every CU.  4 waves; wave w multiplies 16 weight
-// rows (gate/up: waves 0-1 gate, 2-3 up) by the expert's token rows, with
-// fragments loaded straight into registers, up to 8 K steps ahead.  The list of
-// active experts is built in LDS from the offsets at kernel start, so no
-// separate schedule launch is needed.
+// Weight-streaming kernel.  The host picks it for calls of at most 32 tokens
+// (so an expert rarely has more; any count is still handled, in chunks of
+// NB*16 rows).  Such a launch only streams the active experts' weights, and
+// the 256-row tiles above would leave most CUs idle (8 active experts x F/128
+// output tiles).  Here a work item is one expert x 64 weight rows (gate/up:
+// 32 gate + 32 up rows of the same features), so the same launch spreads over
+// every CU.  4 waves; wave w multiplies 16 weight rows (gate/up: waves 0-1
+// gate, 2-3 up) by the expert's token rows, with fragments loaded straight
+// into registers from a ring of up to 8 K steps.  The list of experts it
+// serves (0 < count <= max_count) is built in LDS from the offsets at kernel
+// start, so no separate schedule launch is needed.
 //
 // The MFMA sequence of an output element is the one of the 256 x 256 kernel:
 // v_mfma_f32_16x16x32_bf16, lane l holding row l%16 and K positions
 // 32s + 8(l/16) .. +7 of step s on both operands, accumulators from 0, steps
 // ascending, no split.  So the bits equal those of the tiled kernel.
+//
+// SPLIT (the load-dependent variant only): an expert's K steps are cut into
+// variant_parts(count) parts, one work item each; a part's fp32 sums go to a
+// workspace row of its own and variant_reduce_kernel adds the parts.  The
+// summation order of an element then depends on its expert's token count:
+// this mode is deliberately not batch-invariant.
 // ---------------------------------------------------------------------------
 constexpr int kS_Threads = 256;
 constexpr int kS_MaxE = 512;
 constexpr int kS_GateUpF = 32;         // features per gate/up work item
 constexpr int kS_DownH = 64;           // output rows per down work item
-constexpr int kS_MaxTok = 32;          // the host's threshold (tokens per call)
+constexpr int kS_MaxTok = 32;          // invariant path: tokens per call for this kernel
+constexpr int kV_MaxTok = 32;          // variant: experts up to this count are split
 
-template <int MODE, int NB, int U>
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int t = __shfl_up(v, d, kWave);
+        if (lane >= d) v += t;
+    }
+    return v;
+}
+
+// K parts of a split expert: the fewer tokens, the more parts
+__device__ __forceinline__ int variant_parts(int m, int parts_max) {
+    return min(parts_max, m <= 4 ? 4 : 2);
+}
+
+template <int MODE, int NB, int U, bool SPLIT>
 __global__ __launch_bounds__(kS_Threads) void expert_gemm_stream_kernel(GemmParams P) {
     __shared__ int act_list[kS_MaxE];
-    __shared__ int wcnt[kS_Threads / kWave];
-    __shared__ floatx4 xch[2][NB][kWave];   // up waves' accumulators, for the gate waves
+    __shared__ int item_start[kS_MaxE + 1];    // SPLIT: first work item of a list entry
+    __shared__ int row_start[kS_MaxE + 1];     // SPLIT: first workspace row of an entry
+    __shared__ int wsum[3][kS_Threads / kWave];
+    __shared__ floatx4 xch[2][NB][kWave];      // up waves' accumulators, for the gate waves
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int E = P.E;
+    const int n_tiles = P.n_tiles;
+    const int KS = P.K / 32;
 
-    // active experts in ascending order
-    int n_act = 0;
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    // the experts served, ascending, with (SPLIT) the prefix of their work
+    // items (n_tiles x parts) and of their rows
+    int n_act = 0, items_tot = 0, rows_tot = 0;
     for (int e0 = 0; e0 < E; e0 += kS_Threads) {
         const int e = e0 + tid;
-        const bool a = e < E && P.offsets[e + 1] > P.offsets[e];
-        const uint64_t bal = __ballot(a);
-        if (lane == 0) wcnt[wave] = __popcll(bal);
+        const int m = (e < E) ? P.offsets[e + 1] - P.offsets[e] : 0;
+        const bool a = m > 0 && m <= P.max_count;
+        const int c_items = a ? n_tiles * (SPLIT ? variant_parts(m, P.parts_max) : 1) : 0;
+        const int c_rows = a ? m : 0;
+        const int s_act = wave_incl_scan(a ? 1 : 0, lane);
+        const int s_items = wave_incl_scan(c_items, lane);
+        const int s_rows = wave_incl_scan(c_rows, lane);
+        if (lane == kWave - 1) {
+            wsum[0][wave] = s_act;
+            wsum[1][wave] = s_items;
+            wsum[2][wave] = s_rows;
+        }
         __syncthreads();
-        int off = n_act, tot = 0;
+        int o_act = n_act, o_items = items_tot, o_rows = rows_tot;
 #pragma unroll
         for (int w = 0; w < kS_Threads / kWave; ++w) {
-            off += (w < wave) ? wcnt[w] : 0;
-            tot += wcnt[w];
+            if (w < wave) {
+                o_act += wsum[0][w];
+                o_items += wsum[1][w];
+                o_rows += wsum[2][w];
+            }
+            n_act += wsum[0][w];
+            items_tot += wsum[1][w];
+            rows_tot += wsum[2][w];
         }
-        if (a) act_list[off + __popcll(bal & below)] = e;
-        n_act += tot;
+        if (a) {
+            const int idx = o_act + s_act - 1;
+            act_list[idx] = e;
+            if (SPLIT) {
+                item_start[idx] = o_items + s_items - c_items;
+                row_start[idx] = o_rows + s_rows - c_rows;
+            }
+        }
         __syncthreads();
     }
+    if (SPLIT && tid == 0) {
+        item_start[n_act] = items_tot;
+        row_start[n_act] = rows_tot;
+        if (blockIdx.x == 0) P.nrows[0] = rows_tot;
+    }
+    __syncthreads();
 
-    const int n_tiles = P.n_tiles;
-    const int total = n_act * n_tiles;
-    const int KS = P.K / 32;
+    const int total = SPLIT ? items_tot : n_act * n_tiles;
     const int koff = (lane >> 4) * 8;          // this lane's K offset inside a step
+    const int colq = 4 * (lane >> 4);          // epilogue: this lane's first output row
     for (int item = blockIdx.x; item < total; item += gridDim.x) {
-        const int e = act_list[item / n_tiles];
-        const int nt = item - (item / n_tiles) * n_tiles;
+        int li, nt, part = 0, parts = 1;
+        if (SPLIT) {
+            int lo = 0, hi = n_act - 1;        // the list entry holding this item
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (item_start[mid] <= item) lo = mid; else hi = mid - 1;
+            }
+            li = lo;
+            const int ee = act_list[li];
+            parts = variant_parts(P.offsets[ee + 1] - P.offsets[ee], P.parts_max);
+            const int r = item - item_start[li];
+            nt = r / parts;
+            part = r - nt * parts;
+        } else {
+            li = item / n_tiles;
+            nt = item - li * n_tiles;
+        }
+        const int e = act_list[li];
         const int seg0 = P.offsets[e], seg1 = P.offsets[e + 1];
+        const int ks_part = KS / parts;        // a multiple of U (the host's choice)
+        const int s_begin = part * ks_part, s_end = s_begin + ks_part;
 
         // this wave's weight row
         const uint16_t* pa;
@@ -452,29 +515,30 @@ __global__ __launch_bounds__(kS_Threads) void expert_gemm_stream_kernel(GemmPara
                 const int ar = (MODE == MODE_GATE_UP) ? P.perm[p] / P.top_k : p;
                 pb[nb] = P.act + (size_t)ar * P.K + koff;
             }
-            // a ring of U steps of fragments (U divides KS): slot u holds step
-            // s0 + u; after its MFMAs it is refilled with step s0 + u + U (the
-            // last step again past the end: a cache hit whose value is unused)
+            // a ring of U steps of fragments (U divides the part's steps):
+            // slot u holds step s0 + u; after its MFMAs it is refilled with
+            // step s0 + u + U (the last step again past the end: a cache hit
+            // whose value is unused)
             bf16x8 ra[U], rb[U][NB];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                ra[u] = *reinterpret_cast<const bf16x8*>(pa + (size_t)u * 32);
+                ra[u] = *reinterpret_cast<const bf16x8*>(pa + (size_t)(s_begin + u) * 32);
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
-                    rb[u][nb] = *reinterpret_cast<const bf16x8*>(pb[nb] + (size_t)u * 32);
+                    rb[u][nb] = *reinterpret_cast<const bf16x8*>(pb[nb] + (size_t)(s_begin + u) * 32);
                 __builtin_amdgcn_sched_barrier(0);   // issue slot by slot, as in the loop
             }
             floatx4 acc[NB];
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) acc[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
-            for (int s0 = 0; s0 < KS; s0 += U) {
+            for (int s0 = s_begin; s0 < s_end; s0 += U) {
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb)
                         acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra[u], rb[u][nb],
                                                                            acc[nb], 0, 0, 0);
-                    const int sn = min(s0 + u + U, KS - 1);
+                    const int sn = min(s0 + u + U, s_end - 1);
                     ra[u] = *reinterpret_cast<const bf16x8*>(pa + (size_t)sn * 32);
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb)
@@ -486,9 +550,25 @@ __global__ __launch_bounds__(kS_Threads) void expert_gemm_stream_kernel(GemmPara
                 }
             }
 
-            // epilogue: lane holds weight rows 4*(lane>>4)+q of token column lane&15
-            const int colq = 4 * (lane >> 4);
-            if (MODE == MODE_GATE_UP) {
+            // epilogue: lane holds weight rows colq + q of token column lane&15
+            if (SPLIT) {
+                const int NW = (MODE == MODE_GATE_UP) ? 2 * P.N : P.N;
+                const int col = (MODE == MODE_GATE_UP)
+                                    ? (wave >= 2 ? P.N : 0) + nt * kS_GateUpF + (wave & 1) * 16 + colq
+                                    : nt * kS_DownH + wave * 16 + colq;
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    const int p = tb + nb * 16 + (lane & 15);
+                    if (p >= seg1) continue;
+                    const int q = row_start[li] + (p - seg0);
+                    *reinterpret_cast<floatx4*>(P.part + ((size_t)part * P.R + q) * NW + col) =
+                        acc[nb];
+                    if (nt == 0 && part == 0 && wave == 0 && lane < 16) {
+                        P.rowmap[2 * q] = p;
+                        P.rowmap[2 * q + 1] = parts;
+                    }
+                }
+            } else if (MODE == MODE_GATE_UP) {
                 if (wave >= 2) {
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb) xch[wave - 2][nb][lane] = acc[nb];
@@ -527,32 +607,65 @@ __global__ __launch_bounds__(kS_Threads) void expert_gemm_stream_kernel(GemmPara
     }
 }
 
+// Variant: add the K parts of every split row in ascending part order, then
+// finish the row: act = bf16(silu(g) * u) (gate/up) or y (down).  One block
+// per workspace row; rows past the count the streaming kernel recorded skip.
 template <int MODE>
-hipError_t launch_stream(const GemmParams& P0, int T, hipStream_t s) {
-    GemmParams P = P0;
-    P.n_tiles = (MODE == MODE_GATE_UP) ? P.N / kS_GateUpF : P.N / kS_DownH;
-    // at most min(E, T*k) experts are active: no more work items than that
-    const long items = (long)std::min(P.E, T * P.top_k) * P.n_tiles;
-    const int grid = (int)std::max(1L, std::min(items, (long)device_cu_count() * 8));
-    // ring depth: the largest of 8, 4, 2 dividing the K steps (K is a
-    // multiple of 64, so KS = K / 32 is even)
-    const int KS = P.K / 32;
-    const int U = (KS % 8 == 0) ? 8 : (KS % 4 == 0 ? 4 : 2);
-    if (T <= 16) {
-        if (U == 8) expert_gemm_stream_kernel<MODE, 1, 8><<<grid, kS_Threads, 0, s>>>(P);
-        else if (U == 4) expert_gemm_stream_kernel<MODE, 1, 4><<<grid, kS_Threads, 0, s>>>(P);
-        else expert_gemm_stream_kernel<MODE, 1, 2><<<grid, kS_Threads, 0, s>>>(P);
-    } else {
-        if (U == 8) expert_gemm_stream_kernel<MODE, 2, 8><<<grid, kS_Threads, 0, s>>>(P);
-        else if (U == 4) expert_gemm_stream_kernel<MODE, 2, 4><<<grid, kS_Threads, 0, s>>>(P);
-        else expert_gemm_stream_kernel<MODE, 2, 2><<<grid, kS_Threads, 0, s>>>(P);
+__global__ __launch_bounds__(256) void variant_reduce_kernel(GemmParams P) {
+    const int r = blockIdx.x;
+    if (r >= P.nrows[0]) return;
+    const int p = P.rowmap[2 * r], parts = P.rowmap[2 * r + 1];
+    const int N = P.N;
+    const int NW = (MODE == MODE_GATE_UP) ? 2 * N : N;
+    for (int c = threadIdx.x * 4; c < N; c += 256 * 4) {
+        const float* base = P.part + (size_t)r * NW + c;
+        const size_t plane = (size_t)P.R * NW;
+        floatx4 a = *reinterpret_cast<const floatx4*>(base);
+        for (int pp = 1; pp < parts; ++pp)
+            a = a + *reinterpret_cast<const floatx4*>(base + pp * plane);
+        if (MODE == MODE_GATE_UP) {
+            floatx4 u = *reinterpret_cast<const floatx4*>(base + N);
+            for (int pp = 1; pp < parts; ++pp)
+                u = u + *reinterpret_cast<const floatx4*>(base + N + pp * plane);
+            uint32_t h[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) h[q] = f32_to_bf16_rne(silu_f(a[q]) * u[q]);
+            uint2 pk;
+            pk.x = h[0] | (h[1] << 16);
+            pk.y = h[2] | (h[3] << 16);
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(P.out) + (size_t)p * N + c) = pk;
+        } else {
+            *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(P.out) +
+                                        (size_t)P.perm[p] * N + c) = a;
+        }
     }
+}
+
+template <int MODE, bool SPLIT, int NB>
+hipError_t launch_stream_nb(const GemmParams& P, int U, int grid, hipStream_t s) {
+    if (U == 8) expert_gemm_stream_kernel<MODE, NB, 8, SPLIT><<<grid, kS_Threads, 0, s>>>(P);
+    else if (U == 4) expert_gemm_stream_kernel<MODE, NB, 4, SPLIT><<<grid, kS_Threads, 0, s>>>(P);
+    else expert_gemm_stream_kernel<MODE, NB, 2, SPLIT><<<grid, kS_Threads, 0, s>>>(P);
     return hipGetLastError();
 }
 
-// K parts for the split-K variant: more parts the fewer tokens an expert has.
-__device__ __forceinline__ int splitk_parts(int m) {
-    return m <= 1 ? 8 : (m <= 4 ? 4 : (m <= 32 ? 2 : 1));
+// max_rows: the most token rows an expert served by this launch can have
+// (16 or fewer: one 16-row chunk per pass; else 32-row chunks).
+template <int MODE, bool SPLIT>
+hipError_t launch_stream(const GemmParams& P0, int T, int max_rows, hipStream_t s) {
+    GemmParams P = P0;
+    P.n_tiles = (MODE == MODE_GATE_UP) ? P.N / kS_GateUpF : P.N / kS_DownH;
+    // ring depth: the largest of 8, 4, 2 dividing the K steps of the
+    // shortest part (K is a multiple of 64, so K / 32 is even; the host's
+    // parts_max keeps K / 32 / parts_max even).  (A ring of 16 measured no
+    // faster at decode sizes.)
+    const int ks = P.K / 32 / (SPLIT ? P.parts_max : 1);
+    const int U = (ks % 8 == 0) ? 8 : (ks % 4 == 0 ? 4 : 2);
+    // at most min(E, T*k) experts are active: no more work items than that
+    const long items = (long)std::min(P.E, T * P.top_k) * P.n_tiles * (SPLIT ? P.parts_max : 1);
+    const int grid = (int)std::max(1L, std::min(items, (long)device_cu_count() * 8));
+    if (max_rows <= 16) return launch_stream_nb<MODE, SPLIT, 1>(P, U, grid, s);
+    return launch_stream_nb<MODE, SPLIT, 2>(P, U, grid, s);
 }
 
 // The token-tile list.  A tile whose valid rows fill at most half of it
@@ -565,10 +678,11 @@ __device__ __forceinline__ int splitk_parts(int m) {
 // faster.  The down projection keeps expert order: there a short tile moved
 // away from its expert's long tiles no longer shares their weights, which
 // cost more than the lockstep gained.)
-//   tile_start[e] = number of long tiles of experts e' < e (x split parts);
+//   tile_start[e] = number of long tiles of experts e' < e;
 //   tail[0] = number of short tiles, tail[1..] = their experts, ascending.
-// With reorder = 0 (and in the split-K variant) every tile is listed as long,
-// in expert order.  One block.
+// With reorder = 0 every tile is listed as long, in expert order.  Experts
+// with at most skip_upto tokens get no tile (the load-dependent variant hands
+// them to the split streaming kernel).  One block.
 __device__ __forceinline__ void block_scan_512(int* sc, int e) {
     for (int d = 1; d < 512; d <<= 1) {
         const int v = (e >= d) ? sc[e - d] : 0;
@@ -578,22 +692,20 @@ __device__ __forceinline__ void block_scan_512(int* sc, int e) {
     }
 }
 
-__global__ __launch_bounds__(512) void tile_schedule_kernel(int E, int variant, int reorder,
+__global__ __launch_bounds__(512) void tile_schedule_kernel(int E, int skip_upto, int reorder,
                                                             const int32_t* __restrict__ offsets,
                                                             int32_t* __restrict__ tile_start,
-                                                            int32_t* __restrict__ split,
                                                             int32_t* __restrict__ tail) {
     __shared__ int sl[512], ss[512];
     const int e = threadIdx.x;
     int nlong = 0, nshort = 0;
     if (e < E) {
-        const int m = offsets[e + 1] - offsets[e];
-        const int parts = (variant == 1) ? splitk_parts(m) : 1;
+        int m = offsets[e + 1] - offsets[e];
+        if (m <= skip_upto) m = 0;
         const int ntile = (m + kP_Tok - 1) / kP_Tok;
         const int rem = m % kP_Tok;
-        nshort = (reorder && variant == 0 && rem != 0 && rem <= kP_Tok / 2) ? 1 : 0;
-        nlong = parts * ntile - nshort;
-        split[e] = parts;
+        nshort = (reorder && rem != 0 && rem <= kP_Tok / 2) ? 1 : 0;
+        nlong = ntile - nshort;
     }
     sl[e] = nlong;
     ss[e] = nshort;
@@ -608,25 +720,6 @@ __global__ __launch_bounds__(512) void tile_schedule_kernel(int E, int variant, 
         tile_start[E] = sl[e];
         tail[0] = ss[e];
     }
-}
-
-// Zero the y rows of experts whose down projection is split (they are summed
-// with atomics).  One block per permuted row; rows of unsplit experts skip.
-__global__ __launch_bounds__(256) void zero_split_rows_kernel(int A, int E, int H,
-                                                              const int32_t* __restrict__ perm,
-                                                              const int32_t* __restrict__ offsets,
-                                                              const int32_t* __restrict__ split,
-                                                              float* __restrict__ y) {
-    const int p = blockIdx.x;
-    if (p >= offsets[E]) return;
-    int lo = 0, hi = E - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (offsets[mid] <= p) lo = mid; else hi = mid - 1;
-    }
-    if (split[lo] <= 1) return;
-    float4* row = reinterpret_cast<float4*>(y + (size_t)perm[p] * H);
-    for (int i = threadIdx.x; i < H / 4; i += 256) row[i] = make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
 template <int MODE>
@@ -660,66 +753,112 @@ int device_cu_count() {
     return cu;
 }
 
-size_t gemm_sched_ws_bytes(int E) { return (size_t)(3 * E + 2) * sizeof(int32_t); }
+size_t gemm_sched_ws_bytes(int E) { return (size_t)(2 * E + 2) * sizeof(int32_t); }
 
-hipError_t launch_tile_schedule(int E, int variant, int reorder, const int32_t* offsets,
+namespace {
+
+size_t up256(size_t v) { return (v + 255) / 256 * 256; }
+
+// Variant: K parts of the GEMM with reduction length K (a part's K steps
+// stay even), and rows of the split experts (each has at most kV_MaxTok).
+int variant_parts_max(int K) {
+    const int ks = K / 32;
+    return ks % 8 == 0 ? 4 : (ks % 4 == 0 ? 2 : 1);
+}
+int variant_rows(int T, int k, int E) {
+    return (int)std::min((long)T * k, (long)kV_MaxTok * E);
+}
+size_t variant_gemm_ws(int T, int k, int E, int K, int NW) {
+    const size_t R = (size_t)variant_rows(T, k, E);
+    return up256((size_t)variant_parts_max(K) * R * NW * 4) + up256(R * 8) + 256;
+}
+
+// The variant's split streaming launch and its reduce, on workspace vws.
+template <int MODE>
+hipError_t launch_variant_small(GemmParams P, int T, int k, void* vws, hipStream_t s) {
+    const int NW = (MODE == MODE_GATE_UP) ? 2 * P.N : P.N;
+    P.max_count = kV_MaxTok;
+    P.parts_max = variant_parts_max(P.K);
+    P.R = variant_rows(T, k, P.E);
+    unsigned char* w = static_cast<unsigned char*>(vws);
+    P.part = reinterpret_cast<float*>(w);
+    w += up256((size_t)P.parts_max * P.R * NW * 4);
+    P.rowmap = reinterpret_cast<int32_t*>(w);
+    w += up256((size_t)P.R * 8);
+    P.nrows = reinterpret_cast<int32_t*>(w);
+    hipError_t err = launch_stream<MODE, true>(P, T, std::min(T, kV_MaxTok), s);
+    if (err != hipSuccess) return err;
+    variant_reduce_kernel<MODE><<<P.R, 256, 0, s>>>(P);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t gemm_variant_ws_bytes(int T, int H, int E, int F, int k) {
+    return std::max(variant_gemm_ws(T, k, E, H, 2 * F), variant_gemm_ws(T, k, E, F, H));
+}
+
+hipError_t launch_tile_schedule(int E, int skip_upto, int reorder, const int32_t* offsets,
                                 int32_t* sched_ws, hipStream_t s) {
-    tile_schedule_kernel<<<1, 512, 0, s>>>(E, variant, reorder, offsets, sched_ws,
-                                           sched_ws + E + 1, sched_ws + 2 * E + 1);
+    tile_schedule_kernel<<<1, 512, 0, s>>>(E, skip_upto, reorder, offsets, sched_ws,
+                                           sched_ws + E + 1);
     return hipGetLastError();
 }
 
 hipError_t launch_gate_up(int T, int H, int E, int F, int k, const uint16_t* x,
                           const int32_t* perm, const int32_t* offsets, const uint16_t* wg,
                           const uint16_t* wu, uint16_t* h_act, int32_t* sched_ws,
-                          hipStream_t s) {
-    if (T <= kS_MaxTok && F % kS_GateUpF == 0) {
-        GemmParams P{};
-        P.K = H; P.N = F; P.top_k = k; P.E = E;
-        P.act = x; P.perm = perm; P.offsets = offsets; P.w0 = wg; P.w1 = wu; P.out = h_act;
-        return launch_stream<MODE_GATE_UP>(P, T, s);
+                          hipStream_t s, int variant, void* vws) {
+    GemmParams P{};
+    P.K = H; P.N = F; P.top_k = k; P.E = E;
+    P.act = x; P.perm = perm; P.offsets = offsets; P.w0 = wg; P.w1 = wu; P.out = h_act;
+    if (variant == 0 && T <= kS_MaxTok) {
+        P.max_count = T * k;   // every active expert
+        return launch_stream<MODE_GATE_UP, false>(P, T, T, s);
     }
-    int32_t* tile_start = sched_ws;
-    int32_t* split = sched_ws + E + 1;
-    int32_t* tail = sched_ws + 2 * E + 1;
-    tile_schedule_kernel<<<1, 512, 0, s>>>(E, 0, 1, offsets, tile_start, split, tail);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    GemmParams P;
-    P.K = H; P.N = F; P.n_tiles = (F + kP_GateUpF - 1) / kP_GateUpF; P.top_k = k; P.E = E;
-    P.act = x; P.perm = perm; P.offsets = offsets; P.tile_start = tile_start; P.split = split;
-    P.tail = tail;
-    P.w0 = wg; P.w1 = wu; P.out = h_act;
-    return launch_gemm<MODE_GATE_UP>(P, s);
+    if (variant == 0 || T > kV_MaxTok) {
+        // the tiled kernel: every expert, or (variant) those above kV_MaxTok
+        int32_t* tile_start = sched_ws;
+        int32_t* tail = sched_ws + E + 1;
+        tile_schedule_kernel<<<1, 512, 0, s>>>(E, variant ? kV_MaxTok : 0, 1, offsets, tile_start,
+                                               tail);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+        GemmParams Q = P;
+        Q.n_tiles = (F + kP_GateUpF - 1) / kP_GateUpF;
+        Q.tile_start = tile_start;
+        Q.tail = tail;
+        err = launch_gemm<MODE_GATE_UP>(Q, s);
+        if (err != hipSuccess || variant == 0) return err;
+    }
+    return launch_variant_small<MODE_GATE_UP>(P, T, k, vws, s);
 }
 
 hipError_t launch_down(int T, int H, int E, int F, int k, const uint16_t* h_act,
                        const int32_t* perm, const int32_t* offsets, const uint16_t* wd,
-                       float* y, int variant, int32_t* sched_ws, hipStream_t s) {
-    if (variant == 0 && T <= kS_MaxTok && H % kS_DownH == 0) {
-        GemmParams P{};
-        P.K = F; P.N = H; P.top_k = k; P.E = E;
-        P.act = h_act; P.perm = perm; P.offsets = offsets; P.w0 = wd; P.w1 = nullptr; P.out = y;
-        return launch_stream<MODE_DOWN>(P, T, s);
+                       float* y, int variant, int32_t* sched_ws, hipStream_t s, void* vws) {
+    GemmParams P{};
+    P.K = F; P.N = H; P.top_k = k; P.E = E;
+    P.act = h_act; P.perm = perm; P.offsets = offsets; P.w0 = wd; P.w1 = nullptr; P.out = y;
+    if (variant == 0 && T <= kS_MaxTok) {
+        P.max_count = T * k;
+        return launch_stream<MODE_DOWN, false>(P, T, T, s);
     }
-    int32_t* tile_start = sched_ws;
-    int32_t* split = sched_ws + E + 1;
-    int32_t* tail = sched_ws + 2 * E + 1;
-    tile_schedule_kernel<<<1, 512, 0, s>>>(E, variant, 0, offsets, tile_start, split, tail);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    GemmParams P;
-    P.K = F; P.N = H; P.n_tiles = (H + kP_W - 1) / kP_W; P.top_k = k; P.E = E;
-    P.act = h_act; P.perm = perm; P.offsets = offsets; P.tile_start = tile_start;
-    P.split = split; P.tail = tail; P.w0 = wd; P.w1 = nullptr; P.out = y;
-    if (variant == 1) {
-        const int A = T * k;
-        zero_split_rows_kernel<<<A, 256, 0, s>>>(A, E, H, perm, offsets, split, y);
-        err = hipGetLastError();
+    if (variant == 0 || T > kV_MaxTok) {
+        int32_t* tile_start = sched_ws;
+        int32_t* tail = sched_ws + E + 1;
+        tile_schedule_kernel<<<1, 512, 0, s>>>(E, variant ? kV_MaxTok : 0, 0, offsets, tile_start,
+                                               tail);
+        hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
-        return launch_gemm<MODE_DOWN_SPLITK>(P, s);
+        GemmParams Q = P;
+        Q.n_tiles = (H + kP_W - 1) / kP_W;
+        Q.tile_start = tile_start;
+        Q.tail = tail;
+        err = launch_gemm<MODE_DOWN>(Q, s);
+        if (err != hipSuccess || variant == 0) return err;
     }
-    return launch_gemm<MODE_DOWN>(P, s);
+    return launch_variant_small<MODE_DOWN>(P, T, k, vws, s);
 }
 
 }  // namespace moe

@@ -36,16 +36,24 @@ hipError_t launch_permute(int A, int E, const int32_t* ids, int32_t* counts,
                           int32_t* ws, hipStream_t s);
 
 // expert GEMMs ---------------------------------------------------------------
-size_t gemm_sched_ws_bytes(int E);  // tile_start [E+1] + split [E] + short-tile list [1+E]
+size_t gemm_sched_ws_bytes(int E);  // tile_start [E+1] + short-tile list [1+E]
+// Extra workspace of the load-dependent variant (variant = 1) of either GEMM:
+// the split experts' partial sums and their row map.
+size_t gemm_variant_ws_bytes(int T, int H, int E, int F, int k);
+// variant = 1: the load-dependent variant, with vws holding
+// gemm_variant_ws_bytes() bytes; variant = 0: the invariant kernels.
 hipError_t launch_gate_up(int T, int H, int E, int F, int k, const uint16_t* x,
                           const int32_t* perm, const int32_t* offsets,
                           const uint16_t* wg, const uint16_t* wu, uint16_t* h_act,
-                          int32_t* sched_ws, hipStream_t s);
+                          int32_t* sched_ws, hipStream_t s, int variant = 0,
+                          void* vws = nullptr);
 hipError_t launch_down(int T, int H, int E, int F, int k, const uint16_t* h_act,
                        const int32_t* perm, const int32_t* offsets, const uint16_t* wd,
-                       float* y, int variant, int32_t* sched_ws, hipStream_t s);
-// the tile list of the grouped GEMMs into sched_ws (gemm_sched_ws_bytes(E))
-hipError_t launch_tile_schedule(int E, int variant, int reorder, const int32_t* offsets,
+                       float* y, int variant, int32_t* sched_ws, hipStream_t s,
+                       void* vws = nullptr);
+// the tile list of the grouped GEMMs into sched_ws (gemm_sched_ws_bytes(E));
+// experts with at most skip_upto tokens get no tile
+hipError_t launch_tile_schedule(int E, int skip_upto, int reorder, const int32_t* offsets,
                                 int32_t* sched_ws, hipStream_t s);
 
 // FP8 rollout path ------------------------------------------------------------

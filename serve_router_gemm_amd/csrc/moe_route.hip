@@ -208,6 +208,90 @@ __global__ __launch_bounds__(kRouteThreads) void router_logits_kernel(
     }
 }
 
+// Router logits of a few tokens (T <= TT <= 8), one partial plane per
+// 256-wide chunk: one wave per (chunk, 64 experts), one thread per expert.
+// A thread loads its expert's 512-byte piece of the chunk at once (32 loads
+// in flight) and runs the chunk's ascending fp32 fma chain from +0 for every
+// token from registers; the tokens' pieces sit in LDS as fp32.  The select
+// kernel folds the planes in ascending order: the same chains and the same
+// bits as the tiled kernel above, with one memory latency per block instead
+// of one per 32 hidden indices.
+template <int TT>
+__global__ __launch_bounds__(kWave) void router_logits_few_kernel(
+    int T, int H, int E, const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+    float* __restrict__ part) {
+    __shared__ __attribute__((aligned(16))) float xs[TT][kLogitChunk];
+    const int lane = threadIdx.x;
+    const int c = blockIdx.y;
+    const int k0 = c * kLogitChunk;
+    const int n = min(kLogitChunk, H - k0);           // a multiple of 64
+    const int e = blockIdx.x * kWave + lane;
+    const uint16_t* row = wr + (size_t)min(e, E - 1) * H + k0;
+    uint4 w[kLogitChunk / 8];
+#pragma unroll
+    for (int u = 0; u < kLogitChunk / 8; ++u)
+        if (8 * u < n) w[u] = *reinterpret_cast<const uint4*>(row + 8 * u);
+    // the tokens' pieces: 16-byte loads, all issued before any is used
+    constexpr int kPieces = kLogitChunk / 8;                  // per token
+    constexpr int NX = (TT * kPieces + kWave - 1) / kWave;
+    uint4 xr[NX];
+#pragma unroll
+    for (int i = 0; i < NX; ++i) {
+        const int c = lane + i * kWave;
+        const int t = c / kPieces, kk = 8 * (c % kPieces);
+        xr[i] = make_uint4(0, 0, 0, 0);
+        if (t < TT && t < T && kk < n)
+            xr[i] = *reinterpret_cast<const uint4*>(x + (size_t)t * H + k0 + kk);
+    }
+#pragma unroll
+    for (int i = 0; i < NX; ++i) {
+        const int c = lane + i * kWave;
+        const int t = c / kPieces, kk = 8 * (c % kPieces);
+        if (t >= TT) continue;
+        const uint32_t q[4] = {xr[i].x, xr[i].y, xr[i].z, xr[i].w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            xs[t][kk + j] = bf16_to_f32((j & 1) ? (q[j >> 1] >> 16) : (q[j >> 1] & 0xFFFFu));
+    }
+    __syncthreads();
+    float acc[TT];
+#pragma unroll
+    for (int t = 0; t < TT; ++t) acc[t] = 0.0f;
+#pragma unroll
+    for (int u = 0; u < kLogitChunk / 8; ++u) {
+        if (8 * u >= n) break;
+        const uint32_t q[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+        float wv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            wv[j] = bf16_to_f32((j & 1) ? (q[j >> 1] >> 16) : (q[j >> 1] & 0xFFFFu));
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+            // the token's 8 hidden values: two 16-byte LDS reads (a broadcast)
+            const float4 xa = *reinterpret_cast<const float4*>(&xs[t][8 * u]);
+            const float4 xb = *reinterpret_cast<const float4*>(&xs[t][8 * u + 4]);
+            const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[t] = __builtin_fmaf(xv[j], wv[j], acc[t]);
+        }
+    }
+    if (e < E) {
+        float* plane = part + (size_t)c * T * E;
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+            if (t < T) plane[(size_t)t * E + e] = acc[t];
+    }
+}
+
+template <int TT>
+hipError_t launch_logits_few(int T, int H, int E, const uint16_t* x, const uint16_t* wr,
+                             float* part, hipStream_t s) {
+    const int nchunks = (H + kLogitChunk - 1) / kLogitChunk;
+    dim3 grid((E + kWave - 1) / kWave, nchunks);
+    router_logits_few_kernel<TT><<<grid, kWave, 0, s>>>(T, H, E, x, wr, part);
+    return hipGetLastError();
+}
+
 // Vocabulary projection for a few tokens (T <= TT <= 8): one thread per
 // vocabulary row streams the row in 16-byte loads (two groups of 8 in flight
 // per lane) and runs the same chains as the folded router kernel: within
@@ -233,10 +317,28 @@ __global__ __launch_bounds__(kStreamThreads) void lm_logits_stream_kernel(
     for (int c0 = 0; c0 < H; c0 += kStreamCh) {
         const int n = min(kStreamCh, H - c0);   // a multiple of 64
         __syncthreads();   // every thread done with the previous span
+        // the tokens' span in 16-byte loads, issued before any is used
+        constexpr int kPieces = kStreamCh / 8;                     // per token
+        constexpr int NX = (TT * kPieces + kStreamThreads - 1) / kStreamThreads;
+        uint4 hr[NX];
 #pragma unroll
-        for (int t = 0; t < TT; ++t)
-            for (int i = threadIdx.x; i < n; i += kStreamThreads)
-                xs[t][i] = t < T ? bf16_to_f32(h[(size_t)t * H + c0 + i]) : 0.0f;
+        for (int i = 0; i < NX; ++i) {
+            const int c = threadIdx.x + i * kStreamThreads;
+            const int t = c / kPieces, kk = 8 * (c % kPieces);
+            hr[i] = make_uint4(0, 0, 0, 0);
+            if (t < TT && t < T && kk < n)
+                hr[i] = *reinterpret_cast<const uint4*>(h + (size_t)t * H + c0 + kk);
+        }
+#pragma unroll
+        for (int i = 0; i < NX; ++i) {
+            const int c = threadIdx.x + i * kStreamThreads;
+            const int t = c / kPieces, kk = 8 * (c % kPieces);
+            if (t >= TT) continue;
+            const uint32_t q[4] = {hr[i].x, hr[i].y, hr[i].z, hr[i].w};
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                xs[t][kk + j] = bf16_to_f32((j & 1) ? (q[j >> 1] >> 16) : (q[j >> 1] & 0xFFFFu));
+        }
         __syncthreads();
 #pragma unroll 2
         for (int i0 = 0; i0 < n; i0 += 64) {
@@ -282,6 +384,7 @@ hipError_t launch_lm_stream(int T, int H, int V, const uint16_t* h, const uint16
 }
 
 constexpr int kSelMaxQ = 8;   // experts per lane: E <= 512
+constexpr int kSelBatch = 4;  // partial planes loaded together in the fold
 
 // One wave per token: fold partial logits, keys, top-k, weights.  With
 // `replay` set (router replay), the experts of each slot are read from it
@@ -298,15 +401,33 @@ __global__ __launch_bounds__(256) void router_select_kernel(
 
     float lg[kSelMaxQ];
     uint64_t rk[kSelMaxQ];
+    // fold the partial planes in ascending order, kSelBatch planes of loads
+    // in flight at a time (one dependent load per plane would cost a memory
+    // latency each)
+#pragma unroll
+    for (int q = 0; q < kSelMaxQ; ++q) lg[q] = 0.0f;
+    for (int c0 = 0; c0 < nparts; c0 += kSelBatch) {
+        float pv[kSelBatch][kSelMaxQ];
+#pragma unroll
+        for (int u = 0; u < kSelBatch; ++u)
+#pragma unroll
+            for (int q = 0; q < kSelMaxQ; ++q) {
+                const int e = lane + 64 * q;
+                pv[u][q] = (e < E && c0 + u < nparts)
+                               ? part[((size_t)(c0 + u) * T + t) * E + e] : 0.0f;
+            }
+#pragma unroll
+        for (int u = 0; u < kSelBatch; ++u)
+#pragma unroll
+            for (int q = 0; q < kSelMaxQ; ++q)
+                if (c0 + u < nparts) lg[q] = lg[q] + pv[u][q];
+    }
 #pragma unroll
     for (int q = 0; q < kSelMaxQ; ++q) {
         const int e = lane + 64 * q;
-        lg[q] = 0.0f;
         rk[q] = 0;
         if (e < E) {
-            float v = 0.0f;
-            for (int c = 0; c < nparts; ++c) v = v + part[((size_t)c * T + t) * E + e];
-            lg[q] = v;
+            const float v = lg[q];
             float key;
             if (score == 0) {
                 key = v;
@@ -443,7 +564,12 @@ hipError_t launch_route(int T, int H, int E, int k, int score, int renorm, const
                         float* part_ws, hipStream_t s, const int32_t* replay) {
     const RoutePlan p = route_plan(T, H, E);
     hipError_t err;
-    if (p.split && p.tt == 1) {
+    if (p.split && T <= 8) {
+        if (T <= 1) err = launch_logits_few<1>(T, H, E, x, wr, part_ws, s);
+        else if (T <= 2) err = launch_logits_few<2>(T, H, E, x, wr, part_ws, s);
+        else if (T <= 4) err = launch_logits_few<4>(T, H, E, x, wr, part_ws, s);
+        else err = launch_logits_few<8>(T, H, E, x, wr, part_ws, s);
+    } else if (p.split && p.tt == 1) {
         err = launch_logits<1, 1, true>(T, H, E, x, wr, part_ws, s);
     } else if (p.split) {
         if (p.te == 1) err = launch_logits<8, 1, true>(T, H, E, x, wr, part_ws, s);

@@ -247,6 +247,41 @@ def test_small_batch_streaming_launch_matches_tiled_launch(name, big):
         f"{big}-token launch (tiled GEMMs, max {c_big.max()} tokens per expert)")
 
 
+def test_load_dependent_variant():
+    """The variant splits the K range of both GEMMs for experts with at most 32
+    tokens (parts from the count) and adds the parts in a second pass: it is
+    deterministic run to run, tokens whose experts all hold more than 32
+    tokens get the invariant bits, others drift, and out stays within the
+    layer tolerance of the oracle."""
+    cfg = _cfg("mid", T=300)
+    L = layer(cfg)
+    hb = host(cfg)
+    x = I.make_x(cfg, DEV)
+    o_inv, ids, _ = fwd(cfg, L, x, 0)
+    o_v1, ids_v, _ = fwd(cfg, L, x, 1)
+    o_v2, _, _ = fwd(cfg, L, x, 1)
+    assert torch.equal(ids, ids_v)
+    assert torch.equal(o_v1.view(torch.int16), o_v2.view(torch.int16)), "variant not deterministic"
+    ids_np = ids.cpu().numpy()
+    counts = np.bincount(ids_np.reshape(-1), minlength=cfg.E)
+    big = np.all(counts[ids_np] > 32, axis=1)
+    small = ~big
+    bi, bv = bits(o_inv), bits(o_v1)
+    assert big.any() and small.any(), (int(big.sum()), int(small.sum()))
+    assert np.array_equal(bi[big], bv[big])
+    moved = int(np.sum(bi[small] != bv[small]))
+    assert moved > 0
+    rows = np.sort(np.random.default_rng(6).choice(np.nonzero(small)[0], 24, replace=False))
+    out_r, ids_r, _, gap = O.forward_tokens(rows, bits(x), hb["w_router"], hb["w_gate"],
+                                            hb["w_up"], hb["w_down"], cfg.k, cfg.score,
+                                            cfg.renorm, bias=hb["bias"])
+    assert np.array_equal(ids_np[rows], ids_r)
+    stats = assert_out_close(bv[rows], out_r, what="variant out")
+    log(f"[variant] mid T=300: deterministic; {int(big.sum())} tokens with only >32-token "
+        f"experts bit-identical to the invariant path; {moved} elements of the other "
+        f"{int(small.sum())} tokens moved; vs oracle {stats}")
+
+
 def _logp(out_row_bits, P):
     """GPU log-probabilities of one layer output row (bf16 bits) over P."""
     h = I.bits_to_bf16(out_row_bits).reshape(1, -1).to(DEV)

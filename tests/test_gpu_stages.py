@@ -34,6 +34,11 @@ ROUTE_CASES = [
     ("mid_T4096", _cfg("mid", T=4096), 256),
     ("large_T16384", _cfg("large"), 512),
     ("dec_T1", _cfg("dec", T=1), None),
+    # up to 8 tokens: one wave per (256-wide chunk, 64 experts), 1/2/4/8 token
+    # chains per thread
+    ("mid_T2_few", _cfg("mid", T=2), None),
+    ("dec_T3_few", _cfg("dec", T=3), None),
+    ("dec_T8_few", _cfg("dec", T=8), None),
     ("dec_T64", _cfg("dec", T=64), None),
     ("E512_k16_H320", _cfg("mid", T=300, E=512, k=16, H=320, F=128), None),
     ("kE_E8", _cfg("tiny", T=50, k=8), None),
