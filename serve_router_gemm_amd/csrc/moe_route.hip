@@ -33,15 +33,16 @@ constexpr int kStageK = 32;   // hidden indices staged in LDS per step
 // (T = 64: 0.89 -> 0.85 ms, T = 1: 0.47 -> 0.38 ms); the router, whose
 // operands sit in L2, loses 4% with it and runs without.  The chains, and so
 // the bits, are the same either way.
-// Thread (ty, tx): tokens t0 + ty*TT + i, experts e0 + tx + 32*j.
+// Thread (ty, tx): tokens t0 + ty*TT + i, experts e0 + tx*TE + j (contiguous,
+// so a thread reads its TE expert values of a step as 16-byte LDS reads).
 template <int TT, int TE, bool SPLIT, bool PF>
 __global__ __launch_bounds__(kRouteThreads) void router_logits_kernel(
     int T, int H, int E, const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
     float* __restrict__ part) {
     constexpr int BT = 8 * TT;
     constexpr int BE = 32 * TE;
-    __shared__ float xs[kStageK][BT];
-    __shared__ float ws[kStageK][BE];
+    __shared__ __attribute__((aligned(16))) float xs[kStageK][BT];
+    __shared__ __attribute__((aligned(16))) float ws[kStageK][BE];
 
     const int tid = threadIdx.x;
     const int tx = tid & 31, ty = tid >> 5;
@@ -122,7 +123,7 @@ __global__ __launch_bounds__(kRouteThreads) void router_logits_kernel(
 #pragma unroll
                 for (int i = 0; i < TT; ++i) xv[i] = xs[kk][ty * TT + i];
 #pragma unroll
-                for (int j = 0; j < TE; ++j) wv[j] = ws[kk][tx + 32 * j];
+                for (int j = 0; j < TE; ++j) wv[j] = ws[kk][tx * TE + j];
 #pragma unroll
                 for (int i = 0; i < TT; ++i)
 #pragma unroll
@@ -175,7 +176,7 @@ __global__ __launch_bounds__(kRouteThreads) void router_logits_kernel(
 #pragma unroll
                 for (int i = 0; i < TT; ++i) xv[i] = xs[kk][ty * TT + i];
 #pragma unroll
-                for (int j = 0; j < TE; ++j) wv[j] = ws[kk][tx + 32 * j];
+                for (int j = 0; j < TE; ++j) wv[j] = ws[kk][tx * TE + j];
 #pragma unroll
                 for (int i = 0; i < TT; ++i)
 #pragma unroll
@@ -202,7 +203,7 @@ __global__ __launch_bounds__(kRouteThreads) void router_logits_kernel(
         if (t >= T) continue;
 #pragma unroll
         for (int j = 0; j < TE; ++j) {
-            const int e = e0 + tx + 32 * j;
+            const int e = e0 + tx * TE + j;
             if (e < E) plane[(size_t)t * E + e] = SPLIT ? acc[i][j] : total[i][j];
         }
     }
@@ -522,11 +523,16 @@ hipError_t launch_logits(int T, int H, int E, const uint16_t* x, const uint16_t*
 
 }  // namespace
 
+// 8 tokens x 8 contiguous experts per thread for E > 128: 64 fmas per four
+// 16-byte LDS reads (large layer 0.90 -> 0.86 ms alone, same bits; 4 tokens
+// x 8 experts, for twice the blocks, measured 1.00 ms)
+constexpr int kBigTT = 8;
+
 RoutePlan route_plan(int T, int H, int E) {
     RoutePlan p;
     const int nchunks = (H + kLogitChunk - 1) / kLogitChunk;
-    // folded tiles: 64 tokens x up to 128 experts per block
-    const int te = E <= 32 ? 1 : (E <= 64 ? 2 : 4);
+    // folded tiles: 64 tokens x up to 256 experts per block
+    const int te = E <= 32 ? 1 : (E <= 64 ? 2 : (E <= 128 ? 4 : 8));
     const long blocks = (long)((T + 63) / 64) * ((E + 32 * te - 1) / (32 * te));
     if (blocks >= 512 || nchunks == 1) {
         p.split = 0; p.nparts = 1; p.tt = 8; p.te = te;
@@ -574,13 +580,16 @@ hipError_t launch_route(int T, int H, int E, int k, int score, int renorm, const
     } else if (p.split) {
         if (p.te == 1) err = launch_logits<8, 1, true>(T, H, E, x, wr, part_ws, s);
         else if (p.te == 2) err = launch_logits<8, 2, true>(T, H, E, x, wr, part_ws, s);
-        else err = launch_logits<8, 4, true>(T, H, E, x, wr, part_ws, s);
+        else if (p.te == 4) err = launch_logits<8, 4, true>(T, H, E, x, wr, part_ws, s);
+        else err = launch_logits<kBigTT, 8, true>(T, H, E, x, wr, part_ws, s);
     } else if (p.te == 1) {
         err = launch_logits<8, 1, false>(T, H, E, x, wr, part_ws, s);
     } else if (p.te == 2) {
         err = launch_logits<8, 2, false>(T, H, E, x, wr, part_ws, s);
-    } else {
+    } else if (p.te == 4) {
         err = launch_logits<8, 4, false>(T, H, E, x, wr, part_ws, s);
+    } else {
+        err = launch_logits<kBigTT, 8, false>(T, H, E, x, wr, part_ws, s);
     }
     if (err != hipSuccess) return err;
     router_select_kernel<<<(T + 3) / 4, 256, 0, s>>>(T, E, k, p.nparts, score, renorm, part_ws,
