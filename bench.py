@@ -35,7 +35,7 @@ METRIC = "MoE-layer tokens/s + MFMA util; bitwise-identical output across batch 
 # HBM bytes per launch of the gate/up kernel from rocprofv3 FETCH_SIZE (x2.0) and
 # WRITE_SIZE (x1.0) on the large workload (profiles/expert_gemm_large_T16384.md),
 # valid only for the sources and build flags they were taken on (gemm_source_hash).
-TRAFFIC = {"kernel_sha256_prefix": "unmeasured", "workload": "large", "bytes": None}
+TRAFFIC = {"kernel_sha256_prefix": "4bba54338f2f6fb0", "workload": "large", "bytes": 23.48e9}
 GEMM_SOURCES = ("moe_gemm.hip", "moe_gemm_tiles.h", "moe_device.h", "moe_internal.h")
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
@@ -59,6 +59,9 @@ def parse():
     ap.add_argument("--cpu-sample", type=int, default=None,
                     help="tokens of the oracle CPU baseline (0 disables)")
     ap.add_argument("--no-check", action="store_true", help="skip the probe invariance check")
+    ap.add_argument("--step-only", action="store_true",
+                    help="time the step and stop: no variant, replay, top-k, FP8 or decode "
+                         "legs (short profiler runs)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 3 plain device copies of MIB MiB (HBM counter calibration)")
     ap.add_argument("--print-gemm-hash", action="store_true",
@@ -245,7 +248,7 @@ def main():
     # many output elements and probe bits move.  Timed with the same events
     # per step as the invariant step.
     variant_res = None
-    if args.variant == 0:
+    if args.variant == 0 and not args.step_only:
         out_inv = out.clone()
         ws_sv = M.workspace(M.OP_GROUPED_SWIGLU, T, H, E, F, k, 1)
 
@@ -309,7 +312,7 @@ def main():
     # Router replay: the same layer with the recorded routing of the step (ids
     # and weights) handed back in; must reproduce the routed output bitwise.
     replay_res = None
-    if args.variant == 0:
+    if args.variant == 0 and not args.step_only:
         ws_f = M.workspace(M.OP_FORWARD, T, H, E, F, k)
         rep = M.forward_replay(x, ids, L["w_gate"], L["w_up"], L["w_down"], topk_w=w,
                                score=cfg.score, renormalize=cfg.renorm, ws=ws_f)
@@ -328,7 +331,7 @@ def main():
     # Sparse-indexer top-k at the pages' shape (top 2048 per query over a
     # 128K-token context; 1024 queries), timed on its own.
     topk_res = None
-    if cfg.name == "large":
+    if cfg.name == "large" and not args.step_only:
         Qs, Ns, ks = 1024, 131072, 2048
         sc = torch.randn((Qs, Ns), generator=torch.Generator().manual_seed(3)).to(dev)
         M.topk_large(sc, ks, want_vals=False)
@@ -350,7 +353,7 @@ def main():
     # the entry points moe_forward_fp8 chains and checked bitwise against it;
     # its output against the bf16 layer's, and probe invariance.
     fp8_res, out8 = None, None
-    if args.variant == 0 and cfg.name in ("large", "dec"):
+    if args.variant == 0 and cfg.name in ("large", "dec") and not args.step_only:
         tq = time.perf_counter()
         wq8 = M.quantize_weights_fp8(L["w_gate"], L["w_up"], L["w_down"])
         torch.cuda.synchronize()
@@ -435,7 +438,7 @@ def main():
     # projection, log-softmax, k3 of this batch against itself), timed on its
     # own; the projection streams V x H bf16 weights.
     decode_res = None
-    if cfg.name == "dec":
+    if cfg.name == "dec" and not args.step_only:
         V = 65536
         gp = torch.Generator().manual_seed(I.PROJ_SEED)
         P = torch.randn((V, H), generator=gp).to(torch.bfloat16).to(dev)
