@@ -444,10 +444,12 @@ def main():
         P = torch.randn((V, H), generator=gp).to(torch.bfloat16).to(dev)
         z = torch.empty((T, V), dtype=torch.float32, device=dev)
         lp = torch.empty_like(z)
+        ws_ls = M.workspace(M.OP_LOG_SOFTMAX, T, V, 1, 64, 1)
+        ws_k3 = M.workspace(M.OP_K3, T, V, 1, 64, 1)
         for _ in range(2):
             M.lm_head_logits(out, P, z=z)
-            M.log_softmax(z, out=lp)
-            M.k3(lp, lp)
+            M.log_softmax(z, out=lp, ws=ws_ls)
+            M.k3(lp, lp, ws=ws_k3)
         KD = max(5, min(K, 20))
         evd = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(KD)]
         torch.cuda.synchronize()
@@ -455,9 +457,9 @@ def main():
             evd[i][0].record(stream)
             M.lm_head_logits(out, P, z=z)
             evd[i][1].record(stream)
-            M.log_softmax(z, out=lp)
+            M.log_softmax(z, out=lp, ws=ws_ls)
             evd[i][2].record(stream)
-            kmean, _, _ = M.k3(lp, lp)
+            kmean, _, _ = M.k3(lp, lp, ws=ws_k3)
             evd[i][3].record(stream)
         torch.cuda.synchronize()
         dms = [float(np.mean([evd[i][j].elapsed_time(evd[i][j + 1]) for i in range(KD)]))
@@ -476,7 +478,10 @@ def main():
         decode_res = {"vocab": V, "lm_head_ms": round(dms[0], 4),
                       "lm_head_hbm_frac": round(proj_bytes / (dms[0] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                       "lm_head_valu_tflops": round(2.0 * T * V * H / (dms[0] * 1e-3) / 1e12, 2),
-                      "log_softmax_ms": round(dms[1], 4), "k3_ms": round(dms[2], 4),
+                      "log_softmax_ms": round(dms[1], 4),
+                      "log_softmax_hbm_frac": round(8.0 * T * V / (dms[1] * 1e-3) / 1e9
+                                                    / PEAK_HBM_GBS, 4),
+                      "k3_ms": round(dms[2], 4),
                       "k3_self": float(kmean.max().item())}
         del P, z, lp
 

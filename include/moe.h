@@ -122,7 +122,9 @@ typedef enum moe_op {
     MOE_OP_FORWARD = 6,
     MOE_OP_GATE_UP_FP8 = 7,
     MOE_OP_DOWN_FP8 = 8,
-    MOE_OP_FORWARD_FP8 = 9
+    MOE_OP_FORWARD_FP8 = 9,
+    MOE_OP_LOG_SOFTMAX = 10,  /* moe_workspace_bytes: pass the vocabulary V as H */
+    MOE_OP_K3 = 11            /* moe_workspace_bytes: pass the vocabulary V as H */
 } moe_op;
 
 /* Bytes of device scratch the entry point `op` needs for these sizes
@@ -299,7 +301,10 @@ int moe_topk_large(int Q, int N, int k, const float* scores, const int32_t* leng
  * "混合专家模型更难对齐").  The pages fix neither the projection's order nor
  * the sums; these entry points pin both, so a token's results never depend
  * on what else is in the call.  Limits: H a multiple of 64 in [64, 65536];
- * 1 <= V <= 2^20; 0 <= T; T*V < 2^31.  No workspace.
+ * 1 <= V <= 2^20; 0 <= T; T*V < 2^31.  moe_log_softmax and moe_k3 take a
+ * workspace of moe_workspace_bytes(MOE_OP_LOG_SOFTMAX / MOE_OP_K3, T, V, ...)
+ * bytes (the per-row segment maxima and chunk sums, about 4 KB per row at
+ * V = 65536); the vocabulary projection takes none.
  * ------------------------------------------------------------------------ */
 
 /* Vocabulary projection (LM head) of layer outputs:
@@ -317,8 +322,9 @@ int moe_lm_head_logits(int T, int H, int V, const uint16_t* h, const uint16_t* p
  *   exp32 and log32 are the exponential and logarithm correctly rounded to
  *   fp32 (evaluated as the fp64 function rounded once).
  *   z [device] [T,V] fp32; logp [device] out [T,V] fp32; logp == z allowed
- *   (in place).  NaN inputs give NaN rows. */
-int moe_log_softmax(int T, int V, const float* z, float* logp, void* stream);
+ *   (in place).  NaN inputs give NaN rows.  ws [device]: the workspace. */
+int moe_log_softmax(int T, int V, const float* z, float* logp, void* ws, size_t ws_bytes,
+                    void* stream);
 
 /* Schulman's k3 estimator, r = p_ref / p_test, per row t:
  *   d_v = logp_ref[t,v] - logp_test[t,v] (fp64),
@@ -330,9 +336,9 @@ int moe_log_softmax(int T, int V, const float* z, float* logp, void* stream);
  *                  logp_test[t,0] is NaN; other NaNs are skipped);
  *   k3_greedy[t] = expm1(d) - d at v = greedy[t] (unweighted).
  *   logp_ref, logp_test [device] [T,V] fp32; k3_mean, k3_greedy [device] out
- *   [T] fp64; greedy [device] out [T] int32. */
+ *   [T] fp64; greedy [device] out [T] int32; ws [device]: the workspace. */
 int moe_k3(int T, int V, const float* logp_ref, const float* logp_test, double* k3_mean,
-           double* k3_greedy, int32_t* greedy, void* stream);
+           double* k3_greedy, int32_t* greedy, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * FP8 rollout path.  The pages' large-MoE recipe trains in BF16, samples

@@ -281,6 +281,12 @@ size_t moe_workspace_bytes(int op, int T, int H, int E, int F, int top_k, int va
         case MOE_OP_FORWARD_FP8:
             if (variant != MOE_GEMM_INVARIANT || check_layer_fp8(T, H, E, F, top_k)) return 0;
             return fwd8_layout(T, H, E, F, top_k).total;
+        case MOE_OP_LOG_SOFTMAX:   // H is the vocabulary size V
+            if (check_vocab(T, H)) return 0;
+            return moe::log_softmax_ws_bytes(T, H);
+        case MOE_OP_K3:            // H is the vocabulary size V
+            if (check_vocab(T, H)) return 0;
+            return moe::k3_ws_bytes(T, H);
         default:
             return 0;
     }
@@ -496,23 +502,26 @@ int moe_lm_head_logits(int T, int H, int V, const uint16_t* h, const uint16_t* p
     return hip_rc(moe::launch_lm_logits(T, H, V, h, proj, z, S(stream)));
 }
 
-int moe_log_softmax(int T, int V, const float* z, float* logp, void* stream) {
+int moe_log_softmax(int T, int V, const float* z, float* logp, void* ws, size_t ws_bytes,
+                    void* stream) {
     MOE_TRY(check_vocab(T, V));
     if (T == 0) return MOE_OK;
-    if (!z || !logp) return MOE_ERR_NULL;
-    if (!aligned16(z) || !aligned16(logp)) return MOE_ERR_ALIGN;
-    return hip_rc(moe::launch_log_softmax(T, V, z, logp, S(stream)));
+    if (!z || !logp || !ws) return MOE_ERR_NULL;
+    if (!aligned16(z) || !aligned16(logp) || !aligned16(ws)) return MOE_ERR_ALIGN;
+    if (ws_bytes < moe::log_softmax_ws_bytes(T, V)) return MOE_ERR_WORKSPACE;
+    return hip_rc(moe::launch_log_softmax(T, V, z, logp, ws, S(stream)));
 }
 
 int moe_k3(int T, int V, const float* logp_ref, const float* logp_test, double* k3_mean,
-           double* k3_greedy, int32_t* greedy, void* stream) {
+           double* k3_greedy, int32_t* greedy, void* ws, size_t ws_bytes, void* stream) {
     MOE_TRY(check_vocab(T, V));
     if (T == 0) return MOE_OK;
-    if (!logp_ref || !logp_test || !k3_mean || !k3_greedy || !greedy) return MOE_ERR_NULL;
+    if (!logp_ref || !logp_test || !k3_mean || !k3_greedy || !greedy || !ws) return MOE_ERR_NULL;
     if (!aligned16(logp_ref) || !aligned16(logp_test) || !aligned16(k3_mean) ||
-        !aligned16(k3_greedy) || !aligned16(greedy))
+        !aligned16(k3_greedy) || !aligned16(greedy) || !aligned16(ws))
         return MOE_ERR_ALIGN;
-    return hip_rc(moe::launch_k3(T, V, logp_ref, logp_test, k3_mean, k3_greedy, greedy,
+    if (ws_bytes < moe::k3_ws_bytes(T, V)) return MOE_ERR_WORKSPACE;
+    return hip_rc(moe::launch_k3(T, V, logp_ref, logp_test, k3_mean, k3_greedy, greedy, ws,
                                  S(stream)));
 }
 

@@ -76,9 +76,12 @@ constexpr int kSumChunk = 256;     // fixed chunk of the vocabulary sums
 constexpr int kMaxVocab = 1 << 20;
 hipError_t launch_lm_logits(int T, int H, int V, const uint16_t* h, const uint16_t* proj,
                             float* z, hipStream_t s);
-hipError_t launch_log_softmax(int T, int V, const float* z, float* logp, hipStream_t s);
+size_t log_softmax_ws_bytes(int T, int V);
+size_t k3_ws_bytes(int T, int V);
+hipError_t launch_log_softmax(int T, int V, const float* z, float* logp, void* ws,
+                              hipStream_t s);
 hipError_t launch_k3(int T, int V, const float* logp_ref, const float* logp_test,
-                     double* mean, double* greedy_k3, int32_t* greedy, hipStream_t s);
+                     double* mean, double* greedy_k3, int32_t* greedy, void* ws, hipStream_t s);
 
 // large-k top-k (sparse attention indexer) ------------------------------------
 constexpr int kMaxTopkLarge = 4096;

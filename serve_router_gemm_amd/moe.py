@@ -22,7 +22,7 @@ INVARIANT = 0
 SPLITK_VARIANT = 1
 
 (OP_ROUTE, OP_PERMUTE, OP_GATE_UP, OP_DOWN, OP_GROUPED_SWIGLU, OP_COMBINE, OP_FORWARD,
- OP_GATE_UP_FP8, OP_DOWN_FP8, OP_FORWARD_FP8) = range(10)
+ OP_GATE_UP_FP8, OP_DOWN_FP8, OP_FORWARD_FP8, OP_LOG_SOFTMAX, OP_K3) = range(12)
 FP8_BLOCK = 128
 
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_ALIGN",
@@ -52,8 +52,8 @@ SIGNATURES = {
                                 _P, _I, _P, _Z, _P]),
     "moe_topk_large": (_I, [_I, _I, _I, _P, _P, _P, _P, _P]),
     "moe_lm_head_logits": (_I, [_I, _I, _I, _P, _P, _P, _P]),
-    "moe_log_softmax": (_I, [_I, _I, _P, _P, _P]),
-    "moe_k3": (_I, [_I, _I, _P, _P, _P, _P, _P, _P]),
+    "moe_log_softmax": (_I, [_I, _I, _P, _P, _P, _Z, _P]),
+    "moe_k3": (_I, [_I, _I, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "moe_quantize_fp8": (_I, [_I, _I, _I, _P, _P, _P, _P]),
     "moe_expert_gate_up_fp8": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                     _P, _P, _Z, _P]),
@@ -368,19 +368,20 @@ def lm_head_logits(h, proj, z=None, stream=None):
     return z
 
 
-def log_softmax(z, out=None, stream=None):
+def log_softmax(z, out=None, ws=None, stream=None):
     """moe_log_softmax: fp32 log-softmax over the last axis (out may be z)."""
     T, V = z.shape
     _dev(z, "z", torch.float32, (T, V))
     if out is None:
         out = torch.empty_like(z)
     _dev(out, "out", torch.float32, (T, V))
-    rc = lib().moe_log_softmax(T, V, _ptr(z), _ptr(out), _stream(stream))
+    ws = _ws(ws, workspace_bytes(OP_LOG_SOFTMAX, T, V, 1, 64, 1), z.device)
+    rc = lib().moe_log_softmax(T, V, _ptr(z), _ptr(out), _ptr(ws), ws.numel(), _stream(stream))
     _check("moe_log_softmax", rc)
     return out
 
 
-def k3(logp_ref, logp_test, stream=None):
+def k3(logp_ref, logp_test, ws=None, stream=None):
     """moe_k3: -> (k3_mean [T] fp64, k3_greedy [T] fp64, greedy [T] int32)."""
     T, V = logp_test.shape
     _dev(logp_ref, "logp_ref", torch.float32, (T, V))
@@ -389,8 +390,9 @@ def k3(logp_ref, logp_test, stream=None):
     mean = torch.empty(T, dtype=torch.float64, device=dev)
     gk3 = torch.empty(T, dtype=torch.float64, device=dev)
     g = torch.empty(T, dtype=torch.int32, device=dev)
+    ws = _ws(ws, workspace_bytes(OP_K3, T, V, 1, 64, 1), dev)
     rc = lib().moe_k3(T, V, _ptr(logp_ref), _ptr(logp_test), _ptr(mean), _ptr(gk3), _ptr(g),
-                      _stream(stream))
+                      _ptr(ws), ws.numel(), _stream(stream))
     _check("moe_k3", rc)
     return mean, gk3, g
 

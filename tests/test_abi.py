@@ -195,16 +195,27 @@ def test_decode_measurement_checks(L):
     assert lm(-1, 64, 100, FAKE, FAKE, FAKE, None) == SHAPE
     assert lm(0, 64, 100, None, None, None, None) == OK
     ls = L.moe_log_softmax
-    assert ls(4, 100, None, FAKE, None) == NULL
-    assert ls(4, 100, FAKE, MIS, None) == ALIGN
-    assert ls(4, 0, FAKE, FAKE, None) == SHAPE
-    assert ls(1 << 12, 1 << 20, FAKE, FAKE, None) == SHAPE       # T*V >= 2^31
-    assert ls(0, 100, None, None, None) == OK
+    wb = L.moe_workspace_bytes
+    need = wb(M.OP_LOG_SOFTMAX, 64, 65536, 1, 64, 1, 0)     # H carries V
+    assert 64 * 256 * 4 <= need < 64 * 4096 * 4               # chunk sums and segment maxima
+    assert ls(4, 100, None, FAKE, FAKE, 1 << 20, None) == NULL
+    assert ls(4, 100, FAKE, FAKE, None, 1 << 20, None) == NULL
+    assert ls(4, 100, FAKE, MIS, FAKE, 1 << 20, None) == ALIGN
+    assert ls(4, 100, FAKE, FAKE, MIS, 1 << 20, None) == ALIGN
+    assert ls(64, 65536, FAKE, FAKE, FAKE, need - 1, None) == WS
+    assert ls(4, 0, FAKE, FAKE, FAKE, 0, None) == SHAPE
+    assert ls(1 << 12, 1 << 20, FAKE, FAKE, FAKE, 0, None) == SHAPE       # T*V >= 2^31
+    assert ls(0, 100, None, None, None, 0, None) == OK
     k3 = L.moe_k3
-    assert k3(4, 100, FAKE, FAKE, FAKE, FAKE, None, None) == NULL
-    assert k3(4, 100, FAKE, FAKE, FAKE, MIS, FAKE, None) == ALIGN
-    assert k3(4, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None) == SHAPE
-    assert k3(0, 100, None, None, None, None, None, None) == OK
+    need = wb(M.OP_K3, 64, 65536, 1, 64, 1, 0)
+    assert need >= 64 * 256 * 8
+    assert k3(4, 100, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 20, None) == NULL
+    assert k3(4, 100, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1 << 20, None) == NULL
+    assert k3(4, 100, FAKE, FAKE, FAKE, MIS, FAKE, FAKE, 1 << 20, None) == ALIGN
+    assert k3(64, 65536, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None) == WS
+    assert k3(4, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == SHAPE
+    assert k3(0, 100, None, None, None, None, None, None, 0, None) == OK
+    assert wb(M.OP_K3, 4, 0, 1, 64, 1, 0) == 0
 
 
 def test_forward_replay_checks(L):
