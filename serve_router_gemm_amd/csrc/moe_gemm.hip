@@ -84,10 +84,11 @@ __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g));
 
 // ---------------------------------------------------------------------------
 // Pipelined kernel: 8 waves, tile = 256 weight rows x 256 token rows, K staged
-// 64 at a time through two LDS stages (64 KB each) filled by direct-to-LDS
-// loads.  Each wave computes 128 weight rows x 64 token rows.
+// 64 at a time through a ring of five 32 KB LDS units (the whole 160 KB) filled
+// by direct-to-LDS loads: the weight rows of a step fill one unit, its token
+// rows another.  Each wave computes 128 weight rows x 64 token rows.
 //
-// A stage holds 512 rows x 128 bytes as 64 blocks of 8 rows (1 KB).  A
+// A unit holds 256 rows x 128 bytes as 32 blocks of 8 rows (1 KB).  A
 // direct-to-LDS load (global_load_lds_dwordx4) writes lane l's 16 bytes at
 // M0 + 16*l, so one wave instruction fills one block: lane l lands at row
 // l/8, physical chunk l%8, and loads logical chunk (l%8) ^ (l/8) of that row.
@@ -98,14 +99,15 @@ __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g));
 //
 // The loads are issued from inline assembly so the compiler does not drain
 // them at barriers; each wave waits for its own loads before the barrier
-// that publishes a stage.  A wave stalls at a load instruction until the
-// CU's address unit accepts it (about 16 cycles per 1 KB instruction on
-// gfx950), so only one wave per SIMD issues loads: the other wave of the
-// SIMD starts its MFMAs at once and keeps the matrix core busy meanwhile
-// (measured: 5% faster than every wave issuing an eighth of the loads).  After each barrier the MFMAs of the previous
-// stage's last quarter run from registers while the new stage's fragment
-// reads are in flight.  The MFMA sequence of an output element is the same
-// as in the kernel above: 16x16x32 bf16 steps over k = 0, 32, 64, ...
+// that publishes a step's units.  A wave stalls at a load instruction until
+// the CU's address unit accepts it (about 16 cycles per 1 KB instruction on
+// gfx950), so only one wave per SIMD issues loads, and it issues them in two
+// halves per step: the other wave of the SIMD keeps the matrix core busy
+// meanwhile (measured: 5% faster than every wave issuing an eighth of the
+// loads; eight issuing waves with the same split measured no better).  After
+// each barrier the MFMAs of the previous step's last quarter run from
+// registers while the new step's fragment reads are in flight.  The MFMA
+// sequence of an output element: 16x16x32 bf16 steps over k = 0, 32, 64, ...
 // ascending, accumulators from 0.
 // ---------------------------------------------------------------------------
 constexpr int kP_Threads = 512;
@@ -113,23 +115,25 @@ constexpr int kP_Tok = kTileTok;
 constexpr int kP_W = 256;
 constexpr int kP_BK = 64;
 constexpr int kP_Rows = kP_W + kP_Tok;          // 512
-constexpr int kP_RowBytes = kP_BK * 2;          // 128
-constexpr int kP_StageBytes = kP_Rows * kP_RowBytes;   // 65536
-constexpr int kP_Blocks = kP_Rows / 8;          // 64 blocks of 8 rows
+constexpr int kP_Blocks = kP_Rows / 8;          // 64 blocks of 8 rows of kP_BK bf16 (128 B)
 constexpr int kP_WBlocks = kP_W / 8;            // 32
 #ifndef MOE_ISSUERS
 #define MOE_ISSUERS 4
 #endif
-constexpr int kP_Issuers = MOE_ISSUERS;         // waves that issue the stage loads
-constexpr int kP_Dma = kP_Blocks / kP_Issuers;  // loads per issuing thread per stage
+constexpr int kP_Issuers = MOE_ISSUERS;         // waves that issue the loads
+constexpr int kP_Dma = kP_Blocks / kP_Issuers;  // loads per issuing thread per K step
 constexpr int kP_WDma = kP_WBlocks / kP_Issuers;   // the first of them: weight blocks
 constexpr int kP_GateUpF = kP_W / 2;            // 128
 // A tile with at most 64 valid token rows needs 32 KB of weight rows and
-// 8 KB of token rows per step: three such stages fit where two full stages
-// do, and keep the loads of two steps in flight.
+// 8 KB of token rows per step: three such stages fit in the ring's space and
+// keep the loads of two steps in flight.
 constexpr int kP_DeepTok = 64;
 constexpr int kP_DeepStageBytes = kP_WBlocks * 1024 + (kP_DeepTok / 8) * 1024;   // 40960
-static_assert(3 * kP_DeepStageBytes <= 2 * kP_StageBytes, "three deep stages fit");
+constexpr int kP_Unit = kP_WBlocks * 1024;     // 32 KB: one operand of one K step
+constexpr int kP_Ring = 5;                      // units in the 160 KB ring
+static_assert(kP_Unit == (kP_Tok / 8) * 1024, "token rows of a step fill one unit");
+static_assert(kP_WDma == 8, "a weight unit is 8 loads per issuing thread");
+static_assert(3 * kP_DeepStageBytes <= kP_Ring * kP_Unit, "three deep stages fit");
 
 template <int MODE, bool DEEP>
 __device__ __forceinline__ void expert_gemm_body(const GemmParams& P, unsigned char* smem) {
@@ -224,61 +228,104 @@ __device__ __forceinline__ void expert_gemm_body(const GemmParams& P, unsigned c
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         block_barrier();
 
-        // Stage of K step kt.  In a launch that only streams weights (DEEP),
-        // a tile with at most 64 valid rows ("deep") cycles through three
-        // 40 KB stages with the loads of two steps in flight.  Every other
-        // tile alternates two 64 KB stages, one step ahead.  Either way a
-        // stage is refilled only after the barrier that follows every wave's
-        // reads of it, and the MFMA sequence of an output element is the
-        // same.
+        // LDS layout.  In a launch that only streams weights (DEEP), a tile
+        // with at most 64 valid token rows ("deep") cycles through three 40 KB
+        // stages (32 KB of weight rows, then its token blocks) with the loads
+        // of two steps in flight.  Every other tile keeps a ring of five 32 KB
+        // units: unit 2kt holds the weight rows of step kt, unit 2kt+1 its
+        // token rows.  After the barrier that opens step kt the units of step
+        // kt-1 are free: the token rows of step kt+1 are loaded into one at
+        // once, the weight rows of step kt+2 into the other after the first
+        // group of this step's MFMAs.  Weight rows, the operand with the least
+        // reuse between workgroups (an expert's weight tile serves only its
+        // own token tiles), so get about 1.5 steps to arrive, and an issuing
+        // wave stalls on half as many loads at a time.  (Measured on gfx950
+        // against two 64 KB stages loaded one step ahead: -4% on the large
+        // layer's gate/up, -11% with 256 experts of 512 tokens, +1% with a
+        // single expert; issuing both operands at the barrier was slower than
+        // two stages.)  Either way a unit is refilled only after the barrier
+        // that follows every wave's reads of it, and the MFMA sequence of an
+        // output element is the same.
         const bool deep = DEEP && valid <= kP_DeepTok;
-        auto stage_off = [&](int kt) {
-            return deep ? ((kt - kt0) % 3) * kP_DeepStageBytes : ((kt - kt0) & 1) * kP_StageBytes;
+        auto w_off = [&](int kt) -> uint32_t {
+            return deep ? (uint32_t)((kt % 3) * kP_DeepStageBytes)
+                        : (uint32_t)(((2 * kt) % kP_Ring) * kP_Unit);
         };
-        auto issue = [&](int kt) {
-            const uint32_t sbase = lds0 + (uint32_t)stage_off(kt);
+        auto x_off = [&](int kt) -> uint32_t {
+            return deep ? (uint32_t)((kt % 3) * kP_DeepStageBytes + kP_Unit)
+                        : (uint32_t)(((2 * kt + 1) % kP_Ring) * kP_Unit);
+        };
+        auto issue_w = [&](int kt) {
             if (wave >= kP_Issuers) return;
+            const uint32_t sb = lds0 + w_off(kt);
 #pragma unroll
-            for (int i = 0; i < kP_Dma; ++i) {
-                if (i >= kP_WDma && (i - kP_WDma) * kP_Issuers + iw >= ntb) continue;
-                dma16(src[i] + (size_t)kt * kP_BK, sbase + (uint32_t)((i * kP_Issuers + iw) * 1024));
+            for (int i = 0; i < kP_WDma; ++i)
+                dma16(src[i] + (size_t)kt * kP_BK, sb + (uint32_t)((i * kP_Issuers + iw) * 1024));
+        };
+        auto issue_x = [&](int kt) {
+            if (wave >= kP_Issuers) return;
+            const uint32_t sb = lds0 + x_off(kt);
+#pragma unroll
+            for (int i = kP_WDma; i < kP_Dma; ++i) {
+                const int bx = (i - kP_WDma) * kP_Issuers + iw;
+                if (bx >= ntb) continue;
+                dma16(src[i] + (size_t)kt * kP_BK, sb + (uint32_t)(bx * 1024));
             }
         };
-        const int ahead = deep ? 2 : 1;
         // loads per step of this thread in a deep tile: 8 weight blocks and
         // its token blocks below ntb (at most 8 in all)
         const int nload =
             wave < kP_Issuers ? kP_WDma + (ntb > iw ? 1 : 0) + (ntb > iw + 4 ? 1 : 0) : 0;
-        for (int j = 0; j < ahead; ++j)
-            if (kt0 + j < kt1) issue(kt0 + j);
+        if (deep) {
+            for (int j = 0; j < 2; ++j)
+                if (kt0 + j < kt1) { issue_w(kt0 + j); issue_x(kt0 + j); }
+        } else {
+            issue_w(kt0);
+            issue_x(kt0);
+            if (kt0 + 1 < kt1) issue_w(kt0 + 1);
+        }
 
         bf16x8 fbP[kNB], faP[4];
         for (int kt = kt0; kt < kt1; ++kt) {
-            // this step's loads landed; a deep tile leaves the next step's
-            // nload loads of this thread in flight (loads complete in order)
+            // this step's loads landed.  A deep tile leaves the next step's
+            // nload loads of this thread in flight, a ring tile the weight
+            // rows of the next step, issued after this step's token rows
+            // (loads complete in order).
             if (deep && kt + 1 < kt1 && nload == 8)
                 asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
             else if (deep && kt + 1 < kt1 && nload == 9)
                 asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
             else if (deep && kt + 1 < kt1 && nload == 10)
                 asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+            else if (!deep && kt + 1 < kt1)
+                asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
             else
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             block_barrier();
-            if (kt + ahead < kt1) issue(kt + ahead);
-            if (!active) continue;
-            const unsigned char* sb = smem + stage_off(kt);
+            if (deep) {
+                if (kt + 2 < kt1) { issue_w(kt + 2); issue_x(kt + 2); }
+            } else if (kt + 1 < kt1) {
+                issue_x(kt + 1);
+            }
+            // a ring tile's weight rows of step kt+2: issued after the first
+            // group of this step's MFMAs (by a wave without MFMAs at once)
+            const bool late_w = !deep && kt + 2 < kt1;
+            if (!active) {
+                if (late_w) issue_w(kt + 2);
+                continue;
+            }
+            const unsigned char* sw = smem + w_off(kt);
+            const unsigned char* sx = smem + x_off(kt);
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                const unsigned char* sk = sb + frag_off[kk];
                 bf16x8 fb[kNB], fa[4];
 #pragma unroll
                 for (int nb = 0; nb < kNB; ++nb)
-                    fb[nb] = *reinterpret_cast<const bf16x8*>(
-                        sk + (kP_WBlocks + wt * 8 + nb * 2) * 1024);
+                    fb[nb] = *reinterpret_cast<const bf16x8*>(sx + frag_off[kk] +
+                                                              (wt * 8 + nb * 2) * 1024);
 #pragma unroll
                 for (int mb = 0; mb < 4; ++mb)
-                    fa[mb] = *reinterpret_cast<const bf16x8*>(sk + wgrp(mb) * 1024);
+                    fa[mb] = *reinterpret_cast<const bf16x8*>(sw + frag_off[kk] + wgrp(mb) * 1024);
                 // second half of the previous 32-wide step (from registers)
                 if (kk == 1 || kt > kt0) {
 #pragma unroll
@@ -296,9 +343,11 @@ __device__ __forceinline__ void expert_gemm_body(const GemmParams& P, unsigned c
                             fa[mb], fb[nb], acc[mb][nb], 0, 0, 0);
 #pragma unroll
                 for (int mb = 0; mb < 4; ++mb)
-                    faP[mb] = *reinterpret_cast<const bf16x8*>(sk + wgrp(mb + 4) * 1024);
+                    faP[mb] = *reinterpret_cast<const bf16x8*>(sw + frag_off[kk] +
+                                                               wgrp(mb + 4) * 1024);
 #pragma unroll
                 for (int nb = 0; nb < kNB; ++nb) fbP[nb] = fb[nb];
+                if (kk == 0 && late_w) issue_w(kt + 2);
             }
         }
         if (kt1 > kt0 && active) {
@@ -357,7 +406,7 @@ __device__ __forceinline__ void expert_gemm_body(const GemmParams& P, unsigned c
 // long tiles, measured slower; so did deciding per tile inside one loop.)
 template <int MODE>
 __global__ __launch_bounds__(kP_Threads) void expert_gemm_pipe_kernel(GemmParams P) {
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kP_StageBytes];
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[kP_Ring * kP_Unit];
     if (MODE == MODE_GATE_UP && P.tile_start[P.E] == 0)
         expert_gemm_body<MODE, MODE == MODE_GATE_UP>(P, smem);
     else
