@@ -384,18 +384,19 @@ hipError_t launch_lm_stream(int T, int H, int V, const uint16_t* h, const uint16
     return hipGetLastError();
 }
 
-constexpr int kSelMaxQ = 8;   // experts per lane: E <= 512
-constexpr int kSelBatch = 4;  // partial planes loaded together in the fold
-
 // One wave per token: fold partial logits, keys, top-k, weights.  With
 // `replay` set (router replay), the experts of each slot are read from it
 // instead of selected, and only the weights are computed, by the same code:
 // replaying the ids this kernel chose reproduces its weights bit for bit.  A
 // replayed id outside [0,E) gets weight 0 and is left out of the sum.
+// kSelMaxQ = experts per lane (E <= 64 * kSelMaxQ); kSelBatch partial planes
+// are loaded together in the fold (32 values per lane in flight).
+template <int kSelMaxQ>
 __global__ __launch_bounds__(256) void router_select_kernel(
     int T, int E, int k, int nparts, int score, int renorm, const float* __restrict__ part,
     const float* __restrict__ bias, const int32_t* __restrict__ replay,
     int32_t* __restrict__ ids, float* __restrict__ wout) {
+    constexpr int kSelBatch = 32 / kSelMaxQ;
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;  // whole wave leaves together
@@ -592,8 +593,19 @@ hipError_t launch_route(int T, int H, int E, int k, int score, int renorm, const
         err = launch_logits<kBigTT, 8, false>(T, H, E, x, wr, part_ws, s);
     }
     if (err != hipSuccess) return err;
-    router_select_kernel<<<(T + 3) / 4, 256, 0, s>>>(T, E, k, p.nparts, score, renorm, part_ws,
-                                                     bias, replay, ids, w);
+    const int blocks = (T + 3) / 4;
+    if (E <= 64)
+        router_select_kernel<1><<<blocks, 256, 0, s>>>(T, E, k, p.nparts, score, renorm, part_ws,
+                                                       bias, replay, ids, w);
+    else if (E <= 128)
+        router_select_kernel<2><<<blocks, 256, 0, s>>>(T, E, k, p.nparts, score, renorm, part_ws,
+                                                       bias, replay, ids, w);
+    else if (E <= 256)
+        router_select_kernel<4><<<blocks, 256, 0, s>>>(T, E, k, p.nparts, score, renorm, part_ws,
+                                                       bias, replay, ids, w);
+    else
+        router_select_kernel<8><<<blocks, 256, 0, s>>>(T, E, k, p.nparts, score, renorm, part_ws,
+                                                       bias, replay, ids, w);
     return hipGetLastError();
 }
 
