@@ -422,7 +422,12 @@ __global__ __launch_bounds__(kP_Threads) void expert_gemm_pipe_kernel(GemmParams
 // 32 gate + 32 up rows of the same features), so the same launch spreads over
 // every CU.  4 waves; wave w multiplies 16 weight rows (gate/up: waves 0-1
 // gate, 2-3 up) by the expert's token rows, with fragments loaded straight
-// into registers from a ring of up to 8 K steps.  The list of experts it
+// into registers from a ring of up to 8 K steps.  A gate/up launch with fewer
+// such items than two per CU (one token on the mid layer: 8 experts x 44
+// items) takes items of 16 features instead, one gate and one up wave each:
+// a CU streams about 25 GB/s whatever it runs, so the time is set by the CUs
+// given the most bytes (mid, one token: 0.029 -> 0.025 ms; with more items the
+// 4-wave blocks measured faster).  The list of experts it
 // serves (0 < count <= max_count) is built in LDS from the offsets at kernel
 // start, so no separate schedule launch is needed.
 //
@@ -437,10 +442,11 @@ __global__ __launch_bounds__(kP_Threads) void expert_gemm_pipe_kernel(GemmParams
 // summation order of an element then depends on its expert's token count:
 // this mode is deliberately not batch-invariant.
 // ---------------------------------------------------------------------------
-constexpr int kS_Threads = 256;
 constexpr int kS_MaxE = 512;
-constexpr int kS_GateUpF = 32;         // features per gate/up work item
-constexpr int kS_DownH = 64;           // output rows per down work item
+constexpr int kS_DownH = 64;           // output rows per down work item (4 waves)
+// features per gate/up work item of a block of TH threads: half its waves
+// hold gate rows, the other half up rows of the same features
+constexpr int stream_gate_up_f(int TH) { return TH / kWave / 2 * 16; }
 constexpr int kS_MaxTok = 32;          // invariant path: tokens per call for this kernel
 constexpr int kV_MaxTok = 32;          // variant: experts up to this count are split
 
@@ -458,13 +464,16 @@ __device__ __forceinline__ int variant_parts(int m, int parts_max) {
     return min(parts_max, m <= 4 ? 4 : 2);
 }
 
-template <int MODE, int NB, int U, bool SPLIT>
+template <int MODE, int NB, int U, bool SPLIT, int kS_Threads>
 __global__ __launch_bounds__(kS_Threads) void expert_gemm_stream_kernel(GemmParams P) {
+    constexpr int kHalf = kS_Threads / kWave / 2;   // gate/up: gate waves, then as many up waves
+    constexpr int kS_GateUpF = stream_gate_up_f(kS_Threads);
+    static_assert(MODE == MODE_GATE_UP || kS_Threads == 4 * kWave, "down: 4 waves of 16 rows");
     __shared__ int act_list[kS_MaxE];
     __shared__ int item_start[kS_MaxE + 1];    // SPLIT: first work item of a list entry
     __shared__ int row_start[kS_MaxE + 1];     // SPLIT: first workspace row of an entry
     __shared__ int wsum[3][kS_Threads / kWave];
-    __shared__ floatx4 xch[2][NB][kWave];      // up waves' accumulators, for the gate waves
+    __shared__ floatx4 xch[kHalf][NB][kWave];  // up waves' accumulators, for the gate waves
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -549,8 +558,8 @@ __global__ __launch_bounds__(kS_Threads) void expert_gemm_stream_kernel(GemmPara
         // this wave's weight row
         const uint16_t* pa;
         if (MODE == MODE_GATE_UP) {
-            const int f = min(nt * kS_GateUpF + (wave & 1) * 16 + (lane & 15), P.N - 1);
-            pa = ((wave < 2) ? P.w0 : P.w1) + ((size_t)e * P.N + f) * P.K + koff;
+            const int f = min(nt * kS_GateUpF + (wave % kHalf) * 16 + (lane & 15), P.N - 1);
+            pa = ((wave < kHalf) ? P.w0 : P.w1) + ((size_t)e * P.N + f) * P.K + koff;
         } else {
             const int h = min(nt * kS_DownH + wave * 16 + (lane & 15), P.N - 1);
             pa = P.w0 + ((size_t)e * P.N + h) * P.K + koff;
@@ -603,7 +612,8 @@ __global__ __launch_bounds__(kS_Threads) void expert_gemm_stream_kernel(GemmPara
             if (SPLIT) {
                 const int NW = (MODE == MODE_GATE_UP) ? 2 * P.N : P.N;
                 const int col = (MODE == MODE_GATE_UP)
-                                    ? (wave >= 2 ? P.N : 0) + nt * kS_GateUpF + (wave & 1) * 16 + colq
+                                    ? (wave >= kHalf ? P.N : 0) + nt * kS_GateUpF +
+                                          (wave % kHalf) * 16 + colq
                                     : nt * kS_DownH + wave * 16 + colq;
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
@@ -618,12 +628,12 @@ __global__ __launch_bounds__(kS_Threads) void expert_gemm_stream_kernel(GemmPara
                     }
                 }
             } else if (MODE == MODE_GATE_UP) {
-                if (wave >= 2) {
+                if (wave >= kHalf) {
 #pragma unroll
-                    for (int nb = 0; nb < NB; ++nb) xch[wave - 2][nb][lane] = acc[nb];
+                    for (int nb = 0; nb < NB; ++nb) xch[wave - kHalf][nb][lane] = acc[nb];
                 }
                 __syncthreads();
-                if (wave < 2) {
+                if (wave < kHalf) {
                     const int f = nt * kS_GateUpF + wave * 16 + colq;
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb) {
@@ -690,20 +700,17 @@ __global__ __launch_bounds__(256) void variant_reduce_kernel(GemmParams P) {
     }
 }
 
-template <int MODE, bool SPLIT, int NB>
+template <int MODE, bool SPLIT, int NB, int TH>
 hipError_t launch_stream_nb(const GemmParams& P, int U, int grid, hipStream_t s) {
-    if (U == 8) expert_gemm_stream_kernel<MODE, NB, 8, SPLIT><<<grid, kS_Threads, 0, s>>>(P);
-    else if (U == 4) expert_gemm_stream_kernel<MODE, NB, 4, SPLIT><<<grid, kS_Threads, 0, s>>>(P);
-    else expert_gemm_stream_kernel<MODE, NB, 2, SPLIT><<<grid, kS_Threads, 0, s>>>(P);
+    if (U == 8) expert_gemm_stream_kernel<MODE, NB, 8, SPLIT, TH><<<grid, TH, 0, s>>>(P);
+    else if (U == 4) expert_gemm_stream_kernel<MODE, NB, 4, SPLIT, TH><<<grid, TH, 0, s>>>(P);
+    else expert_gemm_stream_kernel<MODE, NB, 2, SPLIT, TH><<<grid, TH, 0, s>>>(P);
     return hipGetLastError();
 }
 
-// max_rows: the most token rows an expert served by this launch can have
-// (16 or fewer: one 16-row chunk per pass; else 32-row chunks).
-template <int MODE, bool SPLIT>
-hipError_t launch_stream(const GemmParams& P0, int T, int max_rows, hipStream_t s) {
-    GemmParams P = P0;
-    P.n_tiles = (MODE == MODE_GATE_UP) ? P.N / kS_GateUpF : P.N / kS_DownH;
+template <int MODE, bool SPLIT, int TH>
+hipError_t launch_stream_th(GemmParams P, int T, int max_rows, hipStream_t s) {
+    P.n_tiles = (MODE == MODE_GATE_UP) ? P.N / stream_gate_up_f(TH) : P.N / kS_DownH;
     // ring depth: the largest of 8, 4, 2 dividing the K steps of the
     // shortest part (K is a multiple of 64, so K / 32 is even; the host's
     // parts_max keeps K / 32 / parts_max even).  (A ring of 16 measured no
@@ -713,8 +720,21 @@ hipError_t launch_stream(const GemmParams& P0, int T, int max_rows, hipStream_t 
     // at most min(E, T*k) experts are active: no more work items than that
     const long items = (long)std::min(P.E, T * P.top_k) * P.n_tiles * (SPLIT ? P.parts_max : 1);
     const int grid = (int)std::max(1L, std::min(items, (long)device_cu_count() * 8));
-    if (max_rows <= 16) return launch_stream_nb<MODE, SPLIT, 1>(P, U, grid, s);
-    return launch_stream_nb<MODE, SPLIT, 2>(P, U, grid, s);
+    if (max_rows <= 16) return launch_stream_nb<MODE, SPLIT, 1, TH>(P, U, grid, s);
+    return launch_stream_nb<MODE, SPLIT, 2, TH>(P, U, grid, s);
+}
+
+// max_rows: the most token rows an expert served by this launch can have
+// (16 or fewer: one 16-row chunk per pass; else 32-row chunks).
+template <int MODE, bool SPLIT>
+hipError_t launch_stream(const GemmParams& P, int T, int max_rows, hipStream_t s) {
+    if constexpr (MODE == MODE_GATE_UP && !SPLIT) {
+        // fewer 32-feature items than two per CU: 16-feature items
+        const long items32 = (long)std::min(P.E, T * P.top_k) * (P.N / stream_gate_up_f(256));
+        if (items32 < 2L * device_cu_count())
+            return launch_stream_th<MODE, SPLIT, 128>(P, T, max_rows, s);
+    }
+    return launch_stream_th<MODE, SPLIT, 256>(P, T, max_rows, s);
 }
 
 // The token-tile list.  A tile whose valid rows fill at most half of it

@@ -230,10 +230,11 @@ def test_weight_streaming_launch_matches_full_launch():
 @pytest.mark.parametrize("name,big", [("mid", 4000), ("dec", 600)])
 def test_small_batch_streaming_launch_matches_tiled_launch(name, big):
     """Batches of at most 32 tokens run the weight-streaming GEMMs (64 weight
-    rows per work item, fragments straight from memory into registers); larger
-    ones the 256 x 256 tiled kernels.  The MFMA sequence of an element is the
-    same, so the rows of T = 1, 5, 16, 17 and 32 tokens alone equal the same
-    rows inside a large batch bit for bit."""
+    rows per work item, fragments straight from memory into registers; a
+    gate/up launch with few items, as one token on the mid layer, 32 rows:
+    16 gate and 16 up); larger ones the 256 x 256 tiled kernels.  The MFMA
+    sequence of an element is the same, so the rows of T = 1, 5, 16, 17 and 32
+    tokens alone equal the same rows inside a large batch bit for bit."""
     cfg = _cfg(name, T=big)
     L = layer(cfg)
     x = I.make_tokens(big, cfg.H, 5151, "cpu").to(DEV)
