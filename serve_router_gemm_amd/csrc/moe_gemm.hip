@@ -793,7 +793,7 @@ __global__ __launch_bounds__(512) void tile_schedule_kernel(int E, int skip_upto
 
 template <int MODE>
 hipError_t launch_gemm(const GemmParams& P, hipStream_t s) {
-    // one persistent workgroup per CU (the two 64 KB stages hold its LDS),
+    // one persistent workgroup per CU (its 160 KB LDS ring fills the CU),
     // rounded up to whole XCD rows
     const int cu = device_cu_count();
     const int b = (cu + kXcds - 1) / kXcds * kXcds;
