@@ -40,6 +40,19 @@ GEMM_SOURCES = ("moe_gemm.hip", "moe_gemm_tiles.h", "moe_device.h", "moe_interna
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 PEAK_FP32_VALU_TFLOPS = 78.6  # 256 CU x 64 lanes x 2 flop x 2.4 GHz, fp32 fma without packed math
+PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X dense fp32 matrix peak
+
+
+def route_uses_matrix_cores(T, H, E):
+    """The router-logits kernel the library's route plan picks (route_plan in
+    csrc/moe_route.hip): the K=1 fp32 MFMA kernel (32 x 64 per wave, blocks of
+    2 x 2 waves for E > 64, else 4 x 1) when its folded tiles give 512 blocks,
+    or, for 512 tokens or more, its one-block-per-chunk tiles do."""
+    we = 2 if E > 64 else 1
+    wt = 4 // we
+    nchunks = (H + 255) // 256
+    mb = ((T + 32 * wt - 1) // (32 * wt)) * ((E + 64 * we - 1) // (64 * we))
+    return mb >= 512 or (T >= 512 and mb * nchunks >= 512)
 PEAK_HBM_GBS = 8000.0
 
 
@@ -477,7 +490,8 @@ def main():
             del lp8
         decode_res = {"vocab": V, "lm_head_ms": round(dms[0], 4),
                       "lm_head_hbm_frac": round(proj_bytes / (dms[0] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                      "lm_head_valu_tflops": round(2.0 * T * V * H / (dms[0] * 1e-3) / 1e12, 2),
+                      "lm_head_kernel": "mfma_f32 32x32x1" if T > 8 else "valu fma, one row per thread",
+                      "lm_head_fp32_tflops": round(2.0 * T * V * H / (dms[0] * 1e-3) / 1e12, 2),
                       "log_softmax_ms": round(dms[1], 4),
                       "log_softmax_hbm_frac": round(8.0 * T * V / (dms[1] * 1e-3) / 1e9
                                                     / PEAK_HBM_GBS, 4),
@@ -531,16 +545,23 @@ def main():
             nd += int(np.unpackbits(np.bitwise_xor(a, b).view(np.uint8)).sum())
         inv_bits = nd
 
-    # router logits: fp32 fma chains in the pinned order (VALU; packed fp32
-    # is not used), and the bytes of x and w_router
+    # router logits: fp32 fma chains in the pinned order, on the matrix cores
+    # (K=1 fp32 MFMA, the same chains bit for bit) where the library's route
+    # plan takes them, else on the VALU (packed fp32 is not used); and the
+    # bytes of x and w_router
     r_flops = 2.0 * T * H * E
     r_bytes = 2.0 * T * H + 2.0 * E * H
     r_s = stage_ms["route"] * 1e-3
-    route_res = {"valu_tflops": round(r_flops / r_s / 1e12, 2),
+    mfma_route = route_uses_matrix_cores(T, H, E)
+    r_peak = PEAK_FP32_MFMA_TFLOPS if mfma_route else PEAK_FP32_VALU_TFLOPS
+    route_res = {"kernel": "mfma_f32 32x32x1" if mfma_route else "valu fma",
+                 "fp32_tflops": round(r_flops / r_s / 1e12, 2),
+                 "frac": round(r_flops / r_s / 1e12 / r_peak, 4),
+                 "peak_tflops": r_peak,
                  "valu_frac": round(r_flops / r_s / 1e12 / PEAK_FP32_VALU_TFLOPS, 4),
                  "hbm_frac": round(r_bytes / r_s / 1e9 / PEAK_HBM_GBS, 4),
-                 "binds": "valu" if r_flops / (PEAK_FP32_VALU_TFLOPS * 1e12) >
-                          r_bytes / (PEAK_HBM_GBS * 1e9) else "hbm"}
+                 "binds": ("mfma_f32" if mfma_route else "valu")
+                          if r_flops / (r_peak * 1e12) > r_bytes / (PEAK_HBM_GBS * 1e9) else "hbm"}
 
     res = {
         "metric": METRIC,

@@ -17,7 +17,9 @@ constexpr int kLogitChunk = 256;
 struct RoutePlan {
     int split;     // 0: logits kernel folds every chunk; 1: one block per chunk
     int nparts;    // partial-logit planes the select kernel folds
-    int tt, te;    // token / expert register tile of the logits kernel
+    int tt, te;    // token / expert register tile of the VALU logits kernel
+    int mfma;      // 1: the matrix-core logits kernel, its 4 waves wt x we
+    int wt, we;
 };
 RoutePlan route_plan(int T, int H, int E);
 size_t route_ws_bytes(int T, int H, int E);

@@ -8,14 +8,16 @@
 //
 // Logits are taken in one fixed order, independent of the batch: hidden
 // indices in chunks of 256, each chunk an ascending fp32 fma chain from +0,
-// chunk sums added in ascending order.  The logits kernel either folds all
-// chunks of its tile itself (large batches) or writes each chunk's sum to
-// its own plane for the select kernel to fold (small batches, where the
-// chunks give the parallelism).  Both produce the same bits.
+// chunk sums added in ascending order.  The logits kernels either fold all
+// chunks of their tile themselves or write each chunk's sum to its own plane
+// for the select kernel to fold (where the chunks give the parallelism).
+// Both produce the same bits.
 //
-// This is fp32 VALU work on purpose: the order inside an MFMA is the
-// hardware's, so only a VALU chain has an order the rest of the stack (and a
-// plain CPU program) can reproduce exactly.
+// A matrix instruction that sums several products (K > 1) adds them in an
+// order of the hardware's that no plain CPU program reproduces, so the chains
+// run either on the VALU or on the matrix cores through the K = 1 fp32 MFMA,
+// which adds exactly one product per accumulator and instruction, rounded as
+// the VALU's fma rounds: the same chain either way.
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -25,6 +27,8 @@ namespace {
 
 constexpr int kRouteThreads = 256;
 constexpr int kStageK = 32;   // hidden indices staged in LDS per step
+
+typedef float floatx32 __attribute__((ext_vector_type(32)));
 
 // part[c][t][e] = fp32 logit (SPLIT=false: all chunks folded, c = 0) or the
 // chunk-c partial sum (SPLIT=true: blockIdx.z = c).  With PF the next step's
@@ -206,6 +210,153 @@ __global__ __launch_bounds__(kRouteThreads) void router_logits_kernel(
             const int e = e0 + tx * TE + j;
             if (e < E) plane[(size_t)t * E + e] = SPLIT ? acc[i][j] : total[i][j];
         }
+    }
+}
+
+// Router logits on the matrix cores, in the same order.  v_mfma_f32_32x32x1_2b_f32
+// adds one product to each of its accumulators per instruction, and on gfx950
+// that add rounds exactly as the VALU's fused multiply-add does (checked on
+// normals, wide exponents, denormal products and sums, signed zeros,
+// infinities and NaN: chains of either are bit-identical).  A chain of these
+// instructions over k ascending is thus the chain of the kernel above, bit
+// for bit, at the matrix cores' fp32 rate (twice the non-packed VALU rate).
+// Block: 4 waves, WT x WE of them along tokens x experts; a wave computes 32
+// tokens x 64 experts, one instruction per k (two 32 x 32 blocks, its two
+// expert halves): lane L supplies token L % 32 and expert L of the wave's 64.
+// The k-major fp32 stages of x and w sit in two LDS buffers (48 KB at 2 x 2
+// waves, so two or three blocks share a CU and one's staging runs under
+// another's MFMAs), the next step's bf16 pieces in registers, and each group
+// of 4 k's operands is read from LDS one group ahead of its MFMAs.  (A wave
+// tile of 64 x 64 as two chains, one block per CU, measured 10% slower.)
+template <int WT, int WE, bool SPLIT>
+__global__ __launch_bounds__(kRouteThreads) void router_logits_mfma_kernel(
+    int T, int H, int E, const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+    float* __restrict__ part) {
+    static_assert(WT * WE * kWave == kRouteThreads, "4 waves");
+    constexpr int BT = 32 * WT;
+    constexpr int BE = 64 * WE;
+    __shared__ __attribute__((aligned(16))) float xs[2][kStageK][BT];
+    __shared__ __attribute__((aligned(16))) float ws[2][kStageK][BE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wt = wave / WE, we = wave % WE;
+    const int t0 = blockIdx.x * BT;
+    const int e0 = blockIdx.y * BE;
+
+    int k_begin = 0, k_end = H;
+    if (SPLIT) {
+        k_begin = blockIdx.z * kLogitChunk;
+        k_end = min(H, k_begin + kLogitChunk);
+    }
+
+    // piece c of a step: row c / 4, hidden indices k0 + 8 * (c % 4) .. + 7
+    constexpr int NX = (BT * 4 + kRouteThreads - 1) / kRouteThreads;
+    constexpr int NW = (BE * 4 + kRouteThreads - 1) / kRouteThreads;
+    uint4 xr[NX], wg[NW];
+    auto fetch = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < NX; ++i) {
+            const int c = tid + i * kRouteThreads;
+            const int t = t0 + (c >> 2);
+            xr[i] = make_uint4(0, 0, 0, 0);
+            if (c < BT * 4 && t < T)
+                xr[i] = *reinterpret_cast<const uint4*>(x + (size_t)t * H + k0 + (c & 3) * 8);
+        }
+#pragma unroll
+        for (int i = 0; i < NW; ++i) {
+            const int c = tid + i * kRouteThreads;
+            const int e = e0 + (c >> 2);
+            wg[i] = make_uint4(0, 0, 0, 0);
+            if (c < BE * 4 && e < E)
+                wg[i] = *reinterpret_cast<const uint4*>(wr + (size_t)e * H + k0 + (c & 3) * 8);
+        }
+    };
+    auto stage = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < NX; ++i) {
+            const int c = tid + i * kRouteThreads;
+            if (c >= BT * 4) continue;
+            const int row = c >> 2, q = c & 3;
+            const uint32_t w4[4] = {xr[i].x, xr[i].y, xr[i].z, xr[i].w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                xs[buf][q * 8 + 2 * u][row] = bf16_to_f32(w4[u] & 0xFFFFu);
+                xs[buf][q * 8 + 2 * u + 1][row] = bf16_to_f32(w4[u] >> 16);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NW; ++i) {
+            const int c = tid + i * kRouteThreads;
+            if (c >= BE * 4) continue;
+            const int row = c >> 2, q = c & 3;
+            const uint32_t w4[4] = {wg[i].x, wg[i].y, wg[i].z, wg[i].w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                ws[buf][q * 8 + 2 * u][row] = bf16_to_f32(w4[u] & 0xFFFFu);
+                ws[buf][q * 8 + 2 * u + 1][row] = bf16_to_f32(w4[u] >> 16);
+            }
+        }
+    };
+
+    floatx32 acc, total;
+#pragma unroll
+    for (int r = 0; r < 32; ++r) { acc[r] = 0.0f; total[r] = 0.0f; }
+
+    const int nsteps = (k_end - k_begin) / kStageK;
+    if (nsteps > 0) fetch(k_begin);
+    for (int st = 0; st < nsteps; ++st) {
+        const int k0 = k_begin + st * kStageK;
+        const int buf = st & 1;
+        // buffer buf was last read in step st-2, before every wave passed the
+        // barrier of step st-1: one barrier per step
+        stage(buf);
+        __syncthreads();
+        if (st + 1 < nsteps) fetch(k0 + kStageK);
+        const float* xa = &xs[buf][0][wt * 32 + (lane & 31)];
+        const float* wb = &ws[buf][0][we * 64 + lane];
+        constexpr int G = 4;
+        float oa[2][G], ob[2][G];
+        auto rd = [&](int slot, int k) {
+#pragma unroll
+            for (int u = 0; u < G; ++u) {
+                oa[slot][u] = xa[(k + u) * BT];
+                ob[slot][u] = wb[(k + u) * BE];
+            }
+        };
+        rd(0, 0);
+#pragma unroll
+        for (int gk = 0; gk < kStageK / G; ++gk) {
+            if (gk + 1 < kStageK / G) rd((gk + 1) & 1, (gk + 1) * G);
+            // keep the next group's reads ahead of this group's MFMAs (the
+            // scheduler would otherwise sink each read to its MFMA)
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < G; ++u)
+                acc = __builtin_amdgcn_mfma_f32_32x32x1f32(oa[gk & 1][u], ob[gk & 1][u], acc, 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // end of a 256-wide chunk (or of H): fold the chunk sum in order
+        const int kn = k0 + kStageK;
+        if (!SPLIT && ((kn % kLogitChunk) == 0 || kn == k_end)) {
+#pragma unroll
+            for (int r = 0; r < 32; ++r) {
+                total[r] = total[r] + acc[r];
+                acc[r] = 0.0f;
+            }
+        }
+    }
+
+    // accumulator r: 32 x 32 block r / 16 (the expert half), token
+    // 8 * ((r % 16) / 4) + 4 * (L / 32) + r % 4 of the wave's 32, expert L % 32
+    float* plane = part + (SPLIT ? (size_t)blockIdx.z * T * E : 0);
+#pragma unroll
+    for (int r = 0; r < 32; ++r) {
+        const int rr = r & 15;
+        const int t = t0 + wt * 32 + 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
+        const int e = e0 + we * 64 + 32 * (r >> 4) + (lane & 31);
+        if (t < T && e < E) plane[(size_t)t * E + e] = SPLIT ? acc[r] : total[r];
     }
 }
 
@@ -522,6 +673,23 @@ hipError_t launch_logits(int T, int H, int E, const uint16_t* x, const uint16_t*
     return hipGetLastError();
 }
 
+template <int WT, int WE, bool SPLIT>
+hipError_t launch_logits_mfma(int T, int H, int E, const uint16_t* x, const uint16_t* wr,
+                              float* part, hipStream_t s) {
+    constexpr int BT = 32 * WT, BE = 64 * WE;
+    const int nchunks = (H + kLogitChunk - 1) / kLogitChunk;
+    dim3 grid((T + BT - 1) / BT, (E + BE - 1) / BE, SPLIT ? nchunks : 1);
+    router_logits_mfma_kernel<WT, WE, SPLIT><<<grid, kRouteThreads, 0, s>>>(T, H, E, x, wr, part);
+    return hipGetLastError();
+}
+
+template <bool SPLIT>
+hipError_t launch_logits_mfma_plan(const RoutePlan& p, int T, int H, int E, const uint16_t* x,
+                                   const uint16_t* wr, float* part, hipStream_t s) {
+    if (p.we == 2) return launch_logits_mfma<2, 2, SPLIT>(T, H, E, x, wr, part, s);
+    return launch_logits_mfma<4, 1, SPLIT>(T, H, E, x, wr, part, s);
+}
+
 }  // namespace
 
 // 8 tokens x 8 contiguous experts per thread for E > 128: 64 fmas per four
@@ -531,7 +699,25 @@ constexpr int kBigTT = 8;
 
 RoutePlan route_plan(int T, int H, int E) {
     RoutePlan p;
+    p.mfma = 0;
+    p.wt = 1;
+    p.we = 4;
     const int nchunks = (H + kLogitChunk - 1) / kLogitChunk;
+    // matrix cores where they fill the chip: 32 x 64 per wave, the block's 4
+    // waves 2 x 2 (E > 64: 64 tokens x 128 experts) or 4 x 1 (128 x 64) along
+    // tokens x experts; every chunk folded in the kernel when that alone gives
+    // two blocks per CU (the large layer: one plane instead of one per chunk),
+    // else one block per chunk for batches of 512 tokens or more
+    {
+        const int we = E > 64 ? 2 : 1, wt = 4 / we;
+        const long mb = (long)((T + 32 * wt - 1) / (32 * wt)) * ((E + 64 * we - 1) / (64 * we));
+        if (mb >= 512 || (T >= 512 && mb * nchunks >= 512)) {
+            p.mfma = 1; p.wt = wt; p.we = we; p.tt = 8; p.te = 8;
+            p.split = mb >= 512 ? 0 : 1;
+            p.nparts = p.split ? nchunks : 1;
+            return p;
+        }
+    }
     // folded tiles: 64 tokens x up to 256 experts per block
     const int te = E <= 32 ? 1 : (E <= 64 ? 2 : (E <= 128 ? 4 : 8));
     const long blocks = (long)((T + 63) / 64) * ((E + 32 * te - 1) / (32 * te));
@@ -554,16 +740,16 @@ size_t route_ws_bytes(int T, int H, int E) {
 
 // Vocabulary projection of a decode step (z = h . proj^T) in the router's
 // pinned order: up to 8 tokens by the streaming kernel (one vocabulary row per
-// thread), more by the folded router kernel with its register tile.  Each z
-// depends only on its own row pair and is the same chain in both, so the
-// choice never changes its bits.
+// thread), more by the matrix-core router kernel (64 tokens x 128 vocabulary
+// rows per block, every chunk folded).  Each z depends only on its own row
+// pair and is the same chain in both, so the choice never changes its bits.
 hipError_t launch_lm_logits(int T, int H, int V, const uint16_t* h, const uint16_t* proj,
                             float* z, hipStream_t s) {
     if (T <= 1) return launch_lm_stream<1>(T, H, V, h, proj, z, s);
     if (T <= 2) return launch_lm_stream<2>(T, H, V, h, proj, z, s);
     if (T <= 4) return launch_lm_stream<4>(T, H, V, h, proj, z, s);
     if (T <= 8) return launch_lm_stream<8>(T, H, V, h, proj, z, s);
-    return launch_logits<8, 4, false, true>(T, H, V, h, proj, z, s);
+    return launch_logits_mfma<2, 2, false>(T, H, V, h, proj, z, s);
 }
 
 hipError_t launch_route(int T, int H, int E, int k, int score, int renorm, const uint16_t* x,
@@ -571,7 +757,10 @@ hipError_t launch_route(int T, int H, int E, int k, int score, int renorm, const
                         float* part_ws, hipStream_t s, const int32_t* replay) {
     const RoutePlan p = route_plan(T, H, E);
     hipError_t err;
-    if (p.split && T <= 8) {
+    if (p.mfma) {
+        err = p.split ? launch_logits_mfma_plan<true>(p, T, H, E, x, wr, part_ws, s)
+                      : launch_logits_mfma_plan<false>(p, T, H, E, x, wr, part_ws, s);
+    } else if (p.split && T <= 8) {
         if (T <= 1) err = launch_logits_few<1>(T, H, E, x, wr, part_ws, s);
         else if (T <= 2) err = launch_logits_few<2>(T, H, E, x, wr, part_ws, s);
         else if (T <= 4) err = launch_logits_few<4>(T, H, E, x, wr, part_ws, s);
