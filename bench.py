@@ -47,12 +47,12 @@ def route_uses_matrix_cores(T, H, E):
     """The router-logits kernel the library's route plan picks (route_plan in
     csrc/moe_route.hip): the K=1 fp32 MFMA kernel (32 x 64 per wave, blocks of
     2 x 2 waves for E > 64, else 4 x 1) when its folded tiles give 512 blocks,
-    or, for 512 tokens or more, its one-block-per-chunk tiles do."""
+    or, for 512 tokens or more, its one-block-per-chunk tiles give 256."""
     we = 2 if E > 64 else 1
     wt = 4 // we
     nchunks = (H + 255) // 256
     mb = ((T + 32 * wt - 1) // (32 * wt)) * ((E + 64 * we - 1) // (64 * we))
-    return mb >= 512 or (T >= 512 and mb * nchunks >= 512)
+    return mb >= 512 or (T >= 512 and mb * nchunks >= 256)
 PEAK_HBM_GBS = 8000.0
 
 
