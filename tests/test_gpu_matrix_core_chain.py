@@ -97,3 +97,15 @@ def test_matrix_core_logits_bit_exact_at_layer_shapes():
         z = M.lm_head_logits(x.to(DEV), w.to(DEV)).cpu().numpy()
         zr = O.lm_head_logits(bits(x), bits(w))
         assert np.array_equal(z.view(np.uint32), zr.view(np.uint32)), name
+
+
+def test_matrix_core_logits_ragged_shapes():
+    """Partial token and expert blocks and a last chunk narrower than 256
+    (H = 2112 ends in a 64-wide chunk), against the oracle bit for bit."""
+    g = torch.Generator().manual_seed(21)
+    for T, H, V in ((37, 2112, 200), (70, 320, 129), (9, 64, 1)):
+        h = torch.randn((T, H), generator=g).to(torch.bfloat16)
+        p = (torch.randn((V, H), generator=g) * 0.05).to(torch.bfloat16)
+        z = M.lm_head_logits(h.to(DEV), p.to(DEV)).cpu().numpy()
+        zr = O.lm_head_logits(bits(h), bits(p))
+        assert np.array_equal(z.view(np.uint32), zr.view(np.uint32)), (T, H, V)
