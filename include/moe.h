@@ -148,7 +148,12 @@ int moe_version(void);
  *   bias [device] [E] fp32 or NULL (sigmoid only: NULL means all zero; a
  *   non-NULL bias with softmax is rejected with MOE_ERR_UNSUPPORTED);
  *   topk_ids [device] out [T,k] int32; topk_w [device] out [T,k] fp32.
- * score: moe_score_fn.  renormalize: 0 or 1.  ws holds partial logits. */
+ * score: moe_score_fn.  renormalize: 0 or 1.  ws [device] holds the logits,
+ * or one plane of partial logits per 256-wide chunk where the library splits
+ * the hidden dimension over blocks (moe_workspace_bytes(MOE_OP_ROUTE, ...)
+ * gives the size the library will use; its content on entry is ignored).
+ * Whether the chains run on the VALU or on the matrix cores (the K = 1 fp32
+ * MFMA) is the library's choice from T, H and E; both give the same bits. */
 int moe_route(int T, int H, int E, int top_k, int score, int renormalize,
               const uint16_t* x, const uint16_t* w_router, const float* bias,
               int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes, void* stream);
