@@ -94,7 +94,7 @@ __global__ __launch_bounds__(kSegThreads) void ls_max_kernel(int V, int nseg,
     if (threadIdx.x == 0) segmax[(size_t)blockIdx.x * nseg + blockIdx.y] = m;
 }
 
-constexpr int kMaxSeg = (kMaxVocab + kSegLen - 1) / kSegLen;      // 128
+constexpr int kMaxSeg = (kMaxVocab + kSegLen - 1) / kSegLen;      // 512
 constexpr int kMaxChunks = (kMaxVocab + kSumChunk - 1) / kSumChunk;  // 4096
 
 // The row's maximum from its segment maxima, loaded by the block's threads

@@ -535,6 +535,37 @@ hipError_t launch_lm_stream(int T, int H, int V, const uint16_t* h, const uint16
     return hipGetLastError();
 }
 
+// Wave-uniform maximum of a 64-bit value: DPP exchanges inside each 16-lane
+// row (quad neighbours, then the mirrored half row, then the mirrored row), so
+// that every lane holds its row's maximum, then the four rows' maxima read
+// into scalars.  No LDS crossbar traffic (the 64-bit xor-shuffle butterfly it
+// replaces took 12 crossbar shuffles per maximum); the maximum of distinct
+// keys is the same in any order.
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_max_u64(uint64_t v) {
+    const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+    const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, CTRL, 0xF, 0xF, false);
+    const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, CTRL, 0xF, 0xF, false);
+    const uint64_t o = ((uint64_t)ohi << 32) | olo;
+    return o > v ? o : v;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+    v = dpp_max_u64<0xB1>(v);    // quad_perm [1, 0, 3, 2]
+    v = dpp_max_u64<0x4E>(v);    // quad_perm [2, 3, 0, 1]
+    v = dpp_max_u64<0x141>(v);   // row_half_mirror
+    v = dpp_max_u64<0x140>(v);   // row_mirror
+    uint64_t m = 0;
+#pragma unroll
+    for (int r = 0; r < kWave / 16; ++r) {
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 16 * r);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 16 * r);
+        const uint64_t x = ((uint64_t)hi << 32) | lo;
+        m = x > m ? x : m;
+    }
+    return m;
+}
+
 // One wave per token: fold partial logits, keys, top-k, weights.  With
 // `replay` set (router replay), the experts of each slot are read from it
 // instead of selected, and only the weights are computed, by the same code:
@@ -612,11 +643,7 @@ __global__ __launch_bounds__(256) void router_select_kernel(
         uint64_t best = rk[0];
 #pragma unroll
         for (int q = 1; q < kSelMaxQ; ++q) best = rk[q] > best ? rk[q] : best;
-#pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) {
-            const uint64_t o = shfl_xor_u64(best, m);
-            best = o > best ? o : best;
-        }
+        best = wave_max_u64(best);
         const int e = (int)(~(uint32_t)best);
         const int qs = e >> 6, owner = e & 63;
         float mine = 0.0f;
