@@ -44,6 +44,12 @@ ROUTE_CASES = [
     ("kE_E8", _cfg("tiny", T=50, k=8), None),
     ("E1_k1", _cfg("tiny", T=33, E=1, k=1), None),
     ("sigmoid_norenorm", _cfg("large", T=200, H=512, E=64, renorm=False), None),
+    # the matrix-core logits kernel, one block per chunk: a ragged token block
+    # (600 = 4 x 128 + 88) and a last chunk 64 wide (H = 52 x 256 + 64)
+    ("mfma_split_ragged", _cfg("mid", T=600, H=13376, F=128), 256),
+    # the matrix-core kernel folding every chunk: ragged token and expert
+    # blocks (16400 = 256 x 64 + 16 tokens, 200 = 128 + 72 experts)
+    ("mfma_fold_ragged", _cfg("large", T=16400, H=256, E=200, F=128), 512),
 ]
 
 
