@@ -341,6 +341,46 @@ def main():
                       "out_bit_identical_to_routed": same}
         del ws_f, rep
 
+    # The same step as one captured HIP graph (moe_forward on the launch
+    # stream, workspace and output preallocated), replayed: the launches'
+    # gaps are what it removes, so it matters at decode sizes.  Every replay
+    # must give the step's output bit for bit.
+    graph_res = None
+    if args.variant == 0 and not args.step_only:
+        ws_g = M.workspace(M.OP_FORWARD, T, H, E, F, k)
+        out_g = torch.empty_like(out)
+        fwd = lambda: M.forward(x, L["w_router"], L["w_gate"], L["w_up"], L["w_down"], k,
+                                cfg.score, cfg.renorm, bias=bias, out=out_g, ws=ws_g)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fwd()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            fwd()
+        out_g.fill_(0.0)
+        graph.replay()
+        torch.cuda.synchronize()
+        same_g = bool(torch.equal(out_g.view(torch.int16), out.view(torch.int16)))
+        KG = K
+        gs = torch.cuda.current_stream()
+        eg = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        for _ in range(max(1, args.warmup)):
+            graph.replay()
+        torch.cuda.synchronize()
+        eg[0].record(gs)
+        for _ in range(KG):
+            graph.replay()
+        eg[1].record(gs)
+        torch.cuda.synchronize()
+        g_ms = eg[0].elapsed_time(eg[1]) / KG
+        graph_res = {"ms_per_step": round(g_ms, 4), "tokens_per_s": round(T / (g_ms * 1e-3), 1),
+                     "staged_over_graph_ms": round(ms_step / g_ms, 4),
+                     "out_bit_identical": same_g}
+        del graph, ws_g, out_g
+
     # Sparse-indexer top-k at the pages' shape (top 2048 per query over a
     # 128K-token context; 1024 queries), timed on its own.
     topk_res = None
@@ -601,6 +641,7 @@ def main():
         "probe_bits_differing": inv_bits,
         "variant": variant_res,
         "router_replay": replay_res,
+        "graph_replay": graph_res,
         "indexer_topk": topk_res,
         "fp8_experts": fp8_res,
     }
