@@ -27,6 +27,11 @@ namespace {
 
 constexpr int kRouteThreads = 256;
 constexpr int kStageK = 32;   // hidden indices staged in LDS per step
+// One float of padding per k-row of the matrix-core kernel's LDS stages: the
+// staging writes of a wave (16 rows x 4 k-groups) then spread over the banks
+// instead of four lanes sharing one (large layer: route 0.571 -> 0.550 ms;
+// padding by 2 gave 0.556, by 4 0.589)
+constexpr int kMfmaPad = 1;
 
 typedef float floatx32 __attribute__((ext_vector_type(32)));
 
@@ -223,7 +228,7 @@ __global__ __launch_bounds__(kRouteThreads) void router_logits_kernel(
 // Block: 4 waves, WT x WE of them along tokens x experts; a wave computes 32
 // tokens x 64 experts, one instruction per k (two 32 x 32 blocks, its two
 // expert halves): lane L supplies token L % 32 and expert L of the wave's 64.
-// The k-major fp32 stages of x and w sit in two LDS buffers (48 KB at 2 x 2
+// The k-major fp32 stages of x and w sit in two LDS buffers (50 KB at 2 x 2
 // waves, so two or three blocks share a CU and one's staging runs under
 // another's MFMAs), the next step's bf16 pieces in registers, and each group
 // of 4 k's operands is read from LDS one group ahead of its MFMAs.  (A wave
@@ -235,8 +240,9 @@ __global__ __launch_bounds__(kRouteThreads) void router_logits_mfma_kernel(
     static_assert(WT * WE * kWave == kRouteThreads, "4 waves");
     constexpr int BT = 32 * WT;
     constexpr int BE = 64 * WE;
-    __shared__ __attribute__((aligned(16))) float xs[2][kStageK][BT];
-    __shared__ __attribute__((aligned(16))) float ws[2][kStageK][BE];
+    constexpr int SX = BT + kMfmaPad, SW = BE + kMfmaPad;   // LDS row strides
+    __shared__ __attribute__((aligned(16))) float xs[2][kStageK][SX];
+    __shared__ __attribute__((aligned(16))) float ws[2][kStageK][SW];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -321,8 +327,8 @@ __global__ __launch_bounds__(kRouteThreads) void router_logits_mfma_kernel(
         auto rd = [&](int slot, int k) {
 #pragma unroll
             for (int u = 0; u < G; ++u) {
-                oa[slot][u] = xa[(k + u) * BT];
-                ob[slot][u] = wb[(k + u) * BE];
+                oa[slot][u] = xa[(k + u) * SX];
+                ob[slot][u] = wb[(k + u) * SW];
             }
         };
         rd(0, 0);
