@@ -118,13 +118,15 @@ __global__ __launch_bounds__(kSegThreads) void ls_chunk_kernel(int V, int nseg, 
     int v0, v1;
     seg_range(V, v0, v1);
     const float* zr = z + (size_t)blockIdx.x * V;
-    const float m = row_max(nseg, segmax, sm_l);
+    // the segment's values are loaded before the row maximum, so the two
+    // memory round trips overlap
     float t[kSegU];
 #pragma unroll
     for (int u = 0; u < kSegU; ++u) {
         const int v = v0 + u * kSegThreads + threadIdx.x;
         t[u] = v < v1 ? zr[v] : 0.0f;
     }
+    const float m = row_max(nseg, segmax, sm_l);
 #pragma unroll
     for (int u = 0; u < kSegU; ++u) {
         const int i = u * kSegThreads + threadIdx.x;
@@ -163,6 +165,15 @@ __global__ __launch_bounds__(kSegThreads) void ls_write_kernel(int V, int nseg, 
     __shared__ float cs_l[kMaxChunks];
     int v0, v1;
     seg_range(V, v0, v1);
+    const float* zr = z + (size_t)blockIdx.x * V;
+    float* lr = logp + (size_t)blockIdx.x * V;
+    // the segment's values first: their loads overlap the fold below
+    float t[kSegU];
+#pragma unroll
+    for (int u = 0; u < kSegU; ++u) {
+        const int v = v0 + u * kSegThreads + threadIdx.x;
+        t[u] = v < v1 ? zr[v] : 0.0f;
+    }
     // the row's chunk sums, loaded together, then added in ascending order
     const float* cs = csum + (size_t)blockIdx.x * nch;
     for (int i = threadIdx.x; i < nch; i += kSegThreads) cs_l[i] = cs[i];
@@ -174,14 +185,6 @@ __global__ __launch_bounds__(kSegThreads) void ls_write_kernel(int V, int nseg, 
     }
     __syncthreads();
     const float lse = s_lse;
-    const float* zr = z + (size_t)blockIdx.x * V;
-    float* lr = logp + (size_t)blockIdx.x * V;
-    float t[kSegU];
-#pragma unroll
-    for (int u = 0; u < kSegU; ++u) {
-        const int v = v0 + u * kSegThreads + threadIdx.x;
-        t[u] = v < v1 ? zr[v] : 0.0f;
-    }
 #pragma unroll
     for (int u = 0; u < kSegU; ++u) {
         const int v = v0 + u * kSegThreads + threadIdx.x;
@@ -197,9 +200,11 @@ __global__ __launch_bounds__(kSegThreads) void k3_chunk_kernel(int V, int nseg, 
                                                                const float* __restrict__ test,
                                                                double* __restrict__ csum,
                                                                float* __restrict__ gval,
-                                                               int32_t* __restrict__ gidx) {
+                                                               int32_t* __restrict__ gidx,
+                                                               double* __restrict__ gterm) {
     __shared__ double seg[kSegChunks * kPad];
     __shared__ float best_v[kSegThreads / 64];
+    __shared__ float best_r[kSegThreads / 64];
     __shared__ int best_i[kSegThreads / 64];
     int v0, v1;
     seg_range(V, v0, v1);
@@ -212,7 +217,9 @@ __global__ __launch_bounds__(kSegThreads) void k3_chunk_kernel(int V, int nseg, 
         tq[u] = v < v1 ? qr[v] : 0.0f;
         tr[u] = v < v1 ? rr[v] : 0.0f;
     }
-    float bv = -INFINITY;
+    // the candidate carries its logp_ref value, so the segment can give the
+    // candidate's own term and the fold needs no further loads
+    float bv = -INFINITY, br = 0.0f;
     int bi = V;
 #pragma unroll
     for (int u = 0; u < kSegU; ++u) {
@@ -220,18 +227,20 @@ __global__ __launch_bounds__(kSegThreads) void k3_chunk_kernel(int V, int nseg, 
         const int v = v0 + i;
         if (v < v1) {
             seg[(i / kSumChunk) * kPad + (i % kSumChunk)] = exp((double)tq[u]) * k3_term(tr[u], tq[u]);
-            if (!isnan(tq[u]) && (bi == V || tq[u] > bv)) { bv = tq[u]; bi = v; }
+            if (!isnan(tq[u]) && (bi == V || tq[u] > bv)) { bv = tq[u]; br = tr[u]; bi = v; }
         }
     }
     // (value descending, index ascending, no element last) is a total order,
     // so a tree reduction finds the same first largest element
     for (int o = 32; o >= 1; o >>= 1) {
         const float ov = __shfl_xor(bv, o, 64);
+        const float orr = __shfl_xor(br, o, 64);
         const int oi = __shfl_xor(bi, o, 64);
-        if (oi < V && (bi == V || ov > bv || (ov == bv && oi < bi))) { bv = ov; bi = oi; }
+        if (oi < V && (bi == V || ov > bv || (ov == bv && oi < bi))) { bv = ov; br = orr; bi = oi; }
     }
     if ((threadIdx.x & 63) == 0) {
         best_v[threadIdx.x >> 6] = bv;
+        best_r[threadIdx.x >> 6] = br;
         best_i[threadIdx.x >> 6] = bi;
     }
     __syncthreads();
@@ -253,60 +262,72 @@ __global__ __launch_bounds__(kSegThreads) void k3_chunk_kernel(int V, int nseg, 
         csum[(size_t)blockIdx.x * nch + c0 + c] = s;
     }
     if (threadIdx.x == 0) {
-        float gv = -INFINITY;
+        float gv = -INFINITY, gr = 0.0f;
         int gi = V;
         for (int j = 0; j < kSegThreads / 64; ++j) {
             const int i = best_i[j];
             if (i >= V) continue;
             const float w = best_v[j];
-            if (gi == V || w > gv || (w == gv && i < gi)) { gv = w; gi = i; }
+            if (gi == V || w > gv || (w == gv && i < gi)) { gv = w; gr = best_r[j]; gi = i; }
         }
-        gval[(size_t)blockIdx.x * nseg + blockIdx.y] = gv;
-        gidx[(size_t)blockIdx.x * nseg + blockIdx.y] = gi;
+        const size_t o = (size_t)blockIdx.x * nseg + blockIdx.y;
+        gval[o] = gv;
+        gidx[o] = gi;
+        gterm[o] = gi < V ? k3_term(gr, gv) : 0.0;
     }
 }
 
 // k3, 2: one block per row: the chunk sums (loaded together into LDS) added
 // in ascending order, the greedy token over the segments' candidates (0 if
 // logp_test[0] is NaN, the rule of a running "strictly greater" scan from
-// index 0), and its term
+// index 0), and its term (the winning segment's, or index 0's)
 __global__ __launch_bounds__(kSegThreads) void k3_fold_kernel(int V, int nseg, int nch,
                                                               const float* __restrict__ ref,
                                                               const float* __restrict__ test,
                                                               const double* __restrict__ csum,
                                                               const float* __restrict__ gval,
                                                               const int32_t* __restrict__ gidx,
+                                                              const double* __restrict__ gterm,
                                                               double* __restrict__ mean,
                                                               double* __restrict__ greedy_k3,
                                                               int32_t* __restrict__ greedy) {
     __shared__ double cs_l[kMaxChunks];
+    __shared__ double gt_l[kMaxSeg];
     __shared__ float gv_l[kMaxSeg];
     __shared__ int gi_l[kMaxSeg];
     const int t = blockIdx.x;
+    // index 0's values, loaded with the rest (one memory round trip)
+    const float q0 = test[(size_t)t * V];
+    const float r0 = ref[(size_t)t * V];
     const double* cs = csum + (size_t)t * nch;
     for (int i = threadIdx.x; i < nch; i += kSegThreads) cs_l[i] = cs[i];
     for (int i = threadIdx.x; i < nseg; i += kSegThreads) {
         gv_l[i] = gval[(size_t)t * nseg + i];
         gi_l[i] = gidx[(size_t)t * nseg + i];
+        gt_l[i] = gterm[(size_t)t * nseg + i];
     }
     __syncthreads();
     if (threadIdx.x != 0) return;
     double S = 0.0;
     for (int c = 0; c < nch; ++c) S = S + cs_l[c];
     float gv = -INFINITY;
-    int gi = V;
+    int gi = V, gj = -1;
     for (int j = 0; j < nseg; ++j) {
         const int i = gi_l[j];
         if (i >= V) continue;
         const float w = gv_l[j];
-        if (gi == V || w > gv || (w == gv && i < gi)) { gv = w; gi = i; }
+        if (gi == V || w > gv || (w == gv && i < gi)) { gv = w; gi = i; gj = j; }
     }
-    const float* qr = test + (size_t)t * V;
-    const float* rr = ref + (size_t)t * V;
-    if (gi == V || isnan(qr[0])) gi = 0;
+    double term;
+    if (gi == V || isnan(q0)) {
+        gi = 0;
+        term = k3_term(r0, q0);
+    } else {
+        term = gt_l[gj];
+    }
     mean[t] = S;
     greedy[t] = gi;
-    greedy_k3[t] = k3_term(rr[gi], qr[gi]);
+    greedy_k3[t] = term;
 }
 
 size_t up256(size_t v) { return (v + 255) / 256 * 256; }
@@ -322,7 +343,8 @@ size_t log_softmax_ws_bytes(int T, int V) {
 
 size_t k3_ws_bytes(int T, int V) {
     const int nseg = measure_segments(V), nch = (V + kSumChunk - 1) / kSumChunk;
-    return up256((size_t)T * nch * 8) + up256((size_t)T * nseg * 4) + up256((size_t)T * nseg * 4);
+    return up256((size_t)T * nch * 8) + up256((size_t)T * nseg * 4) + up256((size_t)T * nseg * 4) +
+           up256((size_t)T * nseg * 8);
 }
 
 hipError_t launch_log_softmax(int T, int V, const float* z, float* logp, void* ws,
@@ -351,12 +373,14 @@ hipError_t launch_k3(int T, int V, const float* logp_ref, const float* logp_test
     float* gval = reinterpret_cast<float*>(w);
     w += up256((size_t)T * nseg * 4);
     int32_t* gidx = reinterpret_cast<int32_t*>(w);
+    w += up256((size_t)T * nseg * 4);
+    double* gterm = reinterpret_cast<double*>(w);
     k3_chunk_kernel<<<dim3(T, nseg), kSegThreads, 0, s>>>(V, nseg, nch, logp_ref, logp_test,
-                                                           csum, gval, gidx);
+                                                           csum, gval, gidx, gterm);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     k3_fold_kernel<<<T, kSegThreads, 0, s>>>(V, nseg, nch, logp_ref, logp_test, csum, gval, gidx,
-                                              mean, greedy_k3, greedy);
+                                              gterm, mean, greedy_k3, greedy);
     return hipGetLastError();
 }
 
