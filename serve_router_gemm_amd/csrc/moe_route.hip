@@ -578,22 +578,28 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 // replaying the ids this kernel chose reproduces its weights bit for bit.  A
 // replayed id outside [0,E) gets weight 0 and is left out of the sum.
 // kSelMaxQ = experts per lane (E <= 64 * kSelMaxQ); kSelBatch partial planes
-// are loaded together in the fold (32 values per lane in flight).
-template <int kSelMaxQ>
+// are loaded together in the fold (one memory latency per batch: a decode
+// step's 24 planes of a 6144-wide hidden state come in one batch).  The
+// bias is loaded before the fold, and each selected logit is read from its
+// owner lane into a scalar register (no LDS crossbar round trip per slot).
+template <int kSelMaxQ, int kSelBatch>
 __global__ __launch_bounds__(256) void router_select_kernel(
     int T, int E, int k, int nparts, int score, int renorm, const float* __restrict__ part,
     const float* __restrict__ bias, const int32_t* __restrict__ replay,
     int32_t* __restrict__ ids, float* __restrict__ wout) {
-    constexpr int kSelBatch = 32 / kSelMaxQ;
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;  // whole wave leaves together
 
+    float bz[kSelMaxQ];
+#pragma unroll
+    for (int q = 0; q < kSelMaxQ; ++q) {
+        const int e = lane + 64 * q;
+        bz[q] = (score != 0 && bias && e < E) ? bias[e] : 0.0f;
+    }
     float lg[kSelMaxQ];
     uint64_t rk[kSelMaxQ];
-    // fold the partial planes in ascending order, kSelBatch planes of loads
-    // in flight at a time (one dependent load per plane would cost a memory
-    // latency each)
+    // fold the partial planes in ascending order
 #pragma unroll
     for (int q = 0; q < kSelMaxQ; ++q) lg[q] = 0.0f;
     for (int c0 = 0; c0 < nparts; c0 += kSelBatch) {
@@ -623,11 +629,21 @@ __global__ __launch_bounds__(256) void router_select_kernel(
                 key = v;
             } else {
                 const float sg = 1.0f / (1.0f + expf(-v));
-                key = sg + (bias ? bias[e] : 0.0f);
+                key = sg + bz[q];
             }
             rk[q] = sel_rank(key, e);
         }
     }
+
+    // the logit of expert e (uniform), read from its owner lane
+    auto logit_of = [&](int e) -> float {
+        const int qs = e >> 6, owner = e & 63;
+        float v = 0.0f;
+#pragma unroll
+        for (int q = 0; q < kSelMaxQ; ++q)
+            if (q == qs) v = lg[q];
+        return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), owner));
+    };
 
     int sel[16];
     float lsel[16];
@@ -635,15 +651,7 @@ __global__ __launch_bounds__(256) void router_select_kernel(
         if (replay) {
             const int e = replay[(size_t)t * k + j];
             sel[j] = e;
-            float mine = 0.0f;
-            if (e >= 0 && e < E) {
-                const int qs = e >> 6, owner = e & 63;
-#pragma unroll
-                for (int q = 0; q < kSelMaxQ; ++q)
-                    if (q == qs) mine = lg[q];
-                mine = __shfl(mine, owner, 64);
-            }
-            lsel[j] = mine;
+            lsel[j] = (e >= 0 && e < E) ? logit_of(e) : 0.0f;
             continue;
         }
         uint64_t best = rk[0];
@@ -652,15 +660,11 @@ __global__ __launch_bounds__(256) void router_select_kernel(
         best = wave_max_u64(best);
         const int e = (int)(~(uint32_t)best);
         const int qs = e >> 6, owner = e & 63;
-        float mine = 0.0f;
 #pragma unroll
         for (int q = 0; q < kSelMaxQ; ++q)
-            if (q == qs) {
-                mine = lg[q];
-                if (lane == owner) rk[q] = 0;  // taken
-            }
+            if (q == qs && lane == owner) rk[q] = 0;  // taken
         sel[j] = e;
-        lsel[j] = __shfl(mine, owner, 64);
+        lsel[j] = logit_of(e);
     }
 
     float p[16];
@@ -786,6 +790,43 @@ hipError_t launch_lm_logits(int T, int H, int V, const uint16_t* h, const uint16
     return launch_logits_mfma<2, 2, false>(T, H, V, h, proj, z, s);
 }
 
+// Select for E <= 64 * Q experts per token.  The partial planes are folded
+// from batches of loads: the smallest batch of 8, 16 or 32 planes that holds
+// them all (at most 128 values per lane), since unused slots of a batch still
+// take registers and so waves per SIMD (8 planes in the tie layer's 8192
+// tokens with a 32-plane batch: 0.117 -> 0.123 ms).
+template <int Q, int B>
+hipError_t launch_select_qb(int T, int E, int k, int nparts, int score, int renorm,
+                            const float* part, const float* bias, const int32_t* replay,
+                            int32_t* ids, float* w, hipStream_t s) {
+    router_select_kernel<Q, B><<<(T + 3) / 4, 256, 0, s>>>(T, E, k, nparts, score, renorm, part,
+                                                          bias, replay, ids, w);
+    return hipGetLastError();
+}
+
+template <int Q>
+hipError_t launch_select_q(int T, int E, int k, int nparts, int score, int renorm,
+                           const float* part, const float* bias, const int32_t* replay,
+                           int32_t* ids, float* w, hipStream_t s) {
+    constexpr int kMaxBatch = 128 / Q;
+    if (nparts <= 1)
+        return launch_select_qb<Q, 1>(T, E, k, nparts, score, renorm, part, bias, replay, ids, w, s);
+    if (nparts <= 8 || kMaxBatch < 16)
+        return launch_select_qb<Q, 8>(T, E, k, nparts, score, renorm, part, bias, replay, ids, w, s);
+    if (nparts <= 16 || kMaxBatch < 32)
+        return launch_select_qb<Q, 16>(T, E, k, nparts, score, renorm, part, bias, replay, ids, w, s);
+    return launch_select_qb<Q, 32>(T, E, k, nparts, score, renorm, part, bias, replay, ids, w, s);
+}
+
+hipError_t launch_select(int T, int E, int k, int nparts, int score, int renorm,
+                         const float* part, const float* bias, const int32_t* replay,
+                         int32_t* ids, float* w, hipStream_t s) {
+    if (E <= 64) return launch_select_q<1>(T, E, k, nparts, score, renorm, part, bias, replay, ids, w, s);
+    if (E <= 128) return launch_select_q<2>(T, E, k, nparts, score, renorm, part, bias, replay, ids, w, s);
+    if (E <= 256) return launch_select_q<4>(T, E, k, nparts, score, renorm, part, bias, replay, ids, w, s);
+    return launch_select_q<8>(T, E, k, nparts, score, renorm, part, bias, replay, ids, w, s);
+}
+
 hipError_t launch_route(int T, int H, int E, int k, int score, int renorm, const uint16_t* x,
                         const uint16_t* wr, const float* bias, int32_t* ids, float* w,
                         float* part_ws, hipStream_t s, const int32_t* replay) {
@@ -816,20 +857,7 @@ hipError_t launch_route(int T, int H, int E, int k, int score, int renorm, const
         err = launch_logits<kBigTT, 8, false>(T, H, E, x, wr, part_ws, s);
     }
     if (err != hipSuccess) return err;
-    const int blocks = (T + 3) / 4;
-    if (E <= 64)
-        router_select_kernel<1><<<blocks, 256, 0, s>>>(T, E, k, p.nparts, score, renorm, part_ws,
-                                                       bias, replay, ids, w);
-    else if (E <= 128)
-        router_select_kernel<2><<<blocks, 256, 0, s>>>(T, E, k, p.nparts, score, renorm, part_ws,
-                                                       bias, replay, ids, w);
-    else if (E <= 256)
-        router_select_kernel<4><<<blocks, 256, 0, s>>>(T, E, k, p.nparts, score, renorm, part_ws,
-                                                       bias, replay, ids, w);
-    else
-        router_select_kernel<8><<<blocks, 256, 0, s>>>(T, E, k, p.nparts, score, renorm, part_ws,
-                                                       bias, replay, ids, w);
-    return hipGetLastError();
+    return launch_select(T, E, k, p.nparts, score, renorm, part_ws, bias, replay, ids, w, s);
 }
 
 }  // namespace moe
