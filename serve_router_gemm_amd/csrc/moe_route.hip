@@ -27,11 +27,12 @@ namespace {
 
 constexpr int kRouteThreads = 256;
 constexpr int kStageK = 32;   // hidden indices staged in LDS per step
-// One float of padding per k-row of the matrix-core kernel's LDS stages: the
-// staging writes of a wave (16 rows x 4 k-groups) then spread over the banks
-// instead of four lanes sharing one (large layer: route 0.571 -> 0.550 ms;
-// padding by 2 gave 0.556, by 4 0.589)
-constexpr int kMfmaPad = 1;
+// Padding of each staged row of the matrix-core router kernel, in bf16
+// elements (a multiple of 8, so the 16-byte stage writes stay aligned).
+#ifndef MOE_ROUTE_ROW_PAD
+#define MOE_ROUTE_ROW_PAD 16
+#endif
+constexpr int kMfmaRowPad = MOE_ROUTE_ROW_PAD;
 
 typedef float floatx32 __attribute__((ext_vector_type(32)));
 
@@ -228,11 +229,15 @@ __global__ __launch_bounds__(kRouteThreads) void router_logits_kernel(
 // Block: 4 waves, WT x WE of them along tokens x experts; a wave computes 32
 // tokens x 64 experts, one instruction per k (two 32 x 32 blocks, its two
 // expert halves): lane L supplies token L % 32 and expert L of the wave's 64.
-// The k-major fp32 stages of x and w sit in two LDS buffers (50 KB at 2 x 2
-// waves, so two or three blocks share a CU and one's staging runs under
-// another's MFMAs), the next step's bf16 pieces in registers, and each group
-// of 4 k's operands is read from LDS one group ahead of its MFMAs.  (A wave
-// tile of 64 x 64 as two chains, one block per CU, measured 10% slower.)
+// The stages of x and w sit in two LDS buffers as loaded (bf16 rows, one
+// 16-byte write per piece; 37 KB at 2 x 2 waves, so several blocks share a CU
+// and one's staging runs under another's MFMAs), the next step's pieces in
+// registers, and each group of 4 k's operands is read from LDS one group
+// ahead of its MFMAs, as one 8-byte read per operand widened to fp32 in
+// registers.  (Staged as k-major fp32 instead, with 8 conversions and 8
+// 4-byte writes per piece and 4-byte operand reads: large layer 0.540 ->
+// 0.521 ms for the route, same bits.  A wave tile of 64 x 64 as two chains,
+// one block per CU, measured 10% slower.)
 template <int WT, int WE, bool SPLIT>
 __global__ __launch_bounds__(kRouteThreads) void router_logits_mfma_kernel(
     int T, int H, int E, const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
@@ -240,9 +245,13 @@ __global__ __launch_bounds__(kRouteThreads) void router_logits_mfma_kernel(
     static_assert(WT * WE * kWave == kRouteThreads, "4 waves");
     constexpr int BT = 32 * WT;
     constexpr int BE = 64 * WE;
-    constexpr int SX = BT + kMfmaPad, SW = BE + kMfmaPad;   // LDS row strides
-    __shared__ __attribute__((aligned(16))) float xs[2][kStageK][SX];
-    __shared__ __attribute__((aligned(16))) float ws[2][kStageK][SW];
+    // the stage's bf16 pieces as loaded: row-major, k contiguous, each row
+    // padded (RS elements apart) so the rows a wave reads at one k offset
+    // spread over the banks
+    constexpr int RS = kStageK + kMfmaRowPad;
+    static_assert((RS * 2) % 16 == 0, "16-byte stage writes stay aligned");
+    __shared__ __attribute__((aligned(16))) uint16_t xs[2][BT * RS];
+    __shared__ __attribute__((aligned(16))) uint16_t ws[2][BE * RS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -284,25 +293,13 @@ __global__ __launch_bounds__(kRouteThreads) void router_logits_mfma_kernel(
         for (int i = 0; i < NX; ++i) {
             const int c = tid + i * kRouteThreads;
             if (c >= BT * 4) continue;
-            const int row = c >> 2, q = c & 3;
-            const uint32_t w4[4] = {xr[i].x, xr[i].y, xr[i].z, xr[i].w};
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                xs[buf][q * 8 + 2 * u][row] = bf16_to_f32(w4[u] & 0xFFFFu);
-                xs[buf][q * 8 + 2 * u + 1][row] = bf16_to_f32(w4[u] >> 16);
-            }
+            *reinterpret_cast<uint4*>(&xs[buf][(c >> 2) * RS + (c & 3) * 8]) = xr[i];
         }
 #pragma unroll
         for (int i = 0; i < NW; ++i) {
             const int c = tid + i * kRouteThreads;
             if (c >= BE * 4) continue;
-            const int row = c >> 2, q = c & 3;
-            const uint32_t w4[4] = {wg[i].x, wg[i].y, wg[i].z, wg[i].w};
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                ws[buf][q * 8 + 2 * u][row] = bf16_to_f32(w4[u] & 0xFFFFu);
-                ws[buf][q * 8 + 2 * u + 1][row] = bf16_to_f32(w4[u] >> 16);
-            }
+            *reinterpret_cast<uint4*>(&ws[buf][(c >> 2) * RS + (c & 3) * 8]) = wg[i];
         }
     };
 
@@ -320,16 +317,24 @@ __global__ __launch_bounds__(kRouteThreads) void router_logits_mfma_kernel(
         stage(buf);
         __syncthreads();
         if (st + 1 < nsteps) fetch(k0 + kStageK);
-        const float* xa = &xs[buf][0][wt * 32 + (lane & 31)];
-        const float* wb = &ws[buf][0][we * 64 + lane];
+        // this lane's token row and expert row of the stage
+        const uint16_t* xa = &xs[buf][(wt * 32 + (lane & 31)) * RS];
+        const uint16_t* wb = &ws[buf][(we * 64 + lane) * RS];
         constexpr int G = 4;
         float oa[2][G], ob[2][G];
+        // G = 4 consecutive k of each operand in one 8-byte read, widened
+        // from bf16 to fp32 (exact) by placing the 16 bits high
         auto rd = [&](int slot, int k) {
-#pragma unroll
-            for (int u = 0; u < G; ++u) {
-                oa[slot][u] = xa[(k + u) * SX];
-                ob[slot][u] = wb[(k + u) * SW];
-            }
+            const uint2 a = *reinterpret_cast<const uint2*>(xa + k);
+            const uint2 w = *reinterpret_cast<const uint2*>(wb + k);
+            oa[slot][0] = __uint_as_float(a.x << 16);
+            oa[slot][1] = __uint_as_float(a.x & 0xFFFF0000u);
+            oa[slot][2] = __uint_as_float(a.y << 16);
+            oa[slot][3] = __uint_as_float(a.y & 0xFFFF0000u);
+            ob[slot][0] = __uint_as_float(w.x << 16);
+            ob[slot][1] = __uint_as_float(w.x & 0xFFFF0000u);
+            ob[slot][2] = __uint_as_float(w.y << 16);
+            ob[slot][3] = __uint_as_float(w.y & 0xFFFF0000u);
         };
         rd(0, 0);
 #pragma unroll
