@@ -27,12 +27,6 @@ namespace {
 
 constexpr int kRouteThreads = 256;
 constexpr int kStageK = 32;   // hidden indices staged in LDS per step
-// Padding of each staged row of the matrix-core router kernel, in bf16
-// elements (a multiple of 8, so the 16-byte stage writes stay aligned).
-#ifndef MOE_ROUTE_ROW_PAD
-#define MOE_ROUTE_ROW_PAD 16
-#endif
-constexpr int kMfmaRowPad = MOE_ROUTE_ROW_PAD;
 
 typedef float floatx32 __attribute__((ext_vector_type(32)));
 
@@ -229,15 +223,16 @@ __global__ __launch_bounds__(kRouteThreads) void router_logits_kernel(
 // Block: 4 waves, WT x WE of them along tokens x experts; a wave computes 32
 // tokens x 64 experts, one instruction per k (two 32 x 32 blocks, its two
 // expert halves): lane L supplies token L % 32 and expert L of the wave's 64.
-// The stages of x and w sit in two LDS buffers as loaded (bf16 rows, one
-// 16-byte write per piece; 37 KB at 2 x 2 waves, so several blocks share a CU
-// and one's staging runs under another's MFMAs), the next step's pieces in
-// registers, and each group of 4 k's operands is read from LDS one group
-// ahead of its MFMAs, as one 8-byte read per operand widened to fp32 in
-// registers.  (Staged as k-major fp32 instead, with 8 conversions and 8
-// 4-byte writes per piece and 4-byte operand reads: large layer 0.540 ->
-// 0.521 ms for the route, same bits.  A wave tile of 64 x 64 as two chains,
-// one block per CU, measured 10% slower.)
+// The stages of x and w come as loaded (bf16 rows of 32 k) by direct-to-LDS
+// loads into a ring of four (55 KB at 2 x 2 waves), three steps of loads in
+// flight, and each group of 8 k's operands is read from LDS one group ahead
+// of its MFMAs, as one 16-byte read per operand widened to fp32 in registers.
+// (Measured on the large layer's route, same bits throughout: 0.540 ms with
+// k-major fp32 stages written from registers (8 conversions and 8 4-byte
+// writes per piece, 4-byte operand reads), 0.518 with bf16 rows written
+// from registers and 8-byte reads of 4 k, 0.511 / 0.497 with this ring and
+// 8- / 16-byte reads, 0.504 with a ring of three.  A wave tile of 64 x 64 as
+// two chains, one block per CU, measured 10% slower.)
 template <int WT, int WE, bool SPLIT>
 __global__ __launch_bounds__(kRouteThreads) void router_logits_mfma_kernel(
     int T, int H, int E, const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
@@ -245,13 +240,22 @@ __global__ __launch_bounds__(kRouteThreads) void router_logits_mfma_kernel(
     static_assert(WT * WE * kWave == kRouteThreads, "4 waves");
     constexpr int BT = 32 * WT;
     constexpr int BE = 64 * WE;
-    // the stage's bf16 pieces as loaded: row-major, k contiguous, each row
-    // padded (RS elements apart) so the rows a wave reads at one k offset
-    // spread over the banks
-    constexpr int RS = kStageK + kMfmaRowPad;
-    static_assert((RS * 2) % 16 == 0, "16-byte stage writes stay aligned");
-    __shared__ __attribute__((aligned(16))) uint16_t xs[2][BT * RS];
-    __shared__ __attribute__((aligned(16))) uint16_t ws[2][BE * RS];
+    // Stages arrive by direct-to-LDS loads, NB of them in a ring (the loads
+    // of NB - 1 steps in flight).  A stage is NG groups of 16 rows x 64 bytes
+    // (token rows, then expert rows), each group 1 KB written by one wave
+    // instruction and padded to 1152 bytes; in a group, lane l fills row l/4
+    // at chunk position l%4 with the row's chunk (l%4) ^ ((l/16) & 3), so the
+    // 16 rows of a group read at one k offset (16 bytes a lane) cover the 64
+    // banks once: a wave's 32 token rows take the two passes 512 bytes need.
+    constexpr int GX = BT / 16, GW = BE / 16, NG = GX + GW;
+    static_assert(NG % 4 == 0, "each wave loads NG / 4 groups");
+    constexpr int kPerWave = NG / 4;
+    constexpr int kGroupBytes = 1024 + 128;
+    constexpr int kStageBytes = NG * kGroupBytes;
+    constexpr int NB = 4;
+    __shared__ __attribute__((aligned(1024))) unsigned char sm[NB * kStageBytes];
+    const uint32_t lds0 =
+        (uint32_t)(uintptr_t)((__attribute__((address_space(3))) unsigned char*)sm);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -266,82 +270,76 @@ __global__ __launch_bounds__(kRouteThreads) void router_logits_mfma_kernel(
         k_end = min(H, k_begin + kLogitChunk);
     }
 
-    // piece c of a step: row c / 4, hidden indices k0 + 8 * (c % 4) .. + 7
-    constexpr int NX = (BT * 4 + kRouteThreads - 1) / kRouteThreads;
-    constexpr int NW = (BE * 4 + kRouteThreads - 1) / kRouteThreads;
-    uint4 xr[NX], wg[NW];
-    auto fetch = [&](int k0) {
+    // source rows of this wave's groups (rows past T or E load the last row;
+    // their results are dropped at the store)
+    const int rl = lane >> 2;
+    const int lchunk = (lane & 3) ^ ((rl >> 2) & 3);
+    const uint16_t* src[kPerWave];
 #pragma unroll
-        for (int i = 0; i < NX; ++i) {
-            const int c = tid + i * kRouteThreads;
-            const int t = t0 + (c >> 2);
-            xr[i] = make_uint4(0, 0, 0, 0);
-            if (c < BT * 4 && t < T)
-                xr[i] = *reinterpret_cast<const uint4*>(x + (size_t)t * H + k0 + (c & 3) * 8);
+    for (int i = 0; i < kPerWave; ++i) {
+        const int gi = wave * kPerWave + i;
+        if (gi < GX) {
+            const int t = min(t0 + gi * 16 + rl, T - 1);
+            src[i] = x + (size_t)t * H + lchunk * 8;
+        } else {
+            const int e = min(e0 + (gi - GX) * 16 + rl, E - 1);
+            src[i] = wr + (size_t)e * H + lchunk * 8;
         }
+    }
+    auto issue = [&](int st) {
+        const uint32_t sb = lds0 + (uint32_t)((st % NB) * kStageBytes);
+        const int k0 = k_begin + st * kStageK;
 #pragma unroll
-        for (int i = 0; i < NW; ++i) {
-            const int c = tid + i * kRouteThreads;
-            const int e = e0 + (c >> 2);
-            wg[i] = make_uint4(0, 0, 0, 0);
-            if (c < BE * 4 && e < E)
-                wg[i] = *reinterpret_cast<const uint4*>(wr + (size_t)e * H + k0 + (c & 3) * 8);
-        }
-    };
-    auto stage = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < NX; ++i) {
-            const int c = tid + i * kRouteThreads;
-            if (c >= BT * 4) continue;
-            *reinterpret_cast<uint4*>(&xs[buf][(c >> 2) * RS + (c & 3) * 8]) = xr[i];
-        }
-#pragma unroll
-        for (int i = 0; i < NW; ++i) {
-            const int c = tid + i * kRouteThreads;
-            if (c >= BE * 4) continue;
-            *reinterpret_cast<uint4*>(&ws[buf][(c >> 2) * RS + (c & 3) * 8]) = wg[i];
+        for (int i = 0; i < kPerWave; ++i) {
+            const int gi = wave * kPerWave + i;
+            asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                         :: "v"(src[i] + k0), "s"(sb + (uint32_t)(gi * kGroupBytes)) : "memory");
         }
     };
+    // this lane's token row and expert row: group, row in group, swizzle
+    const int tr = wt * 32 + (lane & 31), er = we * 64 + lane;
+    const int xoff = (tr >> 4) * kGroupBytes + (tr & 15) * 64, xsw = ((tr & 15) >> 2) & 3;
+    const int woff = (GX + (er >> 4)) * kGroupBytes + (er & 15) * 64, wsw = ((er & 15) >> 2) & 3;
 
     floatx32 acc, total;
 #pragma unroll
     for (int r = 0; r < 32; ++r) { acc[r] = 0.0f; total[r] = 0.0f; }
 
     const int nsteps = (k_end - k_begin) / kStageK;
-    if (nsteps > 0) fetch(k_begin);
+    for (int j = 0; j < NB - 1; ++j)
+        if (j < nsteps) issue(j);
     for (int st = 0; st < nsteps; ++st) {
         const int k0 = k_begin + st * kStageK;
-        const int buf = st & 1;
-        // buffer buf was last read in step st-2, before every wave passed the
-        // barrier of step st-1: one barrier per step
-        stage(buf);
-        __syncthreads();
-        if (st + 1 < nsteps) fetch(k0 + kStageK);
-        // this lane's token row and expert row of the stage
-        const uint16_t* xa = &xs[buf][(wt * 32 + (lane & 31)) * RS];
-        const uint16_t* wb = &ws[buf][(we * 64 + lane) * RS];
-        constexpr int G = 4;
+        // this wave's loads of stage st landed (those of the later stages
+        // already issued may stay in flight; loads complete in order), then
+        // every wave's
+        static_assert(NB == 4, "the waits below count two later stages at most");
+        const int later = min(NB - 2, nsteps - 1 - st);
+        if (later >= 2) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * kPerWave) : "memory");
+        else if (later == 1) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kPerWave) : "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        // the buffer of step st-1 is free: every wave read it before this barrier
+        if (st + NB - 1 < nsteps) issue(st + NB - 1);
+        const unsigned char* sb = sm + (st % NB) * kStageBytes;
+        constexpr int G = 8;
         float oa[2][G], ob[2][G];
-        // G = 4 consecutive k of each operand in one 8-byte read, widened
-        // from bf16 to fp32 (exact) by placing the 16 bits high
-        auto rd = [&](int slot, int k) {
-            const uint2 a = *reinterpret_cast<const uint2*>(xa + k);
-            const uint2 w = *reinterpret_cast<const uint2*>(wb + k);
-            oa[slot][0] = __uint_as_float(a.x << 16);
-            oa[slot][1] = __uint_as_float(a.x & 0xFFFF0000u);
-            oa[slot][2] = __uint_as_float(a.y << 16);
-            oa[slot][3] = __uint_as_float(a.y & 0xFFFF0000u);
-            ob[slot][0] = __uint_as_float(w.x << 16);
-            ob[slot][1] = __uint_as_float(w.x & 0xFFFF0000u);
-            ob[slot][2] = __uint_as_float(w.y << 16);
-            ob[slot][3] = __uint_as_float(w.y & 0xFFFF0000u);
+        auto rd = [&](int slot, int gk) {
+            const uint4 a = *reinterpret_cast<const uint4*>(sb + xoff + ((gk ^ xsw) << 4));
+            const uint4 w = *reinterpret_cast<const uint4*>(sb + woff + ((gk ^ wsw) << 4));
+            const uint32_t av[4] = {a.x, a.y, a.z, a.w}, wv[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                oa[slot][2 * j] = __uint_as_float(av[j] << 16);
+                oa[slot][2 * j + 1] = __uint_as_float(av[j] & 0xFFFF0000u);
+                ob[slot][2 * j] = __uint_as_float(wv[j] << 16);
+                ob[slot][2 * j + 1] = __uint_as_float(wv[j] & 0xFFFF0000u);
+            }
         };
         rd(0, 0);
 #pragma unroll
         for (int gk = 0; gk < kStageK / G; ++gk) {
-            if (gk + 1 < kStageK / G) rd((gk + 1) & 1, (gk + 1) * G);
-            // keep the next group's reads ahead of this group's MFMAs (the
-            // scheduler would otherwise sink each read to its MFMA)
+            if (gk + 1 < kStageK / G) rd((gk + 1) & 1, gk + 1);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int u = 0; u < G; ++u)
