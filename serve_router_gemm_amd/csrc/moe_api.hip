@@ -174,7 +174,6 @@ int enqueue_forward(int T, int H, int E, int F, int top_k, int score, int renorm
                     uint16_t* out, int32_t* topk_ids, float* topk_w, int variant, void* ws,
                     hipStream_t s) {
     const FwdLayout L = fwd_layout(T, H, E, F, top_k, variant);
-    const int A = T * top_k;
     int32_t* ids = topk_ids ? topk_ids : reinterpret_cast<int32_t*>(at(ws, L.ids));
     float* w = topk_w ? topk_w : reinterpret_cast<float*>(at(ws, L.w));
     int32_t* counts = reinterpret_cast<int32_t*>(at(ws, L.counts));
@@ -186,9 +185,9 @@ int enqueue_forward(int T, int H, int E, int F, int top_k, int score, int renorm
     int32_t* sched = reinterpret_cast<int32_t*>(at(ws, L.sched));
     uint16_t* hact = reinterpret_cast<uint16_t*>(at(ws, L.hact));
     float* y = reinterpret_cast<float*>(at(ws, L.y));
-    MOE_TRY(hip_rc(moe::launch_route(T, H, E, top_k, score, renormalize, x, w_router, bias, ids,
-                                     w, part, s)));
-    MOE_TRY(hip_rc(moe::launch_permute(A, E, ids, counts, offsets, perm, inv, pws, s)));
+    MOE_TRY(hip_rc(moe::launch_route_permute(T, H, E, top_k, score, renormalize, x, w_router,
+                                             bias, ids, w, part, counts, offsets, perm, inv, pws,
+                                             s)));
     void* vws = variant ? at(ws, L.var) : nullptr;
     MOE_TRY(hip_rc(moe::launch_gate_up(T, H, E, F, top_k, x, perm, offsets, w_gate, w_up, hact,
                                        sched, s, variant, vws)));
@@ -597,7 +596,6 @@ int moe_forward_fp8(int T, int H, int E, int F, int top_k, int score, int renorm
         return MOE_ERR_ALIGN;
     const Fwd8Layout L = fwd8_layout(T, H, E, F, top_k);
     if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
-    const int A = T * top_k;
     int32_t* ids = topk_ids ? topk_ids : reinterpret_cast<int32_t*>(at(ws, L.ids));
     float* w = topk_w ? topk_w : reinterpret_cast<float*>(at(ws, L.w));
     int32_t* counts = reinterpret_cast<int32_t*>(at(ws, L.counts));
@@ -613,10 +611,10 @@ int moe_forward_fp8(int T, int H, int E, int F, int top_k, int score, int renorm
     int8_t* ae = reinterpret_cast<int8_t*>(at(ws, L.ae));
     float* y = reinterpret_cast<float*>(at(ws, L.y));
     hipStream_t s = S(stream);
-    MOE_TRY(hip_rc(moe::launch_route(T, H, E, top_k, score, renormalize, x, w_router, bias, ids,
-                                     w, part, s)));
+    MOE_TRY(hip_rc(moe::launch_route_permute(T, H, E, top_k, score, renormalize, x, w_router,
+                                             bias, ids, w, part, counts, offsets, perm, inv, pws,
+                                             s)));
     MOE_TRY(hip_rc(moe::launch_quantize_fp8(T, H, 1, x, xq, xe, s)));
-    MOE_TRY(hip_rc(moe::launch_permute(A, E, ids, counts, offsets, perm, inv, pws, s)));
     MOE_TRY(hip_rc(moe::launch_gate_up_fp8(T, H, E, F, top_k, xq, xe, perm, offsets, wg_q, wg_e,
                                            wu_q, wu_e, aq, ae, nullptr, sched, s)));
     MOE_TRY(hip_rc(moe::launch_down_fp8(T, H, E, F, top_k, aq, ae, perm, offsets, wd_q, wd_e, y,

@@ -575,6 +575,74 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
     return m;
 }
 
+// The permutation outputs of a batch of at most 4 tokens, filled by the
+// select kernel itself (kPermute): one launch fewer for a decode-sized step.
+struct SmallPermute {
+    int32_t* counts;
+    int32_t* offsets;
+    int32_t* perm;
+    int32_t* inv_perm;
+};
+
+// The expert histogram, offsets and stable permutation of A <= 64
+// assignments (a = t*k + j), as the permute kernels compute them: counts[e];
+// offsets = their exclusive prefix in expert order, offsets[E] = A;
+// perm lists the assignments grouped by expert, ascending a inside each;
+// inv_perm[perm[p]] = p.  Each wave (one per token) leaves its k ids in LDS;
+// after the block barrier wave 0 holds assignment a in lane a.
+template <int kSelMaxQ>
+__device__ __forceinline__ void permute_tiny(int A, int E, int t, int k, const int* sel,
+                                             const SmallPermute& sp) {
+    __shared__ int s_ids[64];
+    __shared__ int s_off[64 * kSelMaxQ];
+    const int lane = threadIdx.x & 63;
+    for (int j = 0; j < k; ++j)
+        if (lane == j) s_ids[t * k + j] = sel[j];
+    __syncthreads();
+    if (t != 0) return;
+    const int ea = lane < A ? s_ids[lane] : -1;
+    // counts of experts lane + 64 q
+    int cnt[kSelMaxQ];
+#pragma unroll
+    for (int q = 0; q < kSelMaxQ; ++q) cnt[q] = 0;
+    for (int b = 0; b < A; ++b) {
+        const int eb = __builtin_amdgcn_readlane(ea, b);
+#pragma unroll
+        for (int q = 0; q < kSelMaxQ; ++q) cnt[q] += (lane + 64 * q == eb) ? 1 : 0;
+    }
+    // exclusive prefix in expert order (q major, lane minor)
+    int carry = 0;
+#pragma unroll
+    for (int q = 0; q < kSelMaxQ; ++q) {
+        int incl = cnt[q];
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int v = __shfl_up(incl, d, 64);
+            if (lane >= d) incl += v;
+        }
+        const int e = lane + 64 * q;
+        const int excl = carry + incl - cnt[q];
+        if (e < E) {
+            sp.counts[e] = cnt[q];
+            sp.offsets[e] = excl;
+            s_off[e] = excl;
+        }
+        carry += __builtin_amdgcn_readlane(incl, 63);
+    }
+    if (lane == 0) sp.offsets[E] = carry;
+    __builtin_amdgcn_wave_barrier();
+    // rank among the lower lanes with the same expert
+    int rank = 0;
+    for (int b = 0; b < A; ++b) {
+        const int eb = __builtin_amdgcn_readlane(ea, b);
+        rank += (b < lane && eb == ea) ? 1 : 0;
+    }
+    const bool valid = ea >= 0 && ea < E;
+    const int pos = valid ? s_off[ea] + rank : -1;
+    if (valid) sp.perm[pos] = lane;
+    if (lane < A) sp.inv_perm[lane] = pos;
+}
+
 // One wave per token: fold partial logits, keys, top-k, weights.  With
 // `replay` set (router replay), the experts of each slot are read from it
 // instead of selected, and only the weights are computed, by the same code:
@@ -585,13 +653,14 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 // step's 24 planes of a 6144-wide hidden state come in one batch).  The
 // bias is loaded before the fold, and each selected logit is read from its
 // owner lane into a scalar register (no LDS crossbar round trip per slot).
-template <int kSelMaxQ, int kSelBatch>
+template <int kSelMaxQ, int kSelBatch, bool kPermute>
 __global__ __launch_bounds__(256) void router_select_kernel(
     int T, int E, int k, int nparts, int score, int renorm, const float* __restrict__ part,
     const float* __restrict__ bias, const int32_t* __restrict__ replay,
-    int32_t* __restrict__ ids, float* __restrict__ wout) {
+    int32_t* __restrict__ ids, float* __restrict__ wout, SmallPermute sp) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    // (with kPermute the block is one wave per token: none leaves here)
     if (t >= T) return;  // whole wave leaves together
 
     float bz[kSelMaxQ];
@@ -701,6 +770,7 @@ __global__ __launch_bounds__(256) void router_select_kernel(
             if (!replay) ids[(size_t)t * k + j] = sel[j];
             wout[(size_t)t * k + j] = p[j];
         }
+    if constexpr (kPermute) permute_tiny<kSelMaxQ>(T * k, E, t, k, sel, sp);
 }
 
 template <int TT, int TE, bool SPLIT, bool PF = false>
@@ -798,42 +868,53 @@ hipError_t launch_lm_logits(int T, int H, int V, const uint16_t* h, const uint16
 // them all (at most 128 values per lane), since unused slots of a batch still
 // take registers and so waves per SIMD (8 planes in the tie layer's 8192
 // tokens with a 32-plane batch: 0.117 -> 0.123 ms).
-template <int Q, int B>
+template <int Q, int B, bool P>
 hipError_t launch_select_qb(int T, int E, int k, int nparts, int score, int renorm,
                             const float* part, const float* bias, const int32_t* replay,
-                            int32_t* ids, float* w, hipStream_t s) {
-    router_select_kernel<Q, B><<<(T + 3) / 4, 256, 0, s>>>(T, E, k, nparts, score, renorm, part,
-                                                          bias, replay, ids, w);
+                            int32_t* ids, float* w, const SmallPermute& sp, hipStream_t s) {
+    // with the permutation: one block of one wave per token (T <= 4)
+    const int blocks = P ? 1 : (T + 3) / 4;
+    const int threads = P ? 64 * T : 256;
+    router_select_kernel<Q, B, P><<<blocks, threads, 0, s>>>(T, E, k, nparts, score, renorm,
+                                                             part, bias, replay, ids, w, sp);
     return hipGetLastError();
 }
 
-template <int Q>
+template <int Q, bool P>
 hipError_t launch_select_q(int T, int E, int k, int nparts, int score, int renorm,
                            const float* part, const float* bias, const int32_t* replay,
-                           int32_t* ids, float* w, hipStream_t s) {
+                           int32_t* ids, float* w, const SmallPermute& sp, hipStream_t s) {
     constexpr int kMaxBatch = 128 / Q;
     if (nparts <= 1)
-        return launch_select_qb<Q, 1>(T, E, k, nparts, score, renorm, part, bias, replay, ids, w, s);
+        return launch_select_qb<Q, 1, P>(T, E, k, nparts, score, renorm, part, bias, replay, ids,
+                                         w, sp, s);
     if (nparts <= 8 || kMaxBatch < 16)
-        return launch_select_qb<Q, 8>(T, E, k, nparts, score, renorm, part, bias, replay, ids, w, s);
+        return launch_select_qb<Q, 8, P>(T, E, k, nparts, score, renorm, part, bias, replay, ids,
+                                         w, sp, s);
     if (nparts <= 16 || kMaxBatch < 32)
-        return launch_select_qb<Q, 16>(T, E, k, nparts, score, renorm, part, bias, replay, ids, w, s);
-    return launch_select_qb<Q, 32>(T, E, k, nparts, score, renorm, part, bias, replay, ids, w, s);
+        return launch_select_qb<Q, 16, P>(T, E, k, nparts, score, renorm, part, bias, replay, ids,
+                                          w, sp, s);
+    return launch_select_qb<Q, 32, P>(T, E, k, nparts, score, renorm, part, bias, replay, ids, w,
+                                      sp, s);
 }
 
+template <bool P>
 hipError_t launch_select(int T, int E, int k, int nparts, int score, int renorm,
                          const float* part, const float* bias, const int32_t* replay,
-                         int32_t* ids, float* w, hipStream_t s) {
-    if (E <= 64) return launch_select_q<1>(T, E, k, nparts, score, renorm, part, bias, replay, ids, w, s);
-    if (E <= 128) return launch_select_q<2>(T, E, k, nparts, score, renorm, part, bias, replay, ids, w, s);
-    if (E <= 256) return launch_select_q<4>(T, E, k, nparts, score, renorm, part, bias, replay, ids, w, s);
-    return launch_select_q<8>(T, E, k, nparts, score, renorm, part, bias, replay, ids, w, s);
+                         int32_t* ids, float* w, const SmallPermute& sp, hipStream_t s) {
+    if (E <= 64)
+        return launch_select_q<1, P>(T, E, k, nparts, score, renorm, part, bias, replay, ids, w, sp, s);
+    if (E <= 128)
+        return launch_select_q<2, P>(T, E, k, nparts, score, renorm, part, bias, replay, ids, w, sp, s);
+    if (E <= 256)
+        return launch_select_q<4, P>(T, E, k, nparts, score, renorm, part, bias, replay, ids, w, sp, s);
+    return launch_select_q<8, P>(T, E, k, nparts, score, renorm, part, bias, replay, ids, w, sp, s);
 }
 
-hipError_t launch_route(int T, int H, int E, int k, int score, int renorm, const uint16_t* x,
-                        const uint16_t* wr, const float* bias, int32_t* ids, float* w,
-                        float* part_ws, hipStream_t s, const int32_t* replay) {
-    const RoutePlan p = route_plan(T, H, E);
+namespace {
+
+hipError_t launch_route_logits(const RoutePlan& p, int T, int H, int E, const uint16_t* x,
+                               const uint16_t* wr, float* part_ws, hipStream_t s) {
     hipError_t err;
     if (p.mfma) {
         err = p.split ? launch_logits_mfma_plan<true>(p, T, H, E, x, wr, part_ws, s)
@@ -859,8 +940,37 @@ hipError_t launch_route(int T, int H, int E, int k, int score, int renorm, const
     } else {
         err = launch_logits<kBigTT, 8, false>(T, H, E, x, wr, part_ws, s);
     }
+    return err;
+}
+
+}  // namespace
+
+hipError_t launch_route(int T, int H, int E, int k, int score, int renorm, const uint16_t* x,
+                        const uint16_t* wr, const float* bias, int32_t* ids, float* w,
+                        float* part_ws, hipStream_t s, const int32_t* replay) {
+    const RoutePlan p = route_plan(T, H, E);
+    const hipError_t err = launch_route_logits(p, T, H, E, x, wr, part_ws, s);
     if (err != hipSuccess) return err;
-    return launch_select(T, E, k, p.nparts, score, renorm, part_ws, bias, replay, ids, w, s);
+    return launch_select<false>(T, E, k, p.nparts, score, renorm, part_ws, bias, replay, ids, w,
+                                SmallPermute{}, s);
+}
+
+hipError_t launch_route_permute(int T, int H, int E, int k, int score, int renorm,
+                                const uint16_t* x, const uint16_t* wr, const float* bias,
+                                int32_t* ids, float* w, float* part_ws, int32_t* counts,
+                                int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                                int32_t* permute_ws, hipStream_t s) {
+    if (T < 1 || T > kRoutePermuteMaxT) {
+        const hipError_t err = launch_route(T, H, E, k, score, renorm, x, wr, bias, ids, w,
+                                            part_ws, s);
+        if (err != hipSuccess) return err;
+        return launch_permute(T * k, E, ids, counts, offsets, perm, inv_perm, permute_ws, s);
+    }
+    const RoutePlan p = route_plan(T, H, E);
+    const hipError_t err = launch_route_logits(p, T, H, E, x, wr, part_ws, s);
+    if (err != hipSuccess) return err;
+    return launch_select<true>(T, E, k, p.nparts, score, renorm, part_ws, bias, nullptr, ids, w,
+                               SmallPermute{counts, offsets, perm, inv_perm}, s);
 }
 
 }  // namespace moe
