@@ -321,3 +321,27 @@ def test_decode_probe_invariant_and_variant_drift():
     log(f"[decode] invariant: 0 differing bits, k3 = 0; split-K variant: "
         f"{drift_bits} differing bits, max k3 {drift_k3:.3e} (threshold 1e-3)")
     assert drift_bits > 0
+
+
+@pytest.mark.parametrize("E,k", [(8, 2), (64, 8), (200, 8), (512, 16)])
+def test_tiny_batch_forward_equals_separate_calls(E, k):
+    """moe_forward with at most 4 tokens lets the select kernel also build the
+    expert histogram, offsets and permutation (one launch fewer).  Its outputs
+    and routing must equal those of moe_route, moe_permute, the two expert
+    GEMMs and moe_combine called one after another, bit for bit, at T = 1..4
+    (and at T = 5, which takes the separate launches inside moe_forward too)."""
+    cfg = _cfg("mid", E=E, k=k, H=512, F=256)
+    L = layer(cfg)
+    x_all = I.make_tokens(5, cfg.H, 777 + E, "cpu").to(DEV)
+    for T in (1, 2, 3, 4, 5):
+        x = x_all[:T].contiguous()
+        out, ids, w = fwd(cfg, L, x)
+        ids2, w2 = M.route(x, L["w_router"], cfg.k, cfg.score, cfg.renorm, bias=L["bias"])
+        counts, offs, perm, inv = M.permute(ids2, cfg.E)
+        h = M.expert_gate_up(x, perm, offs, L["w_gate"], L["w_up"], cfg.k)
+        y = M.expert_down(h, perm, offs, L["w_down"], cfg.k)
+        out2 = M.combine(y, w2)
+        assert torch.equal(ids, ids2), (E, k, T)
+        assert torch.equal(w.view(torch.int32), w2.view(torch.int32)), (E, k, T)
+        assert np.array_equal(bits(out), bits(out2)), (E, k, T)
+    log(f"[tiny batch] E={E} k={k}: moe_forward == separate calls at T = 1..5")
