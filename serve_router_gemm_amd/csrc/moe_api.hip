@@ -10,6 +10,19 @@
 #include "../../include/moe.h"
 #include "moe_internal.h"
 
+namespace moe {
+// Route and permute in one call (moe_route.hip): for batches of at most 4
+// tokens the select kernel also writes counts, offsets, perm and inv_perm
+// (one launch fewer); larger batches run launch_route, then launch_permute.
+// The outputs are those of the two calls.  (Declared here, its only caller,
+// rather than among the shared declarations the expert GEMMs build against.)
+hipError_t launch_route_permute(int T, int H, int E, int k, int score, int renorm,
+                                const uint16_t* x, const uint16_t* wr, const float* bias,
+                                int32_t* ids, float* w, float* part_ws, int32_t* counts,
+                                int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                                int32_t* permute_ws, hipStream_t s);
+}  // namespace moe
+
 namespace {
 
 using moe::launch_combine;

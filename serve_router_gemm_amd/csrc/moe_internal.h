@@ -30,17 +30,6 @@ hipError_t launch_route(int T, int H, int E, int k, int score, int renorm,
                         int32_t* ids, float* w, float* part_ws, hipStream_t s,
                         const int32_t* replay = nullptr);
 
-// Route and permute in one call: for batches of at most kRoutePermuteMaxT
-// tokens the select kernel also writes counts, offsets, perm and inv_perm
-// (one launch fewer); larger batches run launch_route, then launch_permute.
-// The outputs are those of the two calls.
-constexpr int kRoutePermuteMaxT = 4;
-hipError_t launch_route_permute(int T, int H, int E, int k, int score, int renorm,
-                                const uint16_t* x, const uint16_t* wr, const float* bias,
-                                int32_t* ids, float* w, float* part_ws, int32_t* counts,
-                                int32_t* offsets, int32_t* perm, int32_t* inv_perm,
-                                int32_t* permute_ws, hipStream_t s);
-
 // permute ------------------------------------------------------------------
 int permute_chunk(int A);
 size_t permute_ws_bytes(int A, int E);

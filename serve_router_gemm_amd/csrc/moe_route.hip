@@ -955,6 +955,12 @@ hipError_t launch_route(int T, int H, int E, int k, int score, int renorm, const
                                 SmallPermute{}, s);
 }
 
+// Route and permute in one call: for batches of at most kRoutePermuteMaxT
+// tokens (one wave each in the select kernel's single block, at most 64
+// assignments) the select kernel also writes counts, offsets, perm and
+// inv_perm; larger batches run launch_route, then launch_permute.
+constexpr int kRoutePermuteMaxT = 4;
+
 hipError_t launch_route_permute(int T, int H, int E, int k, int score, int renorm,
                                 const uint16_t* x, const uint16_t* wr, const float* bias,
                                 int32_t* ids, float* w, float* part_ws, int32_t* counts,
