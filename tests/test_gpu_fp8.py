@@ -485,3 +485,30 @@ def test_forward_fp8_empty_batch():
     x = torch.empty((0, cfg.H), dtype=torch.bfloat16, device=DEV)
     out = M.forward_fp8(x, L["w_router"], wqd, cfg.k, cfg.score, cfg.renorm)
     assert out.shape == (0, cfg.H)
+
+
+@pytest.mark.parametrize("E,k", [(64, 8), (200, 8), (512, 16)])
+def test_tiny_batch_forward_fp8_equals_separate_calls(E, k):
+    """moe_forward_fp8 with at most 4 tokens builds the permutation inside the
+    select kernel; its output and routing must equal moe_route, moe_permute,
+    moe_quantize_fp8 of x, the two FP8 GEMMs and moe_combine called one after
+    another, bit for bit, at T = 1..5."""
+    cfg = I.scaled(I.CONFIGS["mid"], E=E, k=k, H=512, F=256)
+    L = layer(cfg)
+    wqd = M.quantize_weights_fp8(L["w_gate"], L["w_up"], L["w_down"])
+    x_all = I.make_tokens(5, cfg.H, 991 + E, "cpu").to(DEV)
+    for T in (1, 2, 3, 4, 5):
+        x = x_all[:T].contiguous()
+        out, ids, w = M.forward_fp8(x, L["w_router"], wqd, cfg.k, cfg.score, cfg.renorm,
+                                    bias=L["bias"], return_routing=True)
+        ids2, w2 = M.route(x, L["w_router"], cfg.k, cfg.score, cfg.renorm, bias=L["bias"])
+        counts, offs, perm, inv = M.permute(ids2, cfg.E)
+        xq, xe = M.quantize_fp8(x, 1)
+        aq, ae, _ = M.expert_gate_up_fp8(xq, xe, perm, offs, wqd["wg_q"], wqd["wg_e"],
+                                         wqd["wu_q"], wqd["wu_e"], cfg.k)
+        y = M.expert_down_fp8(aq, ae, perm, offs, wqd["wd_q"], wqd["wd_e"], cfg.k)
+        out2 = M.combine(y, w2)
+        assert torch.equal(ids, ids2), (E, k, T)
+        assert torch.equal(w.view(torch.int32), w2.view(torch.int32)), (E, k, T)
+        assert np.array_equal(bits(out), bits(out2)), (E, k, T)
+    log(f"[fp8 tiny batch] E={E} k={k}: moe_forward_fp8 == separate calls at T = 1..5")
