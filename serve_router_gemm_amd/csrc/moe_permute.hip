@@ -26,7 +26,8 @@ namespace {
 constexpr int kHistThreads = 256;
 constexpr int kMaxExperts = 512;
 constexpr int kExpertBits = 9;   // ids < 512
-constexpr int kScanBatch = 16;   // chunk counts loaded together in the scan
+constexpr int kScanBatch = 64;   // chunk counts loaded together in the scan (against 16:
+                                 // A = 131072 permute 39.8 -> 38.6 us, A = 2^21 142 -> 128 us)
 
 __global__ __launch_bounds__(kHistThreads) void permute_hist_kernel(
     int A, int E, int chunk, const int32_t* __restrict__ ids, int32_t* __restrict__ bh) {
