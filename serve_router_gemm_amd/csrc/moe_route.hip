@@ -591,13 +591,12 @@ struct SmallPermute {
 // inv_perm[perm[p]] = p.  Each wave (one per token) leaves its k ids in LDS;
 // after the block barrier wave 0 holds assignment a in lane a.
 template <int kSelMaxQ>
-__device__ __forceinline__ void permute_tiny(int A, int E, int t, int k, const int* sel,
+__device__ __forceinline__ void permute_tiny(int A, int E, int t, int k, int my_sel,
                                              const SmallPermute& sp) {
     __shared__ int s_ids[64];
     __shared__ int s_off[64 * kSelMaxQ];
     const int lane = threadIdx.x & 63;
-    for (int j = 0; j < k; ++j)
-        if (lane == j) s_ids[t * k + j] = sel[j];
+    if (lane < k) s_ids[t * k + lane] = my_sel;
     __syncthreads();
     if (t != 0) return;
     const int ea = lane < A ? s_ids[lane] : -1;
@@ -717,29 +716,36 @@ __global__ __launch_bounds__(256) void router_select_kernel(
         return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), owner));
     };
 
-    int sel[16];
-    float lsel[16];
+    // slot j's expert and logit end up in lane j, which computes that slot's
+    // weight (the same expression for every slot as a wave-wide loop would
+    // evaluate; the renormalising sum still runs over j in order)
+    int my_sel = -1;
+    float my_l = 0.0f;
     for (int j = 0; j < k; ++j) {
+        int e;
+        float l;
         if (replay) {
-            const int e = replay[(size_t)t * k + j];
-            sel[j] = e;
-            lsel[j] = (e >= 0 && e < E) ? logit_of(e) : 0.0f;
-            continue;
+            e = replay[(size_t)t * k + j];
+            l = (e >= 0 && e < E) ? logit_of(e) : 0.0f;
+        } else {
+            uint64_t best = rk[0];
+#pragma unroll
+            for (int q = 1; q < kSelMaxQ; ++q) best = rk[q] > best ? rk[q] : best;
+            best = wave_max_u64(best);
+            e = (int)(~(uint32_t)best);
+            const int qs = e >> 6, owner = e & 63;
+#pragma unroll
+            for (int q = 0; q < kSelMaxQ; ++q)
+                if (q == qs && lane == owner) rk[q] = 0;  // taken
+            l = logit_of(e);
         }
-        uint64_t best = rk[0];
-#pragma unroll
-        for (int q = 1; q < kSelMaxQ; ++q) best = rk[q] > best ? rk[q] : best;
-        best = wave_max_u64(best);
-        const int e = (int)(~(uint32_t)best);
-        const int qs = e >> 6, owner = e & 63;
-#pragma unroll
-        for (int q = 0; q < kSelMaxQ; ++q)
-            if (q == qs && lane == owner) rk[q] = 0;  // taken
-        sel[j] = e;
-        lsel[j] = logit_of(e);
+        if (lane == j) {
+            my_sel = e;
+            my_l = l;
+        }
     }
 
-    float p[16];
+    float p;
     if (score == 0) {
         float m = -INFINITY;
 #pragma unroll
@@ -751,26 +757,26 @@ __global__ __launch_bounds__(256) void router_select_kernel(
 #pragma unroll
         for (int q = 0; q < kSelMaxQ; ++q)
             if (lane + 64 * q < E) S = S + expf(lg[q] - m);
+        // (the butterfly gives every lane the same sum: each step adds the
+        // same two values on both lanes of a pair)
 #pragma unroll
         for (int s = 32; s >= 1; s >>= 1) S = S + __shfl_xor(S, s, 64);
-        for (int j = 0; j < k; ++j) p[j] = expf(lsel[j] - m) / S;
+        p = expf(my_l - m) / S;
     } else {
-        for (int j = 0; j < k; ++j) p[j] = 1.0f / (1.0f + expf(-lsel[j]));
+        p = 1.0f / (1.0f + expf(-my_l));
     }
-    if (replay)
-        for (int j = 0; j < k; ++j)
-            if (sel[j] < 0 || sel[j] >= E) p[j] = 0.0f;
+    if (replay && (my_sel < 0 || my_sel >= E)) p = 0.0f;
     if (renorm) {
         float D = 0.0f;
-        for (int j = 0; j < k; ++j) D = D + p[j];
-        for (int j = 0; j < k; ++j) p[j] = D > 0.0f ? p[j] / D : 0.0f;
+        for (int j = 0; j < k; ++j)
+            D = D + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), j));
+        p = D > 0.0f ? p / D : 0.0f;
     }
-    for (int j = 0; j < k; ++j)
-        if (lane == j) {
-            if (!replay) ids[(size_t)t * k + j] = sel[j];
-            wout[(size_t)t * k + j] = p[j];
-        }
-    if constexpr (kPermute) permute_tiny<kSelMaxQ>(T * k, E, t, k, sel, sp);
+    if (lane < k) {
+        if (!replay) ids[(size_t)t * k + lane] = my_sel;
+        wout[(size_t)t * k + lane] = p;
+    }
+    if constexpr (kPermute) permute_tiny<kSelMaxQ>(T * k, E, t, k, my_sel, sp);
 }
 
 template <int TT, int TE, bool SPLIT, bool PF = false>
