@@ -594,49 +594,54 @@ template <int kSelMaxQ>
 __device__ __forceinline__ void permute_tiny(int A, int E, int t, int k, int my_sel,
                                              const SmallPermute& sp) {
     __shared__ int s_ids[64];
+    __shared__ int s_cnt[64 * kSelMaxQ];
     __shared__ int s_off[64 * kSelMaxQ];
     const int lane = threadIdx.x & 63;
     if (lane < k) s_ids[t * k + lane] = my_sel;
     __syncthreads();
     if (t != 0) return;
     const int ea = lane < A ? s_ids[lane] : -1;
-    // counts of experts lane + 64 q
-    int cnt[kSelMaxQ];
+    const bool valid = ea >= 0 && ea < E;
+    // lanes holding the same expert: one ballot per bit of the id (E <= 512)
+    uint64_t same = __ballot(valid);
+    if (!valid) same = 0;
 #pragma unroll
-    for (int q = 0; q < kSelMaxQ; ++q) cnt[q] = 0;
-    for (int b = 0; b < A; ++b) {
-        const int eb = __builtin_amdgcn_readlane(ea, b);
-#pragma unroll
-        for (int q = 0; q < kSelMaxQ; ++q) cnt[q] += (lane + 64 * q == eb) ? 1 : 0;
+    for (int bt = 0; bt < 9; ++bt) {
+        const bool bit = valid && ((ea >> bt) & 1);
+        const uint64_t bal = __ballot(bit);
+        same &= bit ? bal : ~bal;
     }
+    const uint64_t lower = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    const int rank = __popcll(same & lower);   // lower lanes with this expert
+    const int cnt = __popcll(same);
+    // counts: zero, then the last lane of each expert's group writes the count
+#pragma unroll
+    for (int q = 0; q < kSelMaxQ; ++q) s_cnt[lane + 64 * q] = 0;
+    __builtin_amdgcn_wave_barrier();
+    if (valid && rank == cnt - 1) s_cnt[ea] = cnt;
+    __builtin_amdgcn_wave_barrier();
     // exclusive prefix in expert order (q major, lane minor)
     int carry = 0;
 #pragma unroll
     for (int q = 0; q < kSelMaxQ; ++q) {
-        int incl = cnt[q];
+        const int e = lane + 64 * q;
+        const int c = s_cnt[e];
+        int incl = c;
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
             const int v = __shfl_up(incl, d, 64);
             if (lane >= d) incl += v;
         }
-        const int e = lane + 64 * q;
-        const int excl = carry + incl - cnt[q];
+        const int excl = carry + incl - c;
         if (e < E) {
-            sp.counts[e] = cnt[q];
+            sp.counts[e] = c;
             sp.offsets[e] = excl;
-            s_off[e] = excl;
         }
+        s_off[e] = excl;
         carry += __builtin_amdgcn_readlane(incl, 63);
     }
     if (lane == 0) sp.offsets[E] = carry;
     __builtin_amdgcn_wave_barrier();
-    // rank among the lower lanes with the same expert
-    int rank = 0;
-    for (int b = 0; b < A; ++b) {
-        const int eb = __builtin_amdgcn_readlane(ea, b);
-        rank += (b < lane && eb == ea) ? 1 : 0;
-    }
-    const bool valid = ea >= 0 && ea < E;
     const int pos = valid ? s_off[ea] + rank : -1;
     if (valid) sp.perm[pos] = lane;
     if (lane < A) sp.inv_perm[lane] = pos;
