@@ -16,6 +16,8 @@
 //   scatter one wave per chunk, 64 assignments per step in order: lanes with
 //           the same expert find each other by ballots over the expert-id
 //           bits, the rank inside the step is a popcount of the lower lanes
+#include <algorithm>
+
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -128,18 +130,24 @@ __global__ __launch_bounds__(kWave) void permute_scatter_kernel(
 }
 
 // Small batches (A <= kSmallA assignments): the three steps above in one
-// block of 16 waves, so a decode-sized step pays one launch for them.  Wave w
-// takes the w-th chunk of kSmallChunk assignments: per-wave histograms in LDS,
-// then per expert the prefix over waves (the chunk bases) and the exclusive
-// prefix over experts (offsets), then each wave places its chunk in order
-// with the same ballot ranking.  Same permutation as the three launches.
+// block of 16 waves, so a small step pays one launch for them.  Wave w takes
+// the w-th chunk of `chunk` assignments (A / 16 rounded up to whole waves):
+// per-wave histograms in LDS, then per expert the prefix over waves (the
+// chunk bases) and the exclusive prefix over experts (offsets), then each
+// wave places its chunk in order with the same ballot ranking.  Same
+// permutation as the three launches.
 constexpr int kSmallThreads = 1024;
 constexpr int kSmallWaves = kSmallThreads / kWave;   // 16
-constexpr int kSmallChunk = 256;
-constexpr int kSmallA = kSmallWaves * kSmallChunk;   // 4096
+constexpr int kSmallMaxChunk = 1024;
+constexpr int kSmallA = kSmallWaves * kSmallMaxChunk;   // 16384
+
+int small_chunk(int A) {
+    const int per_wave = (A + kSmallWaves - 1) / kSmallWaves;
+    return std::max(kWave, (per_wave + kWave - 1) / kWave * kWave);
+}
 
 __global__ __launch_bounds__(kSmallThreads) void permute_small_kernel(
-    int A, int E, const int32_t* __restrict__ ids, int32_t* __restrict__ counts,
+    int A, int E, int chunk, const int32_t* __restrict__ ids, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm) {
     __shared__ int hw[kSmallWaves][kMaxExperts];   // per-wave counts, then per-wave bases
     __shared__ int sc[kMaxExperts];
@@ -148,8 +156,8 @@ __global__ __launch_bounds__(kSmallThreads) void permute_small_kernel(
     const int wave = tid >> 6;
     for (int i = tid; i < kSmallWaves * kMaxExperts; i += kSmallThreads) (&hw[0][0])[i] = 0;
     __syncthreads();
-    const int a0 = wave * kSmallChunk;
-    const int a1 = min(A, a0 + kSmallChunk);
+    const int a0 = wave * chunk;
+    const int a1 = min(A, a0 + chunk);
     for (int a = a0 + lane; a < a1; a += kWave) {
         const int e = ids[a];
         if (e >= 0 && e < E) atomicAdd(&hw[wave][e], 1);
@@ -226,8 +234,8 @@ size_t permute_ws_bytes(int A, int E) {
 hipError_t launch_permute(int A, int E, const int32_t* ids, int32_t* counts, int32_t* offsets,
                           int32_t* perm, int32_t* inv_perm, int32_t* ws, hipStream_t s) {
     if (A <= kSmallA) {
-        permute_small_kernel<<<1, kSmallThreads, 0, s>>>(A, E, ids, counts, offsets, perm,
-                                                         inv_perm);
+        permute_small_kernel<<<1, kSmallThreads, 0, s>>>(A, E, small_chunk(A), ids, counts,
+                                                         offsets, perm, inv_perm);
         return hipGetLastError();
     }
     const int chunk = permute_chunk(A);

@@ -95,11 +95,11 @@ def test_permute_checks(L):
     assert p(4, 8, 2, None, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == NULL
     assert p(4, 8, 9, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == SHAPE
     assert p(4, 8, 2, FAKE, FAKE, MIS, FAKE, FAKE, FAKE, 0, None) == ALIGN
-    # small batches (<= 4096 assignments) need no workspace; larger ones do
-    assert L.moe_workspace_bytes(M.OP_PERMUTE, 512, 64, 8, 64, 8, 0) == 0
-    assert L.moe_workspace_bytes(M.OP_PERMUTE, 513, 64, 8, 64, 8, 0) > 0
-    assert p(513, 8, 8, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == NULL
-    assert p(513, 8, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == WS
+    # small batches (<= 16384 assignments) need no workspace; larger ones do
+    assert L.moe_workspace_bytes(M.OP_PERMUTE, 2048, 64, 8, 64, 8, 0) == 0
+    assert L.moe_workspace_bytes(M.OP_PERMUTE, 2049, 64, 8, 64, 8, 0) > 0
+    assert p(2049, 8, 8, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == NULL
+    assert p(2049, 8, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == WS
     assert p(0, 8, 2, None, None, None, None, None, None, 0, None) == OK
 
 
