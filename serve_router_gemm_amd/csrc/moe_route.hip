@@ -220,7 +220,8 @@ __global__ __launch_bounds__(kRouteThreads) void router_logits_kernel(
 // infinities and NaN: chains of either are bit-identical).  A chain of these
 // instructions over k ascending is thus the chain of the kernel above, bit
 // for bit, at the matrix cores' fp32 rate (twice the non-packed VALU rate).
-// Block: 4 waves, WT x WE of them along tokens x experts; a wave computes 32
+// Block: 4 or 8 waves, WT x WE of them along tokens x experts (the first 4
+// issue the loads); a wave computes 32
 // tokens x 64 experts, one instruction per k (two 32 x 32 blocks, its two
 // expert halves): lane L supplies token L % 32 and expert L of the wave's 64.
 // The stages of x and w come as loaded (bf16 rows of 32 k) by direct-to-LDS
@@ -234,10 +235,10 @@ __global__ __launch_bounds__(kRouteThreads) void router_logits_kernel(
 // 8- / 16-byte reads, 0.504 with a ring of three.  A wave tile of 64 x 64 as
 // two chains, one block per CU, measured 10% slower.)
 template <int WT, int WE, bool SPLIT>
-__global__ __launch_bounds__(kRouteThreads) void router_logits_mfma_kernel(
+__global__ __launch_bounds__(WT * WE * kWave) void router_logits_mfma_kernel(
     int T, int H, int E, const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
     float* __restrict__ part) {
-    static_assert(WT * WE * kWave == kRouteThreads, "4 waves");
+    static_assert(WT * WE == 4 || WT * WE == 8, "4 or 8 waves; the first 4 issue the loads");
     constexpr int BT = 32 * WT;
     constexpr int BE = 64 * WE;
     // Stages arrive by direct-to-LDS loads, NB of them in a ring (the loads
@@ -248,7 +249,7 @@ __global__ __launch_bounds__(kRouteThreads) void router_logits_mfma_kernel(
     // 16 rows of a group read at one k offset (16 bytes a lane) cover the 64
     // banks once: a wave's 32 token rows take the two passes 512 bytes need.
     constexpr int GX = BT / 16, GW = BE / 16, NG = GX + GW;
-    static_assert(NG % 4 == 0, "each wave loads NG / 4 groups");
+    static_assert(NG % 4 == 0, "each issuing wave loads NG / 4 groups");
     constexpr int kPerWave = NG / 4;
     constexpr int kGroupBytes = 1024 + 128;
     constexpr int kStageBytes = NG * kGroupBytes;
@@ -277,7 +278,7 @@ __global__ __launch_bounds__(kRouteThreads) void router_logits_mfma_kernel(
     const uint16_t* src[kPerWave];
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i) {
-        const int gi = wave * kPerWave + i;
+        const int gi = min(wave, 3) * kPerWave + i;
         if (gi < GX) {
             const int t = min(t0 + gi * 16 + rl, T - 1);
             src[i] = x + (size_t)t * H + lchunk * 8;
@@ -287,6 +288,7 @@ __global__ __launch_bounds__(kRouteThreads) void router_logits_mfma_kernel(
         }
     }
     auto issue = [&](int st) {
+        if (wave >= 4) return;
         const uint32_t sb = lds0 + (uint32_t)((st % NB) * kStageBytes);
         const int k0 = k_begin + st * kStageK;
 #pragma unroll
@@ -800,13 +802,15 @@ hipError_t launch_logits_mfma(int T, int H, int E, const uint16_t* x, const uint
     constexpr int BT = 32 * WT, BE = 64 * WE;
     const int nchunks = (H + kLogitChunk - 1) / kLogitChunk;
     dim3 grid((T + BT - 1) / BT, (E + BE - 1) / BE, SPLIT ? nchunks : 1);
-    router_logits_mfma_kernel<WT, WE, SPLIT><<<grid, kRouteThreads, 0, s>>>(T, H, E, x, wr, part);
+    router_logits_mfma_kernel<WT, WE, SPLIT><<<grid, WT * WE * kWave, 0, s>>>(T, H, E, x, wr,
+                                                                             part);
     return hipGetLastError();
 }
 
 template <bool SPLIT>
 hipError_t launch_logits_mfma_plan(const RoutePlan& p, int T, int H, int E, const uint16_t* x,
                                    const uint16_t* wr, float* part, hipStream_t s) {
+    if (p.we == 4) return launch_logits_mfma<2, 4, SPLIT>(T, H, E, x, wr, part, s);
     if (p.we == 2) return launch_logits_mfma<2, 2, SPLIT>(T, H, E, x, wr, part, s);
     return launch_logits_mfma<4, 1, SPLIT>(T, H, E, x, wr, part, s);
 }
@@ -824,10 +828,22 @@ RoutePlan route_plan(int T, int H, int E) {
     p.wt = 1;
     p.we = 4;
     const int nchunks = (H + kLogitChunk - 1) / kLogitChunk;
-    // matrix cores where they fill the chip: 32 x 64 per wave, the block's 4
+    // More than 128 experts and tokens enough for a block of 8 waves per CU:
+    // 64 tokens x 256 experts per block, so each token row is staged once
+    // (large layer: route 0.58 -> 0.55 ms in the step; with a block per chunk
+    // the 4-wave blocks below stay faster)
+    if (E > 128) {
+        const long mb8 = (long)((T + 63) / 64) * ((E + 255) / 256);
+        if (mb8 >= 256) {
+            p.mfma = 1; p.wt = 2; p.we = 4; p.tt = 8; p.te = 8;
+            p.split = 0; p.nparts = 1;
+            return p;
+        }
+    }
+    // else matrix cores where they fill the chip: 32 x 64 per wave, the block's 4
     // waves 2 x 2 (E > 64: 64 tokens x 128 experts) or 4 x 1 (128 x 64) along
     // tokens x experts; every chunk folded in the kernel when that alone gives
-    // two blocks per CU (the large layer: one plane instead of one per chunk),
+    // two blocks per CU (16384 tokens: one plane instead of one per chunk),
     // else one block per chunk for batches of 512 tokens or more with a block
     // per CU (mid T = 4096: 0.048 -> 0.037 ms against the VALU plan)
     {
