@@ -421,8 +421,14 @@ __global__ __launch_bounds__(kP_Threads) void expert_gemm_pipe_kernel(GemmParams
 // output tiles).  Here a work item is one expert x 64 weight rows (gate/up:
 // 32 gate + 32 up rows of the same features), so the same launch spreads over
 // every CU.  4 waves; wave w multiplies 16 weight rows (gate/up: waves 0-1
-// gate, 2-3 up) by the expert's token rows, with fragments loaded straight
-// into registers from a ring of up to 8 K steps.  A gate/up launch with fewer
+// gate, 2-3 up) by the expert's token rows.  Its weight rows arrive as whole
+// 128-byte lines, two K steps per pair of loads, four pairs in flight, and
+// each pair passes through 2 KB of LDS into the fragment layout (against
+// loads of 16 half lines straight into the fragment registers, one K step
+// each: gate/up 0.367 -> 0.344 ms at 16 tokens on the large layer, 0.095 ->
+// 0.085 ms at 7 on the mid layer, bit-identical; eight pairs in flight
+// measured no faster).  The token fragments still come straight from
+// global memory (cache hits).  A gate/up launch with fewer
 // such items than two per CU (one token on the mid layer: 8 experts x 44
 // items) takes items of 16 features instead, one gate and one up wave each:
 // a CU streams about 25 GB/s whatever it runs, so the time is set by the CUs
@@ -448,6 +454,7 @@ constexpr int kS_DownH = 64;           // output rows per down work item (4 wave
 // hold gate rows, the other half up rows of the same features
 constexpr int stream_gate_up_f(int TH) { return TH / kWave / 2 * 16; }
 constexpr int kS_MaxTok = 32;          // invariant path: tokens per call for this kernel
+constexpr int kS_Ring = 4;             // pairs of K steps in flight per wave
 constexpr int kV_MaxTok = 32;          // variant: experts up to this count are split
 
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
@@ -464,7 +471,7 @@ __device__ __forceinline__ int variant_parts(int m, int parts_max) {
     return min(parts_max, m <= 4 ? 4 : 2);
 }
 
-template <int MODE, int NB, int U, bool SPLIT, int kS_Threads>
+template <int MODE, int NB, bool SPLIT, int kS_Threads>
 __global__ __launch_bounds__(kS_Threads) void expert_gemm_stream_kernel(GemmParams P) {
     constexpr int kHalf = kS_Threads / kWave / 2;   // gate/up: gate waves, then as many up waves
     constexpr int kS_GateUpF = stream_gate_up_f(kS_Threads);
@@ -474,6 +481,7 @@ __global__ __launch_bounds__(kS_Threads) void expert_gemm_stream_kernel(GemmPara
     __shared__ int row_start[kS_MaxE + 1];     // SPLIT: first workspace row of an entry
     __shared__ int wsum[3][kS_Threads / kWave];
     __shared__ floatx4 xch[kHalf][NB][kWave];  // up waves' accumulators, for the gate waves
+    __shared__ bf16x8 wscr[kS_Threads / kWave][128];   // a wave's pair of weight steps
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -552,18 +560,32 @@ __global__ __launch_bounds__(kS_Threads) void expert_gemm_stream_kernel(GemmPara
         }
         const int e = act_list[li];
         const int seg0 = P.offsets[e], seg1 = P.offsets[e + 1];
-        const int ks_part = KS / parts;        // a multiple of U (the host's choice)
+        const int ks_part = KS / parts;        // even (the host's choice of parts_max)
         const int s_begin = part * ks_part, s_end = s_begin + ks_part;
 
-        // this wave's weight row
-        const uint16_t* pa;
-        if (MODE == MODE_GATE_UP) {
-            const int f = min(nt * kS_GateUpF + (wave % kHalf) * 16 + (lane & 15), P.N - 1);
-            pa = ((wave < kHalf) ? P.w0 : P.w1) + ((size_t)e * P.N + f) * P.K + koff;
-        } else {
-            const int h = min(nt * kS_DownH + wave * 16 + (lane & 15), P.N - 1);
-            pa = P.w0 + ((size_t)e * P.N + h) * P.K + koff;
+        // this wave's 16 weight rows, read as whole 128-byte lines: a pair of
+        // K steps (64 k) is two loads, lane l taking rows l/8 and 8 + l/8 and
+        // the 16-byte chunk (l%8) ^ (l/8) of each; the pair passes through
+        // LDS (2 KB per wave) into the fragment layout of its two steps
+        const uint16_t* pw[2];
+        {
+            const int r0 = (MODE == MODE_GATE_UP) ? nt * kS_GateUpF + (wave % kHalf) * 16
+                                                  : nt * kS_DownH + wave * 16;
+            const uint16_t* wb = (MODE == MODE_GATE_UP && wave >= kHalf) ? P.w1 : P.w0;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int f = min(r0 + (lane >> 3) + 8 * h, P.N - 1);
+                pw[h] = wb + ((size_t)e * P.N + f) * P.K + ((lane & 7) ^ (lane >> 3)) * 8;
+            }
         }
+        int rd_off[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int r = lane & 15, c = 4 * j + (lane >> 4);
+            rd_off[j] = (r >> 3) * 64 + (r & 7) * 8 + (c ^ (r & 7));
+        }
+        bf16x8* const scr = wscr[wave];
+        const int p_begin = s_begin / 2, p_end = s_end / 2;
 
         for (int tb = seg0; tb < seg1; tb += NB * 16) {
             const uint16_t* pb[NB];
@@ -573,37 +595,54 @@ __global__ __launch_bounds__(kS_Threads) void expert_gemm_stream_kernel(GemmPara
                 const int ar = (MODE == MODE_GATE_UP) ? P.perm[p] / P.top_k : p;
                 pb[nb] = P.act + (size_t)ar * P.K + koff;
             }
-            // a ring of U steps of fragments (U divides the part's steps):
-            // slot u holds step s0 + u; after its MFMAs it is refilled with
-            // step s0 + u + U (the last step again past the end: a cache hit
-            // whose value is unused)
-            bf16x8 ra[U], rb[U][NB];
+            // a ring of kS_Ring pairs: slot u holds pair pp0 + u; after its MFMAs
+            // it is refilled with pair pp0 + u + kS_Ring (the last pair again past
+            // the end: a cache hit whose value is unused)
+            bf16x8 wf[kS_Ring][2], rb[kS_Ring][2][NB];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                ra[u] = *reinterpret_cast<const bf16x8*>(pa + (size_t)(s_begin + u) * 32);
+            for (int u = 0; u < kS_Ring; ++u) {
+                const int pr = min(p_begin + u, p_end - 1);
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb)
-                    rb[u][nb] = *reinterpret_cast<const bf16x8*>(pb[nb] + (size_t)(s_begin + u) * 32);
-                __builtin_amdgcn_sched_barrier(0);   // issue slot by slot, as in the loop
+                for (int h = 0; h < 2; ++h)
+                    wf[u][h] = *reinterpret_cast<const bf16x8*>(pw[h] + (size_t)pr * 64);
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+                        rb[u][j][nb] =
+                            *reinterpret_cast<const bf16x8*>(pb[nb] + (size_t)(2 * pr + j) * 32);
+                __builtin_amdgcn_sched_barrier(0);
             }
             floatx4 acc[NB];
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) acc[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
-            for (int s0 = s_begin; s0 < s_end; s0 += U) {
+            for (int pp0 = p_begin; pp0 < p_end; pp0 += kS_Ring) {
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
+                for (int u = 0; u < kS_Ring; ++u) {
+                    if (pp0 + u < p_end) {
+                        scr[lane] = wf[u][0];
+                        scr[64 + lane] = wf[u][1];
+                        const bf16x8 a0 = scr[rd_off[0]];
+                        const bf16x8 a1 = scr[rd_off[1]];
 #pragma unroll
-                    for (int nb = 0; nb < NB; ++nb)
-                        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra[u], rb[u][nb],
-                                                                           acc[nb], 0, 0, 0);
-                    const int sn = min(s0 + u + U, s_end - 1);
-                    ra[u] = *reinterpret_cast<const bf16x8*>(pa + (size_t)sn * 32);
+                        for (int nb = 0; nb < NB; ++nb)
+                            acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, rb[u][0][nb],
+                                                                               acc[nb], 0, 0, 0);
 #pragma unroll
-                    for (int nb = 0; nb < NB; ++nb)
-                        rb[u][nb] = *reinterpret_cast<const bf16x8*>(pb[nb] + (size_t)sn * 32);
-                    // keep each slot's refill right after its MFMAs, so that
-                    // U - 1 steps stay in flight (the scheduler would otherwise
-                    // group every refill after every MFMA of the ring)
+                        for (int nb = 0; nb < NB; ++nb)
+                            acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, rb[u][1][nb],
+                                                                               acc[nb], 0, 0, 0);
+                    }
+                    const int pn = min(pp0 + u + kS_Ring, p_end - 1);
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+                        wf[u][h] = *reinterpret_cast<const bf16x8*>(pw[h] + (size_t)pn * 64);
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb)
+                            rb[u][j][nb] = *reinterpret_cast<const bf16x8*>(
+                                pb[nb] + (size_t)(2 * pn + j) * 32);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
@@ -700,28 +739,18 @@ __global__ __launch_bounds__(256) void variant_reduce_kernel(GemmParams P) {
     }
 }
 
-template <int MODE, bool SPLIT, int NB, int TH>
-hipError_t launch_stream_nb(const GemmParams& P, int U, int grid, hipStream_t s) {
-    if (U == 8) expert_gemm_stream_kernel<MODE, NB, 8, SPLIT, TH><<<grid, TH, 0, s>>>(P);
-    else if (U == 4) expert_gemm_stream_kernel<MODE, NB, 4, SPLIT, TH><<<grid, TH, 0, s>>>(P);
-    else expert_gemm_stream_kernel<MODE, NB, 2, SPLIT, TH><<<grid, TH, 0, s>>>(P);
-    return hipGetLastError();
-}
 
 template <int MODE, bool SPLIT, int TH>
 hipError_t launch_stream_th(GemmParams P, int T, int max_rows, hipStream_t s) {
     P.n_tiles = (MODE == MODE_GATE_UP) ? P.N / stream_gate_up_f(TH) : P.N / kS_DownH;
-    // ring depth: the largest of 8, 4, 2 dividing the K steps of the
-    // shortest part (K is a multiple of 64, so K / 32 is even; the host's
-    // parts_max keeps K / 32 / parts_max even).  (A ring of 16 measured no
-    // faster at decode sizes.)
-    const int ks = P.K / 32 / (SPLIT ? P.parts_max : 1);
-    const int U = (ks % 8 == 0) ? 8 : (ks % 4 == 0 ? 4 : 2);
     // at most min(E, T*k) experts are active: no more work items than that
     const long items = (long)std::min(P.E, T * P.top_k) * P.n_tiles * (SPLIT ? P.parts_max : 1);
     const int grid = (int)std::max(1L, std::min(items, (long)device_cu_count() * 8));
-    if (max_rows <= 16) return launch_stream_nb<MODE, SPLIT, 1, TH>(P, U, grid, s);
-    return launch_stream_nb<MODE, SPLIT, 2, TH>(P, U, grid, s);
+    if (max_rows <= 16)
+        expert_gemm_stream_kernel<MODE, 1, SPLIT, TH><<<grid, TH, 0, s>>>(P);
+    else
+        expert_gemm_stream_kernel<MODE, 2, SPLIT, TH><<<grid, TH, 0, s>>>(P);
+    return hipGetLastError();
 }
 
 // max_rows: the most token rows an expert served by this launch can have
