@@ -393,7 +393,9 @@ int moe_quantize_fp8(int R, int K, int block_rows, const uint16_t* src, uint8_t*
  *   act_q [device] out [T*k,F] codes and act_e [device] out [T*k,F/128]
  *   exps of act = bf16(silu(g)*u), rows in permuted order;
  *   act_bf16 [device] out [T*k,F] bf16 or NULL: act itself.
- *   ws: moe_workspace_bytes(MOE_OP_GATE_UP_FP8, ...). */
+ *   ws: moe_workspace_bytes(MOE_OP_GATE_UP_FP8, ...); a call of at most 32
+ *   tokens streams the weights (same bits) and keeps act there when
+ *   act_bf16 is NULL.  Rows outside every expert segment are not written. */
 int moe_expert_gate_up_fp8(int T, int H, int E, int F, int top_k, const uint8_t* xq,
                            const int8_t* xe, const int32_t* perm, const int32_t* expert_offsets,
                            const uint8_t* wg_q, const int8_t* wg_e, const uint8_t* wu_q,

@@ -5,6 +5,7 @@
 // and the device address of it that is looked up once per GPU.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "../../include/moe.h"
@@ -21,6 +22,18 @@ hipError_t launch_route_permute(int T, int H, int E, int k, int score, int renor
                                 int32_t* ids, float* w, float* part_ws, int32_t* counts,
                                 int32_t* offsets, int32_t* perm, int32_t* inv_perm,
                                 int32_t* permute_ws, hipStream_t s);
+// FP8 expert GEMMs of calls of at most kFp8StreamMaxTok tokens: the
+// weight-streaming forms (same bits as the tiled kernel).  gate/up writes the
+// bf16 act to act16 ([T*k, F]) and quantises it from there.
+constexpr int kFp8StreamMaxTok = 32;
+hipError_t launch_gate_up_fp8_stream(int T, int H, int E, int F, int k, const uint8_t* xq,
+                                     const int8_t* xe, const int32_t* perm,
+                                     const int32_t* offsets, const uint8_t* wgq,
+                                     const int8_t* wge, const uint8_t* wuq, const int8_t* wue,
+                                     uint8_t* aq, int8_t* ae, uint16_t* act16, hipStream_t s);
+hipError_t launch_down_fp8_stream(int T, int H, int E, int F, int k, const uint8_t* aq,
+                                  const int8_t* ae, const int32_t* perm, const int32_t* offsets,
+                                  const uint8_t* wdq, const int8_t* wde, float* y, hipStream_t s);
 }  // namespace moe
 
 namespace {
@@ -106,10 +119,18 @@ int check_layer_fp8(int T, int H, int E, int F, int top_k) {
     return 0;
 }
 
+// gate/up FP8 workspace: the tile schedule, or for a weight-streaming call
+// the bf16 act it quantises from (used when the caller passes no act_bf16).
+size_t gate_up_fp8_ws(int T, int E, int F, int top_k) {
+    const size_t sched = moe::gemm_sched_ws_bytes(E);
+    if (T > moe::kFp8StreamMaxTok) return sched;
+    return std::max(sched, up((size_t)T * top_k * F * 2));
+}
+
 // Workspace layout of moe_forward_fp8.
 struct Fwd8Layout {
     size_t ids, w, counts, offsets, perm, inv_perm, route, permute, sched, xq, xe, aq, ae, y,
-        total;
+        abf, total;
 };
 
 Fwd8Layout fwd8_layout(int T, int H, int E, int F, int top_k) {
@@ -130,6 +151,7 @@ Fwd8Layout fwd8_layout(int T, int H, int E, int F, int top_k) {
     L.aq = o; o += up(A * (size_t)F);
     L.ae = o; o += up(A * (size_t)(F / moe::kFp8Block));
     L.y = o; o += up(A * (size_t)H * 4);
+    L.abf = o; o += T <= moe::kFp8StreamMaxTok ? up(A * (size_t)F * 2) : 0;
     L.total = o;
     return L;
 }
@@ -287,6 +309,8 @@ size_t moe_workspace_bytes(int op, int T, int H, int E, int F, int top_k, int va
             if (check_layer(T, H, E, F, top_k)) return 0;
             return fwd_layout(T, H, E, F, top_k, variant).total;
         case MOE_OP_GATE_UP_FP8:
+            if (variant != MOE_GEMM_INVARIANT || check_layer_fp8(T, H, E, F, top_k)) return 0;
+            return gate_up_fp8_ws(T, E, F, top_k);
         case MOE_OP_DOWN_FP8:
             if (variant != MOE_GEMM_INVARIANT || check_layer_fp8(T, H, E, F, top_k)) return 0;
             return moe::gemm_sched_ws_bytes(E);
@@ -567,7 +591,11 @@ int moe_expert_gate_up_fp8(int T, int H, int E, int F, int top_k, const uint8_t*
         !aligned16(act_q) || !aligned16(act_e) || !aligned16(ws) ||
         (act_bf16 && !aligned16(act_bf16)))
         return MOE_ERR_ALIGN;
-    if (ws_bytes < moe::gemm_sched_ws_bytes(E)) return MOE_ERR_WORKSPACE;
+    if (ws_bytes < gate_up_fp8_ws(T, E, F, top_k)) return MOE_ERR_WORKSPACE;
+    if (T <= moe::kFp8StreamMaxTok)
+        return hip_rc(moe::launch_gate_up_fp8_stream(
+            T, H, E, F, top_k, xq, xe, perm, expert_offsets, wg_q, wg_e, wu_q, wu_e, act_q, act_e,
+            act_bf16 ? act_bf16 : static_cast<uint16_t*>(ws), S(stream)));
     return hip_rc(moe::launch_gate_up_fp8(T, H, E, F, top_k, xq, xe, perm, expert_offsets, wg_q,
                                           wg_e, wu_q, wu_e, act_q, act_e, act_bf16,
                                           static_cast<int32_t*>(ws), S(stream)));
@@ -586,6 +614,9 @@ int moe_expert_down_fp8(int T, int H, int E, int F, int top_k, const uint8_t* ac
         !aligned16(ws))
         return MOE_ERR_ALIGN;
     if (ws_bytes < moe::gemm_sched_ws_bytes(E)) return MOE_ERR_WORKSPACE;
+    if (T <= moe::kFp8StreamMaxTok)
+        return hip_rc(moe::launch_down_fp8_stream(T, H, E, F, top_k, act_q, act_e, perm,
+                                                  expert_offsets, wd_q, wd_e, y, S(stream)));
     return hip_rc(moe::launch_down_fp8(T, H, E, F, top_k, act_q, act_e, perm, expert_offsets,
                                        wd_q, wd_e, y, static_cast<int32_t*>(ws), S(stream)));
 }
@@ -628,10 +659,18 @@ int moe_forward_fp8(int T, int H, int E, int F, int top_k, int score, int renorm
                                              bias, ids, w, part, counts, offsets, perm, inv, pws,
                                              s)));
     MOE_TRY(hip_rc(moe::launch_quantize_fp8(T, H, 1, x, xq, xe, s)));
-    MOE_TRY(hip_rc(moe::launch_gate_up_fp8(T, H, E, F, top_k, xq, xe, perm, offsets, wg_q, wg_e,
-                                           wu_q, wu_e, aq, ae, nullptr, sched, s)));
-    MOE_TRY(hip_rc(moe::launch_down_fp8(T, H, E, F, top_k, aq, ae, perm, offsets, wd_q, wd_e, y,
-                                        sched, s)));
+    if (T <= moe::kFp8StreamMaxTok) {
+        uint16_t* abf = reinterpret_cast<uint16_t*>(at(ws, L.abf));
+        MOE_TRY(hip_rc(moe::launch_gate_up_fp8_stream(T, H, E, F, top_k, xq, xe, perm, offsets,
+                                                      wg_q, wg_e, wu_q, wu_e, aq, ae, abf, s)));
+        MOE_TRY(hip_rc(moe::launch_down_fp8_stream(T, H, E, F, top_k, aq, ae, perm, offsets,
+                                                   wd_q, wd_e, y, s)));
+    } else {
+        MOE_TRY(hip_rc(moe::launch_gate_up_fp8(T, H, E, F, top_k, xq, xe, perm, offsets, wg_q,
+                                               wg_e, wu_q, wu_e, aq, ae, nullptr, sched, s)));
+        MOE_TRY(hip_rc(moe::launch_down_fp8(T, H, E, F, top_k, aq, ae, perm, offsets, wd_q,
+                                            wd_e, y, sched, s)));
+    }
     return hip_rc(launch_combine(T, H, top_k, y, w, out, s));
 }
 

@@ -29,6 +29,8 @@
 // rows x 256 token rows), one instruction, K blocks in ascending order, no
 // split, whatever the expert's token count; padding rows only feed dropped
 // results.
+#include <algorithm>
+
 #include "moe_device.h"
 #include "moe_gemm_tiles.h"
 #include "moe_internal.h"
@@ -93,16 +95,21 @@ __device__ __forceinline__ float absmax8(uint4 v) {
 // one pass for the block maximum, one for the codes (exact scaling by 2^-e,
 // then the hardware conversion).
 // ---------------------------------------------------------------------------
+// (rows != null: only the rows in [rows[0], rows[nseg]), bounds the device
+// holds, e.g. the expert offsets of a permuted matrix.)
 __global__ __launch_bounds__(256) void quantize_fp8_kernel(int R, int K, int block_rows,
                                                            const uint16_t* __restrict__ src,
                                                            uint8_t* __restrict__ q,
-                                                           int8_t* __restrict__ exps) {
+                                                           int8_t* __restrict__ exps,
+                                                           const int32_t* __restrict__ rows,
+                                                           int nseg) {
     const int nkb = K / kFp8Block;
     const long units = (long)(R / block_rows) * nkb;
     const long unit = (long)blockIdx.x * 16 + (threadIdx.x >> 4);
     if (unit >= units) return;   // a 16-lane group leaves as a whole
     const int li = threadIdx.x & 15;
     const int rb = (int)(unit / nkb), kb = (int)(unit % nkb);
+    if (rows && (rb * block_rows < rows[0] || rb * block_rows >= rows[nseg])) return;
     const size_t col = (size_t)kb * kFp8Block + li * 8;
     const int r0 = rb * block_rows, r1 = r0 + block_rows;
     float amax = 0.0f;
@@ -459,6 +466,195 @@ __global__ __launch_bounds__(kQ_Threads) void expert_gemm_fp8_kernel(Fp8Params P
         expert_gemm_fp8_body<MODE, false>(P, smem, s_tsc, s_wsc, s_amax);
 }
 
+// ---------------------------------------------------------------------------
+// Weight-streaming FP8 GEMMs, for calls of at most 32 tokens.  Such a call
+// only streams the active experts' weights, and the 256-row tiles above would
+// leave most CUs idle (8 active experts x F/128 tiles).  A work item is one
+// active expert x 64 weight rows (gate/up: 32 gate + 32 up rows of the same
+// features; down: 64 output rows); each of the block's 4 waves multiplies 16
+// weight rows by the expert's token rows (16 or 32 at a time).  A wave's
+// weight rows arrive as whole 128-byte lines, one K block (128 codes a row)
+// per pair of loads (lane l: rows l/8 and 8 + l/8, chunk (l%8) ^ (l/8)), four
+// K blocks in flight, and pass through 2 KB of the wave's own LDS into the
+// fragment layout (one wave's LDS operations run in order: no barrier).  The
+// token fragments and both exponents come straight from global memory.
+//
+// The MFMA sequence of an output element is the tiled kernel's: one
+// v_mfma_scale_f32_16x16x128_f8f6f4 per K block, K blocks ascending, lane l
+// holding row l%16 and chunks l/16 and 4 + l/16 of the block on both sides,
+// with the same scale bytes, accumulators from 0.  So the bits are equal.
+// gate/up writes act = bf16(silu(g) * u) and leaves its quantisation to the
+// block quantiser (the same exponent and codes the tiled epilogue computes
+// from the same bf16 values), since a 128-feature scale block spans four
+// work items.
+// ---------------------------------------------------------------------------
+constexpr int kQS_MaxE = 512;
+constexpr int kQS_Ring = 4;            // K blocks in flight per wave
+constexpr int kQS_GateUpF = 32;        // gate/up features per work item
+constexpr int kQS_DownH = 64;          // down output rows per work item
+
+template <int MODE, int NB>
+__global__ __launch_bounds__(256) void expert_gemm_fp8_stream_kernel(Fp8Params P,
+                                                                     uint16_t* act16) {
+    __shared__ int act_list[kQS_MaxE];
+    __shared__ int4v wscr[4][128];                  // a wave's K block of weight rows
+    __shared__ floatx4 xch[2][NB][kWave];           // up waves' sums, for the gate waves
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int E = P.E;
+    const int nkb = P.K / kFp8Block;
+    const int nwb = P.N / kFp8Block;
+
+    // the active experts, ascending (wave 0 builds the list; counts <= 32)
+    __shared__ int s_nact;
+    if (wave == 0) {
+        int n = 0;
+        for (int e0 = 0; e0 < E; e0 += kWave) {
+            const int e = e0 + lane;
+            const bool a = e < E && P.offsets[e + 1] > P.offsets[e];
+            const uint64_t m = __ballot(a);
+            if (a) act_list[n + __popcll(m & ((1ull << lane) - 1))] = e;
+            n += __popcll(m);
+        }
+        if (lane == 0) s_nact = n;
+    }
+    __syncthreads();
+    const int n_act = s_nact;
+    const int total = n_act * P.n_tiles;
+
+    const int r = lane & 15, rr = r & 7;
+    const int rd0 = (r >> 3) * 64 + rr * 8 + ((lane >> 4) ^ rr);         // int4v units
+    const int rd1 = (r >> 3) * 64 + rr * 8 + ((4 + (lane >> 4)) ^ rr);
+    int4v* const scr = wscr[wave];
+    const int colq = 4 * (lane >> 4);
+
+    for (int item = blockIdx.x; item < total; item += gridDim.x) {
+        const int li = item / P.n_tiles;
+        const int nt = item - li * P.n_tiles;
+        const int e = act_list[li];
+        const int seg0 = P.offsets[e], seg1 = P.offsets[e + 1];
+
+        // this wave's 16 weight rows and their exponent row
+        const int r0 = (MODE == MODE_GATE_UP) ? nt * kQS_GateUpF + (wave & 1) * 16
+                                              : nt * kQS_DownH + wave * 16;
+        const uint8_t* wb = (MODE == MODE_GATE_UP && wave >= 2) ? P.w1 : P.w0;
+        const int8_t* web = (MODE == MODE_GATE_UP && wave >= 2) ? P.we1 : P.we0;
+        const uint8_t* pw[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            pw[h] = wb + ((size_t)e * P.N + r0 + (lane >> 3) + 8 * h) * P.K +
+                    ((lane & 7) ^ (lane >> 3)) * 16;
+        const int8_t* pwe = web + ((size_t)e * nwb + r0 / kFp8Block) * nkb;
+
+        for (int tb = seg0; tb < seg1; tb += NB * 16) {
+            const uint8_t* pt[NB];
+            const int8_t* pte[NB];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const int p = min(tb + nb * 16 + (lane & 15), seg1 - 1);
+                const int ar = (MODE == MODE_GATE_UP) ? P.perm[p] / P.top_k : p;
+                pt[nb] = P.act + (size_t)ar * P.K + (lane >> 4) * 16;
+                pte[nb] = P.act_e + (size_t)ar * nkb;
+            }
+            // a ring of kQS_Ring K blocks: slot u holds block kb0 + u and is
+            // refilled with block kb0 + u + kQS_Ring after its MFMAs (the last
+            // block again past the end: cache hits whose values are unused)
+            int4v wf[kQS_Ring][2], tf[kQS_Ring][NB][2];
+            int wsc[kQS_Ring], tsc[kQS_Ring][NB];
+            auto load = [&](int u, int kb) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    wf[u][h] = *reinterpret_cast<const int4v*>(pw[h] + (size_t)kb * kFp8Block);
+                wsc[u] = 127 + pwe[kb];
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    tf[u][nb][0] = *reinterpret_cast<const int4v*>(pt[nb] + (size_t)kb * kFp8Block);
+                    tf[u][nb][1] =
+                        *reinterpret_cast<const int4v*>(pt[nb] + (size_t)kb * kFp8Block + 64);
+                    tsc[u][nb] = 127 + pte[nb][kb];
+                }
+            };
+#pragma unroll
+            for (int u = 0; u < kQS_Ring; ++u) {
+                load(u, min(u, nkb - 1));
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            floatx4 acc[NB];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) acc[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+            for (int kb0 = 0; kb0 < nkb; kb0 += kQS_Ring) {
+#pragma unroll
+                for (int u = 0; u < kQS_Ring; ++u) {
+                    if (kb0 + u < nkb) {
+                        scr[lane] = wf[u][0];
+                        scr[64 + lane] = wf[u][1];
+                        const int8v fa = __builtin_shufflevector(scr[rd0], scr[rd1], 0, 1, 2, 3,
+                                                                 4, 5, 6, 7);
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb) {
+                            const int8v fb = __builtin_shufflevector(tf[u][nb][0], tf[u][nb][1],
+                                                                     0, 1, 2, 3, 4, 5, 6, 7);
+                            acc[nb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                fa, fb, acc[nb], 0, 0, 0, wsc[u], 0, tsc[u][nb]);
+                        }
+                    }
+                    load(u, min(kb0 + u + kQS_Ring, nkb - 1));
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+
+            // epilogue: lane holds weight rows r0 + colq + q of token column lane&15
+            if (MODE == MODE_GATE_UP) {
+                if (wave >= 2) {
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) xch[wave - 2][nb][lane] = acc[nb];
+                }
+                __syncthreads();
+                if (wave < 2) {
+                    const int f = r0 + colq;
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+                        const int p = tb + nb * 16 + (lane & 15);
+                        if (p >= seg1) continue;
+                        const floatx4 up = xch[wave][nb][lane];
+                        uint32_t h[4];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            h[q] = f32_to_bf16_rne(silu_f(acc[nb][q]) * up[q]);
+                        uint2 pk;
+                        pk.x = h[0] | (h[1] << 16);
+                        pk.y = h[2] | (h[3] << 16);
+                        *reinterpret_cast<uint2*>(act16 + (size_t)p * P.N + f) = pk;
+                    }
+                }
+                __syncthreads();
+            } else {
+                const int hrow = r0 + colq;
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    const int p = tb + nb * 16 + (lane & 15);
+                    if (p >= seg1) continue;
+                    *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(P.out) +
+                                                (size_t)P.perm[p] * P.N + hrow) = acc[nb];
+                }
+            }
+        }
+    }
+}
+
+template <int MODE>
+hipError_t launch_fp8_stream(const Fp8Params& P, int T, uint16_t* act16, hipStream_t s) {
+    // at most min(E, T*k) experts are active: no more work items than that
+    const long items = (long)std::min(P.E, T * P.top_k) * P.n_tiles;
+    const int grid = (int)std::max(1L, std::min(items, (long)device_cu_count() * 8));
+    if (T <= 16)
+        expert_gemm_fp8_stream_kernel<MODE, 1><<<grid, 256, 0, s>>>(P, act16);
+    else
+        expert_gemm_fp8_stream_kernel<MODE, 2><<<grid, 256, 0, s>>>(P, act16);
+    return hipGetLastError();
+}
+
 template <int MODE>
 hipError_t launch_fp8_gemm(const Fp8Params& P, hipStream_t s) {
     const int cu = device_cu_count();
@@ -474,7 +670,7 @@ hipError_t launch_quantize_fp8(int R, int K, int block_rows, const uint16_t* src
     const long units = (long)(R / block_rows) * (K / kFp8Block);
     if (units == 0) return hipSuccess;
     const long blocks = (units + 15) / 16;
-    quantize_fp8_kernel<<<(unsigned)blocks, 256, 0, s>>>(R, K, block_rows, src, q, exps);
+    quantize_fp8_kernel<<<(unsigned)blocks, 256, 0, s>>>(R, K, block_rows, src, q, exps, nullptr, 0);
     return hipGetLastError();
 }
 
@@ -509,6 +705,40 @@ hipError_t launch_down_fp8(int T, int H, int E, int F, int k, const uint8_t* aq,
     P.w0 = wdq; P.we0 = wde; P.w1 = nullptr; P.we1 = nullptr;
     P.out = y; P.out_e = nullptr; P.out_bf16 = nullptr;
     return launch_fp8_gemm<MODE_DOWN>(P, s);
+}
+
+// The weight-streaming forms (calls of at most kFp8StreamMaxTok tokens; the
+// caller checks).  gate/up writes the bf16 act to act16 ([A, F], permuted
+// rows) and quantises the placed rows from it.
+hipError_t launch_gate_up_fp8_stream(int T, int H, int E, int F, int k, const uint8_t* xq,
+                                     const int8_t* xe, const int32_t* perm,
+                                     const int32_t* offsets, const uint8_t* wgq,
+                                     const int8_t* wge, const uint8_t* wuq, const int8_t* wue,
+                                     uint8_t* aq, int8_t* ae, uint16_t* act16, hipStream_t s) {
+    Fp8Params P;
+    P.K = H; P.N = F; P.n_tiles = F / kQS_GateUpF; P.top_k = k; P.E = E;
+    P.act = xq; P.act_e = xe; P.perm = perm; P.offsets = offsets;
+    P.tile_start = nullptr; P.tail = nullptr;
+    P.w0 = wgq; P.we0 = wge; P.w1 = wuq; P.we1 = wue;
+    P.out = nullptr; P.out_e = nullptr; P.out_bf16 = nullptr;
+    hipError_t err = launch_fp8_stream<MODE_GATE_UP>(P, T, act16, s);
+    if (err != hipSuccess) return err;
+    const int A = T * k;
+    const long blocks = ((long)A * (F / kFp8Block) + 15) / 16;
+    quantize_fp8_kernel<<<(unsigned)blocks, 256, 0, s>>>(A, F, 1, act16, aq, ae, offsets, E);
+    return hipGetLastError();
+}
+
+hipError_t launch_down_fp8_stream(int T, int H, int E, int F, int k, const uint8_t* aq,
+                                  const int8_t* ae, const int32_t* perm, const int32_t* offsets,
+                                  const uint8_t* wdq, const int8_t* wde, float* y, hipStream_t s) {
+    Fp8Params P;
+    P.K = F; P.N = H; P.n_tiles = H / kQS_DownH; P.top_k = k; P.E = E;
+    P.act = aq; P.act_e = ae; P.perm = perm; P.offsets = offsets;
+    P.tile_start = nullptr; P.tail = nullptr;
+    P.w0 = wdq; P.we0 = wde; P.w1 = nullptr; P.we1 = nullptr;
+    P.out = y; P.out_e = nullptr; P.out_bf16 = nullptr;
+    return launch_fp8_stream<MODE_DOWN>(P, T, nullptr, s);
 }
 
 }  // namespace moe

@@ -392,6 +392,46 @@ def test_fp8_weight_streaming_launch_matches_full_launch():
         f"the same rows of a 4000-token launch (max {c2.max()})")
 
 
+def _fp8_gemms(cfg, L, wqd, x, want_bf16=True):
+    """routing, x codes and both FP8 GEMMs; act codes, exponents and bf16 act
+    returned in assignment order, with y (already in assignment order)."""
+    ids, _ = M.route(x, L["w_router"], cfg.k, cfg.score, cfg.renorm, bias=L["bias"])
+    counts, offsets, perm, inv = M.permute(ids, cfg.E)
+    xq, xe = M.quantize_fp8(x, 1)
+    aq, ae, ab = M.expert_gate_up_fp8(xq, xe, perm, offsets, wqd["wg_q"], wqd["wg_e"],
+                                      wqd["wu_q"], wqd["wu_e"], cfg.k, want_bf16=want_bf16)
+    y = M.expert_down_fp8(aq, ae, perm, offsets, wqd["wd_q"], wqd["wd_e"], cfg.k)
+    inv_np = _np(inv)
+    return (_np(aq)[inv_np], _np(ae)[inv_np],
+            bits(ab)[inv_np] if ab is not None else None, _np(y).view(np.uint32))
+
+
+@pytest.mark.parametrize("n", [1, 5, 16, 17, 32])
+def test_fp8_streaming_gemms_equal_tiled(n):
+    """Calls of at most 32 tokens take the weight-streaming FP8 GEMMs (weight
+    rows as whole lines through LDS, act quantised by the block quantiser).
+    The first n tokens alone and inside a 600-token call (the tiled kernel)
+    give bit-identical act codes, exponents, bf16 act, y and layer output; the
+    streaming gate/up without an act_bf16 output gives the same codes."""
+    cfg = I.scaled(I.CONFIGS["mid"], T=600)
+    L = layer(cfg)
+    wqd = M.quantize_weights_fp8(L["w_gate"], L["w_up"], L["w_down"])
+    x = I.make_tokens(600, cfg.H, 5151, "cpu").to(DEV)
+    small = _fp8_gemms(cfg, L, wqd, x[:n].contiguous())
+    big = _fp8_gemms(cfg, L, wqd, x)
+    A = n * cfg.k
+    for name, s, g in zip(("act codes", "act exps", "act bf16", "y"), small, big):
+        assert np.array_equal(s, g[:A]), (n, name)
+    nobf = _fp8_gemms(cfg, L, wqd, x[:n].contiguous(), want_bf16=False)
+    assert np.array_equal(nobf[0], small[0]) and np.array_equal(nobf[1], small[1])
+    assert np.array_equal(nobf[3], small[3])
+    o1 = bits(_fwd8(cfg, L, wqd, x[:n].contiguous()))
+    o2 = bits(_fwd8(cfg, L, wqd, x))
+    assert np.array_equal(o1, o2[:n])
+    log(f"[fp8] {n} tokens: weight-streaming GEMMs == the tiled kernel's rows of a 600-token "
+        f"call (act codes, exps, bf16, y, out)")
+
+
 def test_large_fp8_sampled():
     """The large layer at T = 16384 in the launch configuration the benchmark
     times: the GPU's weight codes of sampled experts bit-exact, and act and y of
