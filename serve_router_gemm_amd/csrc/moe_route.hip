@@ -668,11 +668,18 @@ __global__ __launch_bounds__(256) void router_select_kernel(
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     // (with kPermute the block is one wave per token: none leaves here)
     if (t >= T) return;  // whole wave leaves together
+    // the experts of this lane: with 4 a lane, 4 consecutive ones (one
+    // 16-byte load per plane: decode route 0.0149 -> 0.0139 ms on the large
+    // layer, same bits); else lane, lane + 64, ...  (Which lane holds an
+    // expert changes only the softmax denominator's summation order, the
+    // same at every batch size.)
+    constexpr bool kVec = kSelMaxQ == 4;
+    auto eof = [&](int q) { return kVec ? lane * kSelMaxQ + q : lane + 64 * q; };
 
     float bz[kSelMaxQ];
 #pragma unroll
     for (int q = 0; q < kSelMaxQ; ++q) {
-        const int e = lane + 64 * q;
+        const int e = eof(q);
         bz[q] = (score != 0 && bias && e < E) ? bias[e] : 0.0f;
     }
     float lg[kSelMaxQ];
@@ -682,14 +689,28 @@ __global__ __launch_bounds__(256) void router_select_kernel(
     for (int q = 0; q < kSelMaxQ; ++q) lg[q] = 0.0f;
     for (int c0 = 0; c0 < nparts; c0 += kSelBatch) {
         float pv[kSelBatch][kSelMaxQ];
+        if (kVec && (E & 3) == 0) {
 #pragma unroll
-        for (int u = 0; u < kSelBatch; ++u)
-#pragma unroll
-            for (int q = 0; q < kSelMaxQ; ++q) {
-                const int e = lane + 64 * q;
-                pv[u][q] = (e < E && c0 + u < nparts)
-                               ? part[((size_t)(c0 + u) * T + t) * E + e] : 0.0f;
+            for (int u = 0; u < kSelBatch; ++u) {
+                float4 f4 = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (4 * lane < E && c0 + u < nparts)
+                    f4 = *reinterpret_cast<const float4*>(
+                        part + ((size_t)(c0 + u) * T + t) * E + 4 * lane);
+                pv[u][0] = f4.x;
+                pv[u][1 % kSelMaxQ] = f4.y;
+                pv[u][2 % kSelMaxQ] = f4.z;
+                pv[u][3 % kSelMaxQ] = f4.w;
             }
+        } else {
+#pragma unroll
+            for (int u = 0; u < kSelBatch; ++u)
+#pragma unroll
+                for (int q = 0; q < kSelMaxQ; ++q) {
+                    const int e = eof(q);
+                    pv[u][q] = (e < E && c0 + u < nparts)
+                                   ? part[((size_t)(c0 + u) * T + t) * E + e] : 0.0f;
+                }
+        }
 #pragma unroll
         for (int u = 0; u < kSelBatch; ++u)
 #pragma unroll
@@ -698,7 +719,7 @@ __global__ __launch_bounds__(256) void router_select_kernel(
     }
 #pragma unroll
     for (int q = 0; q < kSelMaxQ; ++q) {
-        const int e = lane + 64 * q;
+        const int e = eof(q);
         rk[q] = 0;
         if (e < E) {
             const float v = lg[q];
@@ -715,7 +736,7 @@ __global__ __launch_bounds__(256) void router_select_kernel(
 
     // the logit of expert e (uniform), read from its owner lane
     auto logit_of = [&](int e) -> float {
-        const int qs = e >> 6, owner = e & 63;
+        const int qs = kVec ? e % kSelMaxQ : e >> 6, owner = kVec ? e / kSelMaxQ : e & 63;
         float v = 0.0f;
 #pragma unroll
         for (int q = 0; q < kSelMaxQ; ++q)
@@ -740,7 +761,7 @@ __global__ __launch_bounds__(256) void router_select_kernel(
             for (int q = 1; q < kSelMaxQ; ++q) best = rk[q] > best ? rk[q] : best;
             best = wave_max_u64(best);
             e = (int)(~(uint32_t)best);
-            const int qs = e >> 6, owner = e & 63;
+            const int qs = kVec ? e % kSelMaxQ : e >> 6, owner = kVec ? e / kSelMaxQ : e & 63;
 #pragma unroll
             for (int q = 0; q < kSelMaxQ; ++q)
                 if (q == qs && lane == owner) rk[q] = 0;  // taken
@@ -757,13 +778,13 @@ __global__ __launch_bounds__(256) void router_select_kernel(
         float m = -INFINITY;
 #pragma unroll
         for (int q = 0; q < kSelMaxQ; ++q)
-            if (lane + 64 * q < E) m = fmaxf(m, lg[q]);
+            if (eof(q) < E) m = fmaxf(m, lg[q]);
 #pragma unroll
         for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, 64));
         float S = 0.0f;
 #pragma unroll
         for (int q = 0; q < kSelMaxQ; ++q)
-            if (lane + 64 * q < E) S = S + expf(lg[q] - m);
+            if (eof(q) < E) S = S + expf(lg[q] - m);
         // (the butterfly gives every lane the same sum: each step adds the
         // same two values on both lanes of a pair)
 #pragma unroll
