@@ -18,7 +18,7 @@ struct RoutePlan {
     int split;     // 0: logits kernel folds every chunk; 1: one block per chunk
     int nparts;    // partial-logit planes the select kernel folds
     int tt, te;    // token / expert register tile of the VALU logits kernel
-    int mfma;      // 1: the matrix-core logits kernel, its 4 waves wt x we
+    int mfma;      // 1: the matrix-core logits kernel, its waves wt x we (4 or 8)
     int wt, we;
 };
 RoutePlan route_plan(int T, int H, int E);
