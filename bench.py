@@ -530,8 +530,10 @@ def main():
             del lp8
         decode_res = {"vocab": V, "lm_head_ms": round(dms[0], 4),
                       "lm_head_hbm_frac": round(proj_bytes / (dms[0] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                      "lm_head_kernel": ("mfma_f32 32x32x1" if T > 8 else "valu fma, one row per thread"
-                                         if T > 2 else "valu fma, whole-line loads through LDS"),
+                      "lm_head_kernel": ("valu fma, one row per thread" if 4 < T <= 8 else
+                                         "valu fma, whole-line loads through LDS"
+                                         if T <= 4 or (T <= 16 and V >= 16384)
+                                         else "mfma_f32 32x32x1"),
                       "lm_head_fp32_tflops": round(2.0 * T * V * H / (dms[0] * 1e-3) / 1e12, 2),
                       "log_softmax_ms": round(dms[1], 4),
                       "log_softmax_hbm_frac": round(8.0 * T * V / (dms[1] * 1e-3) / 1e9

@@ -102,11 +102,13 @@ def test_matrix_core_logits_bit_exact_at_layer_shapes():
 def test_matrix_core_logits_ragged_shapes():
     """Partial token and expert blocks and a last chunk narrower than 256
     (H = 2112 ends in a 64-wide chunk), against the oracle bit for bit; the
-    one- and two-token shapes run the VALU kernel that loads whole lines
-    (partial 64-row groups of the vocabulary, V below one wave's rows)."""
+    one- to four-token shapes and 9-16 tokens over at least 16384 rows run the
+    VALU kernels that load whole lines (partial 64-row groups of the
+    vocabulary, V below one wave's rows, a last span shorter than 512)."""
     g = torch.Generator().manual_seed(21)
     for T, H, V in ((37, 2112, 200), (70, 320, 129), (9, 64, 1), (1, 2112, 200), (2, 320, 129),
-                    (1, 64, 1), (2, 6144, 1000), (4, 2112, 300)):
+                    (1, 64, 1), (2, 6144, 1000), (4, 2112, 300), (3, 576, 77),
+                    (12, 320, 16500), (16, 2112, 16384)):
         h = torch.randn((T, H), generator=g).to(torch.bfloat16)
         p = (torch.randn((V, H), generator=g) * 0.05).to(torch.bfloat16)
         z = M.lm_head_logits(h.to(DEV), p.to(DEV)).cpu().numpy()
