@@ -455,7 +455,7 @@ hipError_t launch_logits_few(int T, int H, int E, const uint16_t* x, const uint1
     return hipGetLastError();
 }
 
-// Vocabulary projection for a few tokens (T <= TT <= 8): one thread per
+// Vocabulary projection for 5 to 8 tokens: one thread per
 // vocabulary row streams the row in 16-byte loads (two groups of 8 in flight
 // per lane) and runs the same chains as the folded router kernel: within
 // each 256-wide chunk an ascending fp32 fma chain from +0 for every token,
@@ -540,8 +540,8 @@ __global__ __launch_bounds__(kStreamThreads) void lm_logits_stream_kernel(
 
 // Vocabulary projection for one or two tokens, the same chains as the kernel
 // above.  A wave takes 64 vocabulary rows (lane = row) and runs them through
-// the whole hidden state.  Each step of 64 hidden indices is 8 KB of rows loaded as
-// whole 128-byte lines (lane l of load i: row 8i + l/8, chunk l%8), kLmRing
+// the whole hidden state.  Each step of 64 hidden indices is 8 KB of rows
+// loaded as whole 128-byte lines (lane l of load i: row 8i + l/8, chunk l%8), kLmRing
 // steps in flight, and passed through 8 KB of the wave's own LDS (chunks
 // XOR-swizzled by row; one wave's LDS operations run in order) so that each
 // lane reads its own row's 128 bytes.  The tokens' hidden values are the same
@@ -1115,10 +1115,11 @@ size_t route_ws_bytes(int T, int H, int E) {
 }
 
 // Vocabulary projection of a decode step (z = h . proj^T) in the router's
-// pinned order: up to 8 tokens by the streaming kernel (one vocabulary row per
-// thread), more by the matrix-core router kernel (64 tokens x 128 vocabulary
-// rows per block, every chunk folded).  Each z depends only on its own row
-// pair and is the same chain in both, so the choice never changes its bits.
+// pinned order: 1-4 tokens, and 9-16 over a large vocabulary, by the VALU
+// kernels with whole-line row loads; 5-8 by one vocabulary row per thread;
+// more by the matrix-core router kernel (64 tokens x 128 vocabulary rows per
+// block, every chunk folded).  Each z depends only on its own row pair and is
+// the same chain in all of them, so the choice never changes its bits.
 hipError_t launch_lm_logits(int T, int H, int V, const uint16_t* h, const uint16_t* proj,
                             float* z, hipStream_t s) {
     if (T <= 1) return launch_lm_stream<1>(T, H, V, h, proj, z, s);
