@@ -413,7 +413,17 @@ def test_fp8_streaming_gemms_equal_tiled(n):
     The first n tokens alone and inside a 600-token call (the tiled kernel)
     give bit-identical act codes, exponents, bf16 act, y and layer output; the
     streaming gate/up without an act_bf16 output gives the same codes."""
-    cfg = I.scaled(I.CONFIGS["mid"], T=600)
+    _streaming_equal_tiled(I.scaled(I.CONFIGS["mid"], T=600), n)
+
+
+@pytest.mark.parametrize("n", [1, 16, 32])
+def test_fp8_streaming_gemms_equal_tiled_decode_layer(n):
+    """The same on the decode layer (H = 6144, 256 experts with the Zipf bias,
+    F = 2048): 48 K blocks on gate/up, 16 on down."""
+    _streaming_equal_tiled(I.scaled(I.CONFIGS["dec"], T=600), n)
+
+
+def _streaming_equal_tiled(cfg, n):
     L = layer(cfg)
     wqd = M.quantize_weights_fp8(L["w_gate"], L["w_up"], L["w_down"])
     x = I.make_tokens(600, cfg.H, 5151, "cpu").to(DEV)
@@ -428,8 +438,8 @@ def test_fp8_streaming_gemms_equal_tiled(n):
     o1 = bits(_fwd8(cfg, L, wqd, x[:n].contiguous()))
     o2 = bits(_fwd8(cfg, L, wqd, x))
     assert np.array_equal(o1, o2[:n])
-    log(f"[fp8] {n} tokens: weight-streaming GEMMs == the tiled kernel's rows of a 600-token "
-        f"call (act codes, exps, bf16, y, out)")
+    log(f"[fp8] {cfg.name} layer, {n} tokens: weight-streaming GEMMs == the tiled kernel's rows "
+        f"of a 600-token call (act codes, exps, bf16, y, out)")
 
 
 def test_large_fp8_sampled():
